@@ -1,0 +1,351 @@
+"""Reference definitions of every step of the quantized linear projection.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  NumPy, float64 and
+int64, no blocking, fusion or reordering beyond what each definition states.
+
+Sources (page title, section):
+  [FQ]  FoldQuantVLA: Native Low-Bit Quantization of Vision-Language-Action
+        Models via Consistent Folding -- abstract (channel scaling, block
+        Hadamard transform, dynamic per-token quantization, W4A4 integer
+        execution, o_proj/down_proj kept at W8A8).
+  [OQ]  Omega-QVLA technical summary -- Metodologia 1, "Rotazione Composita
+        SVD-Hadamard" (normalised Hadamard matrix H) and "Implementazione a
+        Blocchi" (block approximation of the C_in x C_in rotation).
+  [LQ]  LoopQ: Fair, Closed-Loop Evaluation of Quantized VLA Models --
+        abstract (plain round-to-nearest weights; weight-only 4-bit kernels at
+        batch 1; memory-bound action expert).
+  [QV]  QuantVLA technical summary -- Methodology B/C (per-head and per-layer
+        scalars folded into the dequantization scale, no extra runtime op).
+
+Readings where the pages leave a step open are stated at each function.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Hadamard rotation  [OQ] Rotazione Composita / Implementazione a Blocchi,
+#                    [FQ] abstract ("block Hadamard transforms")
+# --------------------------------------------------------------------------
+
+
+def _is_pow2(b: int) -> bool:
+    return b >= 1 and (b & (b - 1)) == 0
+
+
+def sylvester_hadamard(b: int) -> np.ndarray:
+    """Unnormalised Hadamard matrix of order b in Sylvester (natural) order.
+
+    H_b[i, j] = (-1) ** popcount(i & j), entries +-1, int64.  The pages only
+    say "normalised Hadamard matrix"; the natural order is the reading taken.
+    """
+    if not _is_pow2(b):
+        raise ValueError(f"Hadamard order must be a power of two, got {b}")
+    i = np.arange(b, dtype=np.int64)[:, None]
+    j = np.arange(b, dtype=np.int64)[None, :]
+    a = i & j
+    parity = np.zeros_like(a)
+    while np.any(a):
+        parity ^= a & 1
+        a >>= 1
+    return np.where(parity == 0, 1, -1).astype(np.int64)
+
+
+def block_rotation_matrix(k: int, b: int) -> np.ndarray:
+    """Dense k x k block-diagonal rotation blockdiag(H_b / sqrt(b)), float64.
+
+    b in {0, 1} means no rotation (identity).  Used only at small k: the
+    pages replace the dense C_in x C_in rotation by this block form.
+    """
+    if b in (0, 1):
+        return np.eye(k, dtype=np.float64)
+    if k % b:
+        raise ValueError("k must be a multiple of the Hadamard block")
+    hb = sylvester_hadamard(b).astype(np.float64) / math.sqrt(b)
+    r = np.zeros((k, k), dtype=np.float64)
+    for j in range(k // b):
+        r[j * b:(j + 1) * b, j * b:(j + 1) * b] = hb
+    return r
+
+
+def rotate_blocks(v: np.ndarray, b: int) -> np.ndarray:
+    """Row-wise rotation v @ blockdiag(H_b / sqrt(b)) over contiguous k-blocks.
+
+    A dense float64 matmul per block of b input channels (no fast transform).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if b in (0, 1):
+        return v.copy()
+    k = v.shape[-1]
+    if k % b:
+        raise ValueError("k must be a multiple of the Hadamard block")
+    hb = sylvester_hadamard(b).astype(np.float64) / math.sqrt(b)
+    out = np.empty_like(v)
+    for j in range(k // b):
+        out[..., j * b:(j + 1) * b] = v[..., j * b:(j + 1) * b] @ hb
+    return out
+
+
+# --------------------------------------------------------------------------
+# Channel-scale fold  [FQ] abstract ("channel scaling")
+# --------------------------------------------------------------------------
+
+
+def calibrate_fold(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-input-channel fold vector s[k] (float32).
+
+    s_k = sqrt(max_m |X[m, k]| / max_n |W[n, k]|), evaluated in float64 and
+    stored as float32.  W is [N][K] (nn.Linear layout), so the weight maximum
+    is over column k.  If either maximum is zero, s_k = 1.  The formula is the
+    SmoothQuant-style balance point (alpha = 1/2); the pages name channel
+    scaling without its formula.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x and w must share the input dimension")
+    ax = np.max(np.abs(x), axis=0)
+    aw = np.max(np.abs(w), axis=0)
+    s = np.ones(x.shape[1], dtype=np.float64)
+    ok = (ax > 0) & (aw > 0)
+    s[ok] = np.sqrt(ax[ok] / aw[ok])
+    return s.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Symmetric round-to-nearest quantization
+#   [FQ] abstract ("dynamic per-token quantization"), [LQ] abstract ("RTN")
+# --------------------------------------------------------------------------
+
+
+def qmax_of(bits: int) -> int:
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    return (1 << (bits - 1)) - 1
+
+
+def quantize_rows(v: np.ndarray, bits: int):
+    """Per-row symmetric quantization with a dynamic scale.
+
+    amax_m = max_k |v[m, k]|; scale_m = float32(amax_m / qmax);
+    r = v / float64(scale_m); q = clamp(round_half_even(r), -qmax, qmax).
+    A zero row gives scale 0 and codes 0.  qmax = 7 (int4) or 127 (int8): the
+    grid is symmetric, so -8 / -128 never occur.  Codes are computed with the
+    stored (float32) scale.
+
+    Returns (q int64, scale float32, r float64 -- the pre-rounding values).
+    """
+    qmax = qmax_of(bits)
+    v = np.asarray(v, dtype=np.float64)
+    amax = np.max(np.abs(v), axis=1)
+    scale = (amax / qmax).astype(np.float32)
+    s64 = scale.astype(np.float64)
+    r = np.zeros_like(v)
+    nz = s64 > 0
+    r[nz] = v[nz] / s64[nz, None]
+    q = np.clip(np.rint(r), -qmax, qmax).astype(np.int64)
+    return q, scale, r
+
+
+def quantize_groups_w4a16(w: np.ndarray, group: int):
+    """Weight-only int4 with one fp16 scale per (row, group of input channels).
+
+    For row n and group g (input channels [g*group, (g+1)*group)):
+    s16 = fp16_rne(amax / 7); q = clamp(rne(w / float64(s16)), -7, 7);
+    s16 == 0 gives q = 0.  Symmetric, no zero point, no fold, no rotation
+    ([LQ] abstract: 4-bit weight-only kernels, plain RTN).
+
+    Returns (q int64 [N][K], s16 float16 [N][K/group], r float64 [N][K]).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("k must be a multiple of the group size")
+    ng = k // group
+    wg = w.reshape(n, ng, group)
+    amax = np.max(np.abs(wg), axis=2)
+    s16 = (amax / 7.0).astype(np.float16)  # float64 -> float16 directly, RNE
+    s64 = s16.astype(np.float64)
+    r = np.zeros_like(wg)
+    nz = s64 > 0
+    r[nz] = wg[nz] / s64[nz][:, None]
+    q = np.clip(np.rint(r), -7, 7).astype(np.int64)
+    return q.reshape(n, k), s16, r.reshape(n, k)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two int4 codes per byte along the last axis: element 2j in the low
+    nibble, element 2j+1 in the high nibble, two's complement."""
+    q = np.asarray(q, dtype=np.int64)
+    if q.shape[-1] % 2:
+        raise ValueError("int4 packing needs an even last dimension")
+    if np.any(q < -8) or np.any(q > 7):
+        raise ValueError("int4 code out of range")
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: sign-extended nibbles, int64."""
+    p = np.asarray(p, dtype=np.uint8).astype(np.int64)
+    lo = p & 0xF
+    hi = (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# --------------------------------------------------------------------------
+# GeGLU glue between the gate/up and down projections of an MLP block
+# --------------------------------------------------------------------------
+
+_erf = np.vectorize(math.erf, otypes=[np.float64])
+
+
+def gelu(t: np.ndarray) -> np.ndarray:
+    """Exact GeLU t * (1 + erf(t / sqrt 2)) / 2 in float64 with the host libm
+    erf.  The variant (erf vs tanh form) is a reading; the pages are silent."""
+    t = np.asarray(t, dtype=np.float64)
+    return t * 0.5 * (1.0 + _erf(t / math.sqrt(2.0)))
+
+
+def geglu(x: np.ndarray, k: int) -> np.ndarray:
+    """h = gelu(gate) * up for x = [gate | up] along the last axis (width 2k)."""
+    x = np.asarray(x, dtype=np.float64)
+    return gelu(x[..., :k]) * x[..., k:2 * k]
+
+
+# --------------------------------------------------------------------------
+# Whole stages, as the library's entry points expose them
+# --------------------------------------------------------------------------
+
+
+def rotate_quant_act(x, fold_s, had_block: int, bits: int, preop: str = "none"):
+    """Online activation path: (optional GeGLU) -> x / s -> block Hadamard ->
+    per-token dynamic symmetric quantization ([FQ] abstract).
+
+    x: [M][K] (or [M][2K] with preop='geglu'); fold_s: float32 [K] or None.
+    Returns (q int64 [M][K], scale float32 [M], r float64 [M][K]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if preop == "geglu":
+        k = x.shape[1] // 2
+        v = geglu(x, k)
+    elif preop == "none":
+        v = x
+    else:
+        raise ValueError(preop)
+    if fold_s is not None:
+        v = v / np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
+    v = rotate_blocks(v, had_block)
+    return quantize_rows(v, bits)
+
+
+def quantize_weights(w, fold_s, had_block: int, bits: int, group: int = 0):
+    """Offline weight path.
+
+    group == 0: w * s -> block Hadamard on the rows -> per-output-channel
+    symmetric RTN (the consistent counterpart of the activation path, so that
+    (x/s) H (w s H)^T = x w^T).  Returns (q, scale float32 [N], r).
+    group > 0 : W4A16 group quantization (bits must be 4, no fold, no
+    rotation).  Returns (q, s16 float16 [N][K/group], r).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if group:
+        if bits != 4 or fold_s is not None or had_block not in (0, 1):
+            raise ValueError("group quantization is int4 with no fold/rotation")
+        return quantize_groups_w4a16(w, group)
+    if fold_s is not None:
+        w = w * np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
+    w = rotate_blocks(w, had_block)
+    return quantize_rows(w, bits)
+
+
+def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k qx[m, k] * qw[n, k] in int64 ([FQ]: native integer
+    execution).  Checks that the result fits the int32 accumulator."""
+    qx = np.asarray(qx, dtype=np.int64)
+    qw = np.asarray(qw, dtype=np.int64)
+    acc = qx @ qw.T
+    if acc.size and np.max(np.abs(acc)) >= 2 ** 31:
+        raise OverflowError("accumulator exceeds int32")
+    return acc
+
+
+def dequant_epilogue(acc, x_scale, w_scale) -> np.ndarray:
+    """y32 = float32(acc * s_x[m] * s_w[n]) with the product in float64.
+
+    Per-head / per-layer calibration scalars ([QV] Methodology B, C) are
+    pre-multiplied into s_w and need no separate step.
+    """
+    acc = np.asarray(acc, dtype=np.int64).astype(np.float64)
+    sx = np.asarray(x_scale, dtype=np.float32).astype(np.float64)
+    sw = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    return (acc * sx[:, None] * sw[None, :]).astype(np.float32)
+
+
+def round_to_bf16_bits(y32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 with round-half-to-even, as uint16 bit patterns.
+
+    NumPy has no bfloat16: add 0x7FFF plus the lowest kept bit to the float32
+    pattern and drop the low 16 bits.  Finite inputs only.
+    """
+    u = np.ascontiguousarray(y32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return (((u + 0x7FFF + lsb) >> 16) & 0xFFFF).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def round_to_f16(y32: np.ndarray) -> np.ndarray:
+    """float32 -> float16 with round-half-to-even (NumPy's cast)."""
+    return np.asarray(y32, dtype=np.float32).astype(np.float16)
+
+
+def round_output(y32: np.ndarray, dtype: str) -> np.ndarray:
+    """The reference output: the float32 result rounded to the output dtype,
+    returned widened to float64 for comparison."""
+    if dtype == "f16":
+        return round_to_f16(y32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(round_to_bf16_bits(y32))
+    if dtype == "f32":
+        return np.asarray(y32, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def gemm(qx, x_scale, qw, w_scale, out_dtype: str):
+    """Integer GEMM followed by the dequantizing epilogue.
+
+    Returns (acc int64, y32 float32, y_ref float64 rounded to out_dtype).
+    """
+    acc = int_gemm(qx, qw)
+    y32 = dequant_epilogue(acc, x_scale, w_scale)
+    return acc, y32, round_output(y32, out_dtype)
+
+
+def gemv_w4a16(x, qw, s16, group: int):
+    """Weight-only product y[m, n] = sum_k x[m, k] * q[n, k] * s16[n, k//group]
+    in float64, then float32, then float16 (RNE).  [LQ] abstract: batch-1
+    weight-only kernels of the memory-bound action expert.
+
+    Returns (y32 float32, y_ref float64 holding the float16 values).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    q = np.asarray(qw, dtype=np.int64).astype(np.float64)
+    s = np.asarray(s16, dtype=np.float16).astype(np.float64)
+    n, k = q.shape
+    wdq = q * np.repeat(s, group, axis=1)[:, :k]
+    y32 = (x @ wdq.T).astype(np.float32)
+    return y32, round_output(y32, "f16")
