@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized linear projection on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the backbone-shaped
+MLP block at M = 816 tokens (hidden 2048, gate|up 2 x 16384, down 2048):
+
+  rotate+quantize X (bf16, fold, Hadamard 128, int4)
+  -> gate|up W4A4 GEMM (816 x 32768 x 2048) -> bf16
+  -> GeGLU + fold + Hadamard 128 + int8 quantize (816 x 16384)
+  -> down W8A8 GEMM (816 x 2048 x 16384) -> bf16
+
+Weights are quantized once before timing (offline).  Inputs are synthetic,
+seeded, resident in HBM before the timed region.  value = integer GEMM ops of
+the step (2*M*N*K summed) / step time, in TOPS.  Also reported: the
+batch-1 W4A16 GEMV of a 7B-decoder layer (hidden 4096, MLP 11008) in GB/s
+with distinct weight copies rotated to defeat the 256 MB Infinity Cache, the
+dominant kernel's roofline fraction, and the CPU oracle on a row sample.
+
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=16, help="token rows of the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
+    return ap.parse_args()
+
+
+class MlpBlock:
+    """Device buffers and quantized weights of the M = 816 backbone MLP block."""
+
+    def __init__(self, dev):
+        import torch
+
+        import bit_ptq_vla_amd as q
+        from bit_ptq_vla_amd import synth
+
+        self.q = q
+        wl = synth.CFG2
+        self.gu, self.dn = wl.projs
+        self.m = wl.ms[0]
+        self.x_cpu = synth.activation(wl, self.gu, self.m)
+        self.wgu_cpu = synth.weight(wl, self.gu)
+        self.wdn_cpu = synth.weight(wl, self.dn)
+        self.x = self.x_cpu.to(dev)
+        wgu, wdn = self.wgu_cpu.to(dev), self.wdn_cpu.to(dev)
+        # offline: fold calibration and weight quantization
+        self.s1, self.inv1 = q.qlin_calibrate_fold(self.x, wgu)
+        self.wq1, self.ws1 = q.qlin_quantize_weights(wgu, fold_s=self.s1, had_block=128, bits=4)
+        self.xq = torch.empty((self.m, self.gu.k // 2), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty(self.m, dtype=torch.float32, device=dev)
+        self.y1 = torch.empty((self.m, self.gu.n), dtype=torch.bfloat16, device=dev)
+        q.qlin_rotate_quant_act(self.x, fold_inv_s=self.inv1, had_block=128, bits=4, out=(self.xq, self.xs))
+        q.qlin_gemm_w4a4(self.xq, self.xs, self.wq1, self.ws1, self.gu.k, out=self.y1)
+        self.s2, self.inv2 = q.qlin_calibrate_fold(self.y1, wdn, pre=q.QLIN_PRE_GEGLU)
+        self.wq2, self.ws2 = q.qlin_quantize_weights(wdn, fold_s=self.s2, had_block=128, bits=8)
+        del wgu, wdn
+        self.hq = torch.empty((self.m, self.dn.k), dtype=torch.int8, device=dev)
+        self.hs = torch.empty(self.m, dtype=torch.float32, device=dev)
+        self.y2 = torch.empty((self.m, self.dn.n), dtype=torch.bfloat16, device=dev)
+        self.ops = 2 * self.m * (self.gu.n * self.gu.k + self.dn.n * self.dn.k)
+        self.gemm1_ops = 2 * self.m * self.gu.n * self.gu.k
+
+    def step(self, ev=None):
+        q = self.q
+        q.qlin_rotate_quant_act(self.x, fold_inv_s=self.inv1, had_block=128, bits=4, out=(self.xq, self.xs))
+        if ev is not None:
+            ev[0].record()
+        q.qlin_gemm_w4a4(self.xq, self.xs, self.wq1, self.ws1, self.gu.k, out=self.y1)
+        if ev is not None:
+            ev[1].record()
+        q.qlin_rotate_quant_act(self.y1, k=self.dn.k, fold_inv_s=self.inv2, had_block=128, bits=8,
+                                pre=q.QLIN_PRE_GEGLU, out=(self.hq, self.hs))
+        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq2, self.ws2, self.dn.k, out=self.y2)
+
+
+def time_block(block, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        block.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        block.step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    gemm1_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return ms_step, gemm1_ms, wall
+
+
+def gemv_leg(dev, reps=3):
+    """Batch-1 W4A16 GEMV over a 7B-decoder layer; distinct weight copies
+    (>= 512 MB in total) are cycled so that the weights stream from HBM."""
+    import torch
+
+    import bit_ptq_vla_amd as q
+    from bit_ptq_vla_amd import synth
+
+    wl = synth.CFG4
+    layer = []
+    for p in wl.projs:
+        w = synth.weight(wl, p).to(dev)
+        wq, ws = q.qlin_quantize_weights(w, bits=4, group=128)
+        del w
+        layer.append((p, wq, ws))
+    layer_bytes = sum(p.n * p.k // 2 + p.n * (p.k // 128) * 2 for p, _, _ in layer)
+    copies = max(1, -(-512 * 2 ** 20 // layer_bytes) + 1)
+    layers = [layer] + [[(p, wq.clone(), ws.clone()) for p, wq, ws in layer] for _ in range(copies - 1)]
+    xs = {k: synth.normal_tensor(wl.seed, f"gemv_x/{k}", (1, k), dtype="f16").to(dev) for k in (4096, 11008)}
+    ys = {n: torch.empty((1, n), dtype=torch.float16, device=dev) for n in (4096, 11008)}
+    for L in layers:  # warm-up
+        for p, wq, ws in L:
+            q.qlin_gemv_w4a16(xs[p.k], wq, ws, out=ys[p.n])
+    torch.cuda.synchronize()
+    per = {}
+    for _ in range(reps):
+        for L in layers:
+            for p, wq, ws in L:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                q.qlin_gemv_w4a16(xs[p.k], wq, ws, out=ys[p.n])
+                b.record()
+                per.setdefault((p.n, p.k), []).append((a, b))
+    torch.cuda.synchronize()
+    shapes = {}
+    for (n, k), evs in per.items():
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        med = ms[len(ms) // 2]
+        nbytes = n * k // 2 + n * (k // 128) * 2 + 2 * k + 2 * n
+        shapes[f"{n}x{k}"] = {"us": round(med * 1e3, 3), "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    layer_us = sum(shapes[f"{p.n}x{p.k}"]["us"] for p, _, _ in layer)
+    layer_gbs = (layer_bytes + sum(2 * p.k + 2 * p.n for p, _, _ in layer)) / (layer_us * 1e-6) / 1e9
+    return {"workload": "decoder7b_layer_m1_w4a16_g128", "layer_MB": round(layer_bytes / 1e6, 2),
+            "weight_copies": copies, "layer_us": round(layer_us, 2), "GB/s": round(layer_gbs, 1),
+            "frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "shapes": shapes}
+
+
+def cpu_baseline(block, rows):
+    """The oracle as it stands on a row sample of the same step (single
+    thread: NumPy's int64 matmul does not use BLAS; BLAS is pinned to one
+    thread for the float64 rotation)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from bit_ptq_vla_amd import synth
+
+    with threadpool_limits(limits=1):
+        s1 = block.s1.cpu().numpy()
+        s2 = block.s2.cpu().numpy()
+        qw1, sw1, _ = oracle.quantize_weights(synth.to_f64(block.wgu_cpu), s1, 128, 4)
+        qw2, sw2, _ = oracle.quantize_weights(synth.to_f64(block.wdn_cpu), s2, 128, 8)
+        x = synth.to_f64(block.x_cpu[:rows])
+        t0 = time.perf_counter()
+        qx, sx, _ = oracle.rotate_quant_act(x, s1, 128, 4)
+        _, y32, y1 = oracle.gemm(qx, sx, qw1, sw1, "bf16")
+        qh, sh, _ = oracle.rotate_quant_act(y1, s2, 128, 8, preop="geglu")
+        oracle.gemm(qh, sh, qw2, sw2, "bf16")
+        dt = time.perf_counter() - t0
+    ops = 2 * rows * (block.gu.n * block.gu.k + block.dn.n * block.dn.k)
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {block.m} token rows of the M=816 MLP block step "
+                      f"(weights quantized beforehand), {dt:.1f} s on 1 thread of {os.cpu_count()} host cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: preparing the MLP block (weights quantized offline)")
+    block = MlpBlock(dev)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_step, gemm1_ms, wall = time_block(block, args.steps, args.warmup)
+    tops = block.ops / (ms_step * 1e-3) / 1e12
+    gemm1_tops = block.gemm1_ops / (gemm1_ms * 1e-3) / 1e12
+    out = {
+        "metric": "W4A4/W8A8 qlinear TOPS + batch-1 W4A16 GEMV GB/s, % of MI355X roofline",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 MFMA (int4/int8 codes), fp32 rotate/epilogue, bf16 I/O",
+        "data": "synthetic (seeded normals, 1% outlier channels x30; random-init weights N(0, 0.02))",
+        "config": {"workload": "backbone_mlp_m816_h2048_f16384", "m": block.m, "hidden": 2048,
+                   "ffn": 16384, "gate_up": "w4a4", "down": "w8a8", "hadamard_block": 128,
+                   "out_dtype": "bf16", "step_gop": round(block.ops / 1e9, 2)},
+        "roofline": {"kernel": "gate_up W4A4 GEMM 816x32768x2048", "bound": "mfma",
+                     "achieved": round(gemm1_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(gemm1_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "us_per_launch": round(gemm1_ms * 1e3, 3)},
+        "frac_of_int8_peak_step": round(tops / INT8_PEAK_TOPS, 4),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_gemv:
+        log("bench: batch-1 W4A16 GEMV leg")
+        out["gemv"] = gemv_leg(dev)
+    if not args.no_cpu_baseline:
+        log(f"bench: CPU oracle on {args.cpu_rows} rows")
+        out["cpu_baseline"] = cpu_baseline(block, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+"""Python binding of the qlin C ABI (libqlin.so, HIP kernels for gfx950).
+
+Argument marshalling only: device tensors are passed as raw pointers together
+with torch's current HIP stream, output tensors are allocated with torch, and
+every computation runs in the library's kernels.  The function names mirror
+the C entry points declared in include/qlin.h; a non-zero status raises
+QlinError.  Importing works without a GPU; calling a compute entry point
+without the built library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlin.so")
+
+QLIN_OK = 0
+QLIN_ERR_NULL = 1
+QLIN_ERR_SHAPE = 2
+QLIN_ERR_DTYPE = 3
+QLIN_ERR_ALIGN = 4
+QLIN_ERR_UNSUPPORTED = 5
+QLIN_ERR_DEVICE = 6
+QLIN_ERR_LAUNCH = 7
+QLIN_ERR_ALIAS = 8
+
+QLIN_F16, QLIN_BF16, QLIN_F32, QLIN_I32 = 0, 1, 2, 3
+QLIN_PRE_NONE, QLIN_PRE_GEGLU = 0, 1
+
+_TORCH_TO_QLIN = {torch.float16: QLIN_F16, torch.bfloat16: QLIN_BF16,
+                  torch.float32: QLIN_F32, torch.int32: QLIN_I32}
+
+# (name, argtypes) of every exported entry point; restype is int32 unless noted.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+SIGNATURES = {
+    "qlin_abi_version": [],
+    "qlin_status_string": [_I32],
+    "qlin_calibrate_fold": [_P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _I64, _P, _P, _P],
+    "qlin_quantize_weights": [_P, _I32, _I64, _I64, _P, _I32, _I32, _I32, _P, _P, _P],
+    "qlin_rotate_quant_act": [_P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P],
+    "qlin_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemm_w8a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
+}
+
+_lib = None
+
+
+class QlinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """Loads libqlin.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_ptq_vla_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "qlin_status_string" else ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().qlin_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return load().qlin_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != QLIN_OK:
+        raise QlinError(status, where)
+
+
+def _dev_tensor(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+
+def qlin_calibrate_fold(x: torch.Tensor, w: torch.Tensor, pre: int = QLIN_PRE_NONE
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fold vector s[k] and 1/s[k] from activations x [m][k] (or [m][2k] =
+    gate|up with pre=GEGLU) and weights w [n][k]."""
+    lib = load()
+    _dev_tensor(x, "x"); _dev_tensor(w, "w")
+    n, k = w.shape
+    s = torch.empty(k, dtype=torch.float32, device=x.device)
+    inv_s = torch.empty_like(s)
+    st = lib.qlin_calibrate_fold(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], x.shape[0], k, x.stride(0), pre,
+                                 w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, s.data_ptr(), inv_s.data_ptr(),
+                                 _stream(x.device))
+    _check(st, "qlin_calibrate_fold")
+    return s, inv_s
+
+
+def qlin_quantize_weights(w: torch.Tensor, fold_s: Optional[torch.Tensor] = None, had_block: int = 0,
+                          bits: int = 4, group: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Codes (int8 [n][k] or packed uint8 [n][k/2]) and scales (float32 [n],
+    or fp16 [n][k/group] for group quantization) of weights w [n][k]."""
+    lib = load()
+    _dev_tensor(w, "w")
+    n, k = w.shape
+    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
+                     device=w.device)
+    ws = (torch.empty((n, k // group), dtype=torch.float16, device=w.device) if group
+          else torch.empty(n, dtype=torch.float32, device=w.device))
+    st = lib.qlin_quantize_weights(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
+                                   bits, group, wq.data_ptr(), ws.data_ptr(), _stream(w.device))
+    _check(st, "qlin_quantize_weights")
+    return wq, ws
+
+
+def qlin_rotate_quant_act(x: torch.Tensor, k: Optional[int] = None, fold_inv_s: Optional[torch.Tensor] = None,
+                          had_block: int = 0, bits: int = 4, pre: int = QLIN_PRE_NONE,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Activation codes and per-token scales of x [m][ldx] (k inputs, or
+    gate|up of width 2k with pre=GEGLU)."""
+    lib = load()
+    _dev_tensor(x, "x")
+    m = x.shape[0]
+    if k is None:
+        k = x.shape[1] // 2 if pre == QLIN_PRE_GEGLU else x.shape[1]
+    if out is None:
+        xq = torch.empty((m, k // 2) if bits == 4 else (m, k), dtype=torch.uint8 if bits == 4 else torch.int8,
+                         device=x.device)
+        xs = torch.empty(m, dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    st = lib.qlin_rotate_quant_act(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0), pre,
+                                   _ptr(fold_inv_s), had_block, bits, xq.data_ptr(), xs.data_ptr(),
+                                   _stream(x.device))
+    _check(st, "qlin_rotate_quant_act")
+    return xq, xs
+
+
+def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):
+    lib = load()
+    _dev_tensor(wq, "wq")
+    m, n = xq.shape[0], wq.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=y_dtype, device=wq.device)
+    st = getattr(lib, fn_name)(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
+                               y.data_ptr(), _TORCH_TO_QLIN[y.dtype], _stream(wq.device))
+    _check(st, fn_name)
+    return y
+
+
+def qlin_gemm_w4a4(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """y [m][n] from packed int4 codes xq [m][k/2], wq [n][k/2]."""
+    return _gemm("qlin_gemm_w4a4", xq, x_scale, wq, w_scale, k, y_dtype, out)
+
+
+def qlin_gemm_w8a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """y [m][n] from int8 codes xq [m][k], wq [n][k]."""
+    return _gemm("qlin_gemm_w8a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
+
+
+def qlin_gemv_w4a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, group: int = 128,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [m][n] fp16 from fp16 x [m][k] and packed int4 weights with fp16 group scales."""
+    lib = load()
+    _dev_tensor(x, "x")
+    m, k = x.shape
+    n = wq.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+    st = lib.qlin_gemv_w4a16(x.data_ptr(), wq.data_ptr(), w_scale.data_ptr(), m, n, k, group, y.data_ptr(),
+                             _stream(x.device))
+    _check(st, "qlin_gemv_w4a16")
+    return y

@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of the qlin library.
+// Storage conversions, vector types and wave64 cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+enum DType { F16 = 0, BF16 = 1, F32 = 2, I32 = 3 };
+
+// ---- scalar storage conversions ------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16 bits, round half to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = static_cast<_Float16>(f);  // v_cvt_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Eight consecutive elements of a row, widened to fp32.  p must be 16-byte
+// aligned (32-byte rows of f32 are read as two 16-byte loads).
+template <int DT>
+__device__ __forceinline__ void load8(const void* p, float f[8]);
+
+template <>
+__device__ __forceinline__ void load8<F16>(const void* p, float f[8]) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = f16_bits_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+        f[2 * i + 1] = f16_bits_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<BF16>(const void* p, float f[8]) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<F32>(const void* p, float f[8]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    float4 a = q[0], b = q[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// ---- wave64 cross-lane helpers -------------------------------------------
+
+// Value held by lane (lane ^ mask).  For mask < 32 this is ds_swizzle in
+// bit-mask mode (and 0x1F, xor mask), which needs no LDS allocation.
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v) {
+    if constexpr (MASK < 32) {
+        constexpr int pattern = (MASK << 10) | 0x1F;
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), pattern));
+    } else {
+        return __shfl_xor(v, MASK, 64);
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v, int width) {
+    // width is a power of two <= 64; reduce within aligned groups of `width`.
+    if (width >= 2) v = fmaxf(v, lane_xor<1>(v));
+    if (width >= 4) v = fmaxf(v, lane_xor<2>(v));
+    if (width >= 8) v = fmaxf(v, lane_xor<4>(v));
+    if (width >= 16) v = fmaxf(v, lane_xor<8>(v));
+    if (width >= 32) v = fmaxf(v, lane_xor<16>(v));
+    if (width >= 64) v = fmaxf(v, lane_xor<32>(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<8>(v);
+    v += lane_xor<16>(v);
+    v += lane_xor<32>(v);
+    return v;
+}
+
+// Exact GeLU, t * (1 + erf(t / sqrt 2)) / 2, in fp32 (device-library erff).
+__device__ __forceinline__ float gelu_erf(float t) {
+    return 0.5f * t * (1.0f + erff(t * 0.70710678118654752440f));
+}
+
+}  // namespace qlin

@@ -1,0 +1,229 @@
+// Host side of the qlin C ABI: argument validation (before any HIP call),
+// device check, launch, and HIP error mapping.  Declarations and the meaning
+// of every argument are in include/qlin.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/qlin.h"
+#include "qlin_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unchecked, 1 = gfx950, 2 = other device
+int g_device_ok[kMaxDevices] = {0};
+std::mutex g_device_mu;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t dtype_size(qlin_dtype d) {
+    switch (d) {
+        case QLIN_F16: case QLIN_BF16: return 2;
+        case QLIN_F32: case QLIN_I32: return 4;
+    }
+    return 0;
+}
+
+bool is_float_in(qlin_dtype d) { return d == QLIN_F16 || d == QLIN_BF16 || d == QLIN_F32; }
+
+bool pow2_block_ok(int32_t b) { return b == 0 || b == 1 || (b > 1 && b <= 256 && (b & (b - 1)) == 0); }
+
+struct Span {
+    const void* p;
+    int64_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+bool any_overlap(const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+// Checks (once per device, cached) that the current device is a gfx950.
+qlin_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QLIN_ERR_DEVICE;
+    if (dev >= kMaxDevices) return QLIN_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_device_mu);
+    if (g_device_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QLIN_ERR_DEVICE;
+        g_device_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    return g_device_ok[dev] == 1 ? QLIN_OK : QLIN_ERR_DEVICE;
+}
+
+qlin_status map_err(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Largest k the activation / weight row kernel holds in registers:
+// 256 lanes x 16 chunks x 8 values.
+constexpr int64_t kMaxRowK = 32768;
+
+qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                        int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream,
+                        bool int4) {
+    if (!xq && m > 0) return QLIN_ERR_NULL;
+    if (!wq || !y) return QLIN_ERR_NULL;
+    if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
+    if (y_dtype != QLIN_F16 && y_dtype != QLIN_BF16 && y_dtype != QLIN_F32 && y_dtype != QLIN_I32)
+        return QLIN_ERR_DTYPE;
+    if (m < 0 || n < 1 || k < 64 || (k % 64) != 0) return QLIN_ERR_SHAPE;
+    if (k > 131072) return QLIN_ERR_SHAPE;  // keeps |acc| (and 256*acc for int4) below 2^31
+    if (m > 0x7FFFFFFF || n > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))
+        return QLIN_ERR_ALIGN;
+    const int64_t kb = int4 ? k / 2 : k;
+    const Span outs[1] = {{y, m * n * dtype_size(y_dtype)}};
+    const Span ins[4] = {{xq, m * kb}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
+    if (any_overlap(outs, 1, ins, 4)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4);
+    hipStream_t s = as_stream(stream);
+    int32_t* ws = nullptr;
+    if (plan.ws_bytes > 0) {
+        if (hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.ws_bytes), s) != hipSuccess)
+            return QLIN_ERR_DEVICE;
+    }
+    hipError_t e = qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, y, y_dtype, ws, s);
+    if (ws) {
+        if (hipFreeAsync(ws, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
+    }
+    return map_err(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qlin_abi_version(void) { return QLIN_ABI_VERSION; }
+
+const char* qlin_status_string(qlin_status s) {
+    switch (s) {
+        case QLIN_OK: return "ok";
+        case QLIN_ERR_NULL: return "null pointer";
+        case QLIN_ERR_SHAPE: return "invalid shape";
+        case QLIN_ERR_DTYPE: return "unsupported dtype";
+        case QLIN_ERR_ALIGN: return "pointer or row pitch not 16-byte aligned";
+        case QLIN_ERR_UNSUPPORTED: return "unsupported bits, block, group or pre-op";
+        case QLIN_ERR_DEVICE: return "no usable gfx950 device or HIP runtime error";
+        case QLIN_ERR_LAUNCH: return "kernel launch failed";
+        case QLIN_ERR_ALIAS: return "output overlaps an input";
+    }
+    return "unknown status";
+}
+
+qlin_status qlin_calibrate_fold(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                qlin_preop pre, const void* w, qlin_dtype w_dtype, int64_t n, float* s,
+                                float* inv_s, void* stream) {
+    if (!x || !w || !s || !inv_s) return QLIN_ERR_NULL;
+    if (!is_float_in(x_dtype) || !is_float_in(w_dtype)) return QLIN_ERR_DTYPE;
+    if (pre != QLIN_PRE_NONE && pre != QLIN_PRE_GEGLU) return QLIN_ERR_UNSUPPORTED;
+    const int64_t width = (pre == QLIN_PRE_GEGLU) ? 2 * k : k;
+    if (m < 1 || n < 1 || k < 8 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < width) return QLIN_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(inv_s)) return QLIN_ERR_ALIGN;
+    const Span outs[2] = {{s, k * 4}, {inv_s, k * 4}};
+    const Span ins[2] = {{x, ((m - 1) * ldx + width) * dtype_size(x_dtype)}, {w, n * k * dtype_size(w_dtype)}};
+    if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_calibrate_fold(x, x_dtype, m, k, ldx, pre == QLIN_PRE_GEGLU, w, w_dtype,
+                                               n, s, inv_s, as_stream(stream)));
+}
+
+qlin_status qlin_quantize_weights(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                  const float* fold_s, int32_t had_block, int32_t bits, int32_t group,
+                                  void* wq, void* w_scale, void* stream) {
+    if (!w || !wq || !w_scale) return QLIN_ERR_NULL;
+    if (!is_float_in(w_dtype)) return QLIN_ERR_DTYPE;
+    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
+    if (group != 0 && group != 128) return QLIN_ERR_UNSUPPORTED;
+    if (group == 128 && (bits != 4 || fold_s != nullptr || had_block > 1)) return QLIN_ERR_UNSUPPORTED;
+    if (n < 1 || k < 8 || (k % 8) != 0) return QLIN_ERR_SHAPE;
+    if (group && (k % group) != 0) return QLIN_ERR_SHAPE;
+    if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
+    if (!group && k > kMaxRowK) return QLIN_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(fold_s)) return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
+    const int64_t scale_bytes = group ? n * (k / group) * 2 : n * 4;
+    const Span outs[2] = {{wq, code_bytes}, {w_scale, scale_bytes}};
+    const Span ins[2] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}};
+    if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (group) return map_err(qlin::launch_quant_groups_w4(w, w_dtype, n, k, wq, w_scale, s));
+    return map_err(qlin::launch_rotate_quant(w, w_dtype, n, k, k, false, fold_s, had_block, bits, wq,
+                                             static_cast<float*>(w_scale), s));
+}
+
+qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                  qlin_preop pre, const float* fold_inv_s, int32_t had_block, int32_t bits,
+                                  void* xq, float* x_scale, void* stream) {
+    if (m > 0 && (!x || !xq || !x_scale)) return QLIN_ERR_NULL;
+    if (!is_float_in(x_dtype)) return QLIN_ERR_DTYPE;
+    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
+    if (pre != QLIN_PRE_NONE && pre != QLIN_PRE_GEGLU) return QLIN_ERR_UNSUPPORTED;
+    const int64_t width = (pre == QLIN_PRE_GEGLU) ? 2 * k : k;
+    if (m < 0 || k < 8 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < width) return QLIN_ERR_SHAPE;
+    if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
+    if (k > kMaxRowK) return QLIN_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || !aligned16(fold_inv_s)) return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
+    const Span outs[2] = {{xq, code_bytes}, {x_scale, m * 4}};
+    const Span ins[2] = {{x, m > 0 ? ((m - 1) * ldx + width) * dtype_size(x_dtype) : 0},
+                         {fold_inv_s, fold_inv_s ? k * 4 : 0}};
+    if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_rotate_quant(x, x_dtype, m, k, ldx, pre == QLIN_PRE_GEGLU, fold_inv_s,
+                                             had_block, bits, xq, x_scale, as_stream(stream)));
+}
+
+qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                           int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true);
+}
+
+qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                           int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, false);
+}
+
+qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m, int64_t n,
+                            int64_t k, int32_t group, void* y, void* stream) {
+    if (m > 0 && (!x || !y)) return QLIN_ERR_NULL;
+    if (!wq || !w_scale) return QLIN_ERR_NULL;
+    if (group != 128) return QLIN_ERR_UNSUPPORTED;
+    if (m < 0 || m > 64 || n < 1 || k < group || (k % group) != 0) return QLIN_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y)) return QLIN_ERR_ALIGN;
+    const Span outs[1] = {{y, m * n * 2}};
+    const Span ins[3] = {{x, m * k * 2}, {wq, n * k / 2}, {w_scale, n * (k / group) * 2}};
+    if (any_overlap(outs, 1, ins, 3)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_gemv_w4a16(x, wq, w_scale, m, n, k, group, y, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal launchers of the qlin library (host side).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+int row_quant_lanes(int64_t k);
+int row_quant_chunks(int64_t k, int g);
+
+hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                               bool geglu, const float* mult, int had_block, int bits, void* q,
+                               float* scale, hipStream_t st);
+
+hipError_t launch_quant_groups_w4(const void* w, int dtype, int64_t n, int64_t k, void* q,
+                                  void* scale, hipStream_t st);
+
+hipError_t launch_calibrate_fold(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                 bool geglu, const void* w, int w_dtype, int64_t n, float* s,
+                                 float* inv_s, hipStream_t st);
+
+// Integer GEMM.  int4 == true: both operands are packed int4 codes.
+// ws: int32 workspace of splits * m * n elements when splits > 1.
+struct GemmPlan {
+    int bm, bn;     // block tile
+    int splits;     // split-K factor (1 = fused epilogue)
+    int64_t ws_bytes;
+};
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4);
+hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
+                       const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, void* y,
+                       int y_dtype, int32_t* ws, hipStream_t st);
+
+hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
+                             int64_t n, int64_t k, int group, void* y, hipStream_t st);
+
+}  // namespace qlin

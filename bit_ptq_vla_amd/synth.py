@@ -142,3 +142,19 @@ def weight(wl: Workload, proj: Proj, tag: str = "") -> torch.Tensor:
     """Float weights [proj.n][proj.k] of a workload's projection."""
     return normal_tensor(wl.seed, f"{wl.name}/{proj.name}/w{tag}", (proj.n, proj.k),
                          std=wl.w_std, dtype=wl.w_dtype)
+
+
+def random_codes(seed: int, name: str, rows: int, k: int, bits: int) -> torch.Tensor:
+    """Uniform random operand bytes for integer-GEMM tests: int8 codes in
+    [-127, 127] as int8 [rows][k], or arbitrary packed bytes (every nibble
+    value, -8 included) as uint8 [rows][k/2]."""
+    rng = rng_for(seed, name)
+    if bits == 8:
+        return torch.from_numpy(rng.integers(-127, 128, size=(rows, k), dtype=np.int8))
+    return torch.from_numpy(rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8))
+
+
+def random_scales(seed: int, name: str, n: int) -> torch.Tensor:
+    """Positive float32 scales spread over two decades."""
+    rng = rng_for(seed, name)
+    return torch.from_numpy((10.0 ** rng.uniform(-3, -1, size=n)).astype(np.float32))

@@ -1,0 +1,177 @@
+/*
+ * qlin.h -- C ABI of the MI355X (gfx950) quantized linear projection library.
+ *
+ * The projection follows the FoldQuantVLA abstract ("FoldQuantVLA: Native
+ * Low-Bit Quantization of Vision-Language-Action Models via Consistent
+ * Folding"): a per-input-channel scale fold, a block Hadamard rotation and
+ * dynamic per-token quantization of the activations, an integer GEMM against
+ * round-to-nearest per-output-channel int4/int8 weights, and a dequantizing
+ * epilogue; attention-output and FFN-down projections may run at W8A8 while
+ * the rest run at W4A4.  The block form of the rotation follows the
+ * Omega-QVLA technical summary (Metodologia 1, "Implementazione a Blocchi").
+ * The weight-only W4A16 GEMV is the batch-1 memory-bound case of the LoopQ
+ * abstract ("LoopQ: Fair, Closed-Loop Evaluation of Quantized
+ * Vision-Language-Action Models").
+ *
+ * Conventions for every entry point
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  Matrices are
+ *    row-major; W is [n][k] (output channel n, input channel k), so the
+ *    projection is Y[m][n] = sum_k X[m][k] * W[n][k].
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Work is enqueued on it; no entry point synchronizes the device.
+ *  - Arguments are validated on the host before any HIP call.  On an error
+ *    the status is returned and no output is touched.  Asynchronous device
+ *    faults surface at the caller's next synchronization.
+ *  - Every device pointer must be 16-byte aligned; row pitches (ld*) are in
+ *    elements and must keep each row 16-byte aligned.  Outputs must not
+ *    overlap inputs.
+ *  - m == 0 (no tokens) is a valid empty call: QLIN_OK, nothing launched.
+ *  - Entry points are thread-safe.  qlin_gemm_* may take device memory for
+ *    split-K partial sums from the stream-ordered allocator
+ *    (hipMallocAsync/hipFreeAsync on `stream`); no other entry point
+ *    allocates.
+ *  - Codes: int8 codes are int8_t[rows][k]; int4 codes are packed two per
+ *    byte, uint8_t[rows][k/2], element 2j in the low nibble and 2j+1 in the
+ *    high nibble, two's complement.  Both grids are symmetric: codes lie in
+ *    [-7, 7] or [-127, 127].
+ *  - Rounding is round-half-to-even everywhere (codes and fp16/bf16 outputs).
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLIN_ABI_VERSION 1
+
+typedef int32_t qlin_status;
+enum {
+    QLIN_OK = 0,
+    QLIN_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    QLIN_ERR_SHAPE = 2,       /* sizes violate a stated precondition              */
+    QLIN_ERR_DTYPE = 3,       /* dtype not accepted for this argument             */
+    QLIN_ERR_ALIGN = 4,       /* pointer or row pitch not 16-byte aligned         */
+    QLIN_ERR_UNSUPPORTED = 5, /* bits / block / group / pre-op value not supported */
+    QLIN_ERR_DEVICE = 6,      /* no usable gfx950 device / HIP runtime error      */
+    QLIN_ERR_LAUNCH = 7,      /* kernel launch failed (hipGetLastError)           */
+    QLIN_ERR_ALIAS = 8        /* an output overlaps an input                      */
+};
+
+typedef int32_t qlin_dtype;
+enum { QLIN_F16 = 0, QLIN_BF16 = 1, QLIN_F32 = 2, QLIN_I32 = 3 };
+
+typedef int32_t qlin_preop;
+enum { QLIN_PRE_NONE = 0, QLIN_PRE_GEGLU = 1 };
+
+/* Version of this ABI (QLIN_ABI_VERSION). */
+int32_t qlin_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char* qlin_status_string(qlin_status s);
+
+/*
+ * qlin_calibrate_fold -- per-input-channel fold vector of the channel-scale
+ * fold (FoldQuantVLA abstract, "channel scaling"; the balance point
+ * s_j = sqrt(max_m |X[m][j]| / max_n |W[n][j]|) is the formula taken).
+ *
+ *   x        [m][ldx] activations, x_dtype F16/BF16/F32.  With pre == GEGLU a
+ *            row holds [gate | up] (2k values, ldx >= 2k) and the channel
+ *            maximum is taken over gelu(gate) * up (exact erf GeLU, fp32).
+ *   w        [n][k] weights, w_dtype F16/BF16/F32 (channel j is column j).
+ *   s        out float[k]: s_j in fp32 (1 where either maximum is 0).
+ *   inv_s    out float[k]: 1 / s_j rounded to fp32.
+ * Preconditions: m, n, k >= 1; k % 8 == 0; ldx % 8 == 0 and ldx >= k (2k
+ * with GEGLU).  This is an offline calibration step, not part of the timed
+ * projection.
+ */
+qlin_status qlin_calibrate_fold(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                int64_t ldx, qlin_preop pre, const void* w, qlin_dtype w_dtype,
+                                int64_t n, float* s, float* inv_s, void* stream);
+
+/*
+ * qlin_quantize_weights -- offline weight quantization.
+ *
+ * group == 0 (W4A4 / W8A8 weights, FoldQuantVLA abstract "weight rounding"):
+ *   w_hat = (w * fold_s) @ blockdiag(H_b / sqrt(b)) row by row, then per
+ *   output channel n: w_scale[n] = fp32(max_k |w_hat[n][k]| / qmax),
+ *   code = clamp(rne(w_hat / w_scale[n]), -qmax, qmax); qmax = 7 or 127.
+ *   w_scale is float[n].  A zero row gives scale 0 and codes 0.
+ * group == 128 (W4A16, LoopQ abstract: plain round-to-nearest, 4-bit
+ *   weight-only): bits must be 4, fold_s NULL and had_block 0 or 1.  Per row n
+ *   and group g: s16 = fp16_rne(max |w| / 7) over the group's 128 inputs,
+ *   code = clamp(rne(w / s16), -7, 7); w_scale is uint16_t (fp16) [n][k/128].
+ *
+ *   w        [n][k] float weights, w_dtype F16/BF16/F32, contiguous.
+ *   fold_s   float[k] fold vector or NULL (no fold).
+ *   had_block Hadamard block b: 0 or 1 = none, else a power of two <= 256
+ *            dividing k.  Sylvester (natural) order, orthonormal.
+ *   bits     4 or 8.   wq: out codes (layout above).
+ * Preconditions: n, k >= 1; k % 8 == 0; k % group == 0.
+ */
+qlin_status qlin_quantize_weights(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                  const float* fold_s, int32_t had_block, int32_t bits,
+                                  int32_t group, void* wq, void* w_scale, void* stream);
+
+/*
+ * qlin_rotate_quant_act -- the online activation stage (FoldQuantVLA
+ * abstract: channel scaling + block Hadamard + dynamic per-token
+ * quantization).  Per token row m:
+ *   v = (pre(x[m]) * fold_inv_s) @ blockdiag(H_b / sqrt(b));
+ *   x_scale[m] = fp32(max_k |v| / qmax); xq = clamp(rne(v / x_scale[m]), +-qmax).
+ *   pre == NONE : x holds [m][ldx] with the k inputs first in each row.
+ *   pre == GEGLU: x holds [gate | up] (2k values per row, ldx >= 2k) and
+ *                 v is computed from gelu(gate) * up (exact erf form, fp32).
+ *   x_dtype F16/BF16/F32; fold_inv_s float[k] (1/s) or NULL;
+ *   had_block 0/1 = none, else a power of two <= 256 dividing k; bits 4 or 8.
+ *   xq: out codes [m][k] int8 or [m][k/2] packed int4; x_scale: out float[m].
+ *   A zero row gives scale 0 and codes 0.
+ * Preconditions: k >= 8, k % 8 == 0; ldx % 8 == 0.
+ */
+qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                  int64_t ldx, qlin_preop pre, const float* fold_inv_s,
+                                  int32_t had_block, int32_t bits, void* xq, float* x_scale,
+                                  void* stream);
+
+/*
+ * qlin_gemm_w4a4 / qlin_gemm_w8a8 -- integer GEMM with int32 accumulation
+ * and a fused dequantizing epilogue (FoldQuantVLA abstract: native integer
+ * execution of the projections).
+ *   acc[m][n] = sum_k xq[m][k] * wq[n][k]   (exact, int32)
+ *   y[m][n]   = round_{y_dtype}(fp32(acc) * x_scale[m] * w_scale[n])
+ * Per-head or per-layer calibration scalars (QuantVLA technical summary,
+ * Methodology B and C) are expected pre-multiplied into w_scale.
+ *   xq, wq   codes as produced by qlin_rotate_quant_act / qlin_quantize_weights
+ *            (packed int4 for w4a4, int8 for w8a8), contiguous rows of k.
+ *   y_dtype  F16, BF16, F32, or I32 (raw accumulators; the scales may then be NULL).
+ *   y        out [m][n] contiguous.
+ * Preconditions: m >= 0, n >= 1; k >= 64 and k % 64 == 0; k * qmax^2 < 2^31
+ * (k <= 133152 for w8a8).
+ */
+qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq,
+                           const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                           qlin_dtype y_dtype, void* stream);
+qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
+                           const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                           qlin_dtype y_dtype, void* stream);
+
+/*
+ * qlin_gemv_w4a16 -- weight-only int4 projection for small batches (LoopQ
+ * abstract: batch-1 weight-only kernels of the memory-bound action expert).
+ *   y[m][n] = fp16_rne( sum_k x[m][k] * code[n][k] * s16[n][k / group] ),
+ *   products and sums in fp32.
+ *   x        [m][k] fp16, contiguous.   wq: packed int4 [n][k/2].
+ *   w_scale  fp16 [n][k/group] (uint16_t storage).   y: out fp16 [m][n].
+ * Preconditions: 1 <= m <= 64 (m == 0 is an empty call); n >= 1;
+ * group == 128; k % group == 0.
+ */
+qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
+                            int64_t n, int64_t k, int32_t group, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

@@ -1,0 +1,331 @@
+"""Stage-wise parity of the HIP path against the CPU oracle (GPU only).
+
+Each GPU stage is compared with the oracle run on that stage's GPU inputs:
+codes equal up to boundary flips, scales to 1e-6, integer accumulators
+bit-exact, fp16/bf16/f32 outputs within 1e-2 max / 1e-3 RMS of the oracle's
+fp32 result rounded to the output dtype.
+
+Method: FoldQuantVLA abstract (fold, block Hadamard, per-token dynamic
+quantization, W4A4/W8A8 integer GEMM); LoopQ abstract (RTN, W4A16 GEMV).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_ptq_vla_amd as q
+import oracle
+from bit_ptq_vla_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SEED = 1234
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def codes_np(t: torch.Tensor, bits: int) -> np.ndarray:
+    a = t.cpu().numpy()
+    return oracle.unpack_int4(a) if bits == 4 else a.astype(np.int64)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def assert_ok(res, what):
+    assert res.ok, f"{what}: {res.detail}"
+
+
+# ---------------------------------------------------------------- activation stage
+
+ACT_CASES = [
+    # m, k, b, bits, dtype, fold
+    (16, 512, 64, 4, "f16", True),      # single W4A4 linear
+    (37, 2048, 128, 4, "bf16", True),   # backbone hidden, ragged m
+    (5, 16384, 128, 8, "bf16", True),   # down-projection input width
+    (50, 1024, 64, 4, "f16", True),     # action-expert width
+    (3, 11008, 0, 8, "f16", False),     # no rotation, k not a power of two
+    (7, 64, 8, 4, "f32", True),
+    (33, 4096, 256, 8, "f16", True),
+    (2, 128, 2, 4, "bf16", False),
+    (300, 256, 128, 4, "bf16", True),   # several rows per block
+]
+
+
+@pytest.mark.parametrize("m,k,b,bits,dtype,fold", ACT_CASES)
+def test_rotate_quant_act_parity(m, k, b, bits, dtype, fold):
+    say(f"act m={m} k={k} b={b} bits={bits} {dtype} fold={fold}")
+    x = synth.normal_tensor(SEED, f"act/{m}/{k}/{b}", (m, k), dtype=dtype, outliers=max(1, k // 100),
+                            outlier_scale=25.0)
+    x[m // 2] = 0  # one all-zero token
+    s = None
+    if fold:
+        s = synth.random_scales(SEED, f"fold/{k}", k) * 100.0
+    xd = x.to(DEV)
+    inv_s = (1.0 / s).to(DEV) if fold else None
+    xq, xs = q.qlin_rotate_quant_act(xd, fold_inv_s=inv_s, had_block=b, bits=bits)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.rotate_quant_act(synth.to_f64(x), s.numpy() if fold else None, b, bits)
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), s_ref), "scales")
+    assert_ok(oracle.compare_codes(codes_np(xq, bits), q_ref, r_ref), "codes")
+    assert xs[m // 2].item() == 0.0 and np.all(codes_np(xq, bits)[m // 2] == 0)
+
+
+@pytest.mark.parametrize("m,k,dtype", [(9, 2048, "bf16"), (4, 16384, "bf16"), (6, 512, "f16")])
+def test_rotate_quant_act_geglu_parity(m, k, dtype):
+    say(f"act geglu m={m} k={k} {dtype}")
+    gu = synth.normal_tensor(SEED, f"geglu/{m}/{k}", (m, 2 * k), dtype=dtype)
+    s = synth.random_scales(SEED, f"gfold/{k}", k) * 100.0
+    xq, xs = q.qlin_rotate_quant_act(gu.to(DEV), k=k, fold_inv_s=(1.0 / s).to(DEV), had_block=128,
+                                     bits=8, pre=q.QLIN_PRE_GEGLU)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.rotate_quant_act(synth.to_f64(gu), s.numpy(), 128, 8, preop="geglu")
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), s_ref), "scales")
+    assert_ok(oracle.compare_codes(codes_np(xq, 8), q_ref, r_ref), "codes")
+
+
+def test_rotate_quant_act_strided_rows():
+    say("act strided ldx")
+    x = synth.normal_tensor(SEED, "strided", (12, 1536), dtype="f16")
+    view = x.to(DEV)[:, 256:1280]  # k = 1024 inside rows of 1536
+    xq, xs = q.qlin_rotate_quant_act(view, had_block=64, bits=4)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.rotate_quant_act(synth.to_f64(x)[:, 256:1280], None, 64, 4)
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), s_ref), "scales")
+    assert_ok(oracle.compare_codes(codes_np(xq, 4), q_ref, r_ref), "codes")
+
+
+# ---------------------------------------------------------------- weight stage
+
+WQ_CASES = [
+    (512, 512, 64, 4, "f16", True),
+    (300, 2048, 128, 4, "f16", True),
+    (64, 16384, 128, 8, "f16", True),
+    (257, 4096, 0, 8, "bf16", False),
+    (40, 1024, 64, 8, "f32", True),
+]
+
+
+@pytest.mark.parametrize("n,k,b,bits,dtype,fold", WQ_CASES)
+def test_quantize_weights_parity(n, k, b, bits, dtype, fold):
+    say(f"wq n={n} k={k} b={b} bits={bits} {dtype}")
+    w = synth.normal_tensor(SEED, f"w/{n}/{k}", (n, k), std=0.02, dtype=dtype)
+    w[3] = 0
+    s = synth.random_scales(SEED, f"wfold/{k}", k) * 100.0 if fold else None
+    wq, ws = q.qlin_quantize_weights(w.to(DEV), fold_s=s.to(DEV) if fold else None, had_block=b, bits=bits)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.quantize_weights(synth.to_f64(w), s.numpy() if fold else None, b, bits)
+    assert_ok(oracle.compare_scales(ws.cpu().numpy(), s_ref), "scales")
+    assert_ok(oracle.compare_codes(codes_np(wq, bits), q_ref, r_ref), "codes")
+
+
+@pytest.mark.parametrize("n,k,dtype", [(96, 4096, "f16"), (33, 11008, "f16"), (16, 256, "bf16")])
+def test_quantize_weights_group128_parity(n, k, dtype):
+    say(f"wq g128 n={n} k={k}")
+    w = synth.normal_tensor(SEED, f"wg/{n}/{k}", (n, k), std=0.015, dtype=dtype)
+    w[1, :128] = 0  # an all-zero group
+    wq, ws = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
+    torch.cuda.synchronize()
+    q_ref, s_ref, r_ref = oracle.quantize_weights(synth.to_f64(w), None, 0, 4, group=128)
+    assert np.array_equal(ws.cpu().numpy().view(np.uint16), s_ref.view(np.uint16)), "fp16 group scales differ"
+    assert_ok(oracle.compare_codes(codes_np(wq, 4), q_ref, r_ref), "codes")
+
+
+# ---------------------------------------------------------------- integer GEMM
+
+GEMM_SHAPES = [
+    (16, 512, 512),      # single linear
+    (300, 520, 1024),    # ragged M and N tiles
+    (50, 1024, 4096),
+    (64, 256, 16384),    # split-K
+    (1, 96, 128),        # one token
+    (257, 256, 2048),
+    (33, 64, 192),       # k % 128 == 64 (short last int4 stage)
+]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+@pytest.mark.parametrize("scheme", ["w4a4", "w8a8"])
+def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k):
+    say(f"gemm i32 {scheme} {m}x{n}x{k}")
+    bits = 4 if scheme == "w4a4" else 8
+    a = synth.random_codes(SEED, f"A/{m}/{k}/{bits}", m, k, bits)
+    b = synth.random_codes(SEED, f"B/{n}/{k}/{bits}", n, k, bits)
+    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
+    acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
+    torch.cuda.synchronize()
+    ref = oracle.int_gemm(codes_np(a, bits), codes_np(b, bits))
+    got = acc.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
+
+
+@pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("scheme,m,n,k", [("w4a4", 300, 520, 1024), ("w8a8", 129, 384, 4096),
+                                          ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512)])
+def test_gemm_dequant_epilogue(scheme, m, n, k, out):
+    say(f"gemm {out} {scheme} {m}x{n}x{k}")
+    bits = 4 if scheme == "w4a4" else 8
+    a = synth.random_codes(SEED, f"Ae/{m}/{k}/{bits}", m, k, bits)
+    b = synth.random_codes(SEED, f"Be/{n}/{k}/{bits}", n, k, bits)
+    sx = synth.random_scales(SEED, f"sx/{m}", m)
+    sw = synth.random_scales(SEED, f"sw/{n}", n)
+    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
+    y = fn(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, y_dtype=DT[out])
+    torch.cuda.synchronize()
+    _, _, y_ref = oracle.gemm(codes_np(a, bits), sx.numpy(), codes_np(b, bits), sw.numpy(), out)
+    assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+
+
+def test_gemm_deterministic():
+    say("gemm determinism")
+    a = synth.random_codes(SEED, "Ad", 129, 16384, 8).to(DEV)
+    b = synth.random_codes(SEED, "Bd", 256, 16384, 8).to(DEV)
+    sx = synth.random_scales(SEED, "sxd", 129).to(DEV)
+    sw = synth.random_scales(SEED, "swd", 256).to(DEV)
+    y1 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384)
+    y2 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- W4A16 GEMV
+
+GEMV_CASES = [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (3, 520, 1024), (50, 1024, 4096),
+              (64, 256, 256), (17, 1000, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMV_CASES)
+def test_gemv_w4a16_parity(m, n, k):
+    say(f"gemv {m}x{n}x{k}")
+    x = synth.normal_tensor(SEED, f"gx/{m}/{k}", (m, k), dtype="f16")
+    w = synth.normal_tensor(SEED, f"gw/{n}/{k}", (n, k), std=0.015, dtype="f16")
+    wq, ws = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
+    y = q.qlin_gemv_w4a16(x.to(DEV), wq, ws)
+    torch.cuda.synchronize()
+    y32, y_ref = oracle.gemv_w4a16(synth.to_f64(x), codes_np(wq, 4), ws.cpu().numpy(), 128)
+    assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+
+
+# ---------------------------------------------------------------- fold calibration
+
+
+@pytest.mark.parametrize("pre", [q.QLIN_PRE_NONE, q.QLIN_PRE_GEGLU])
+def test_calibrate_fold_parity(pre):
+    say(f"calibrate pre={pre}")
+    m, k, n = 100, 2048, 300
+    width = 2 * k if pre == q.QLIN_PRE_GEGLU else k
+    x = synth.normal_tensor(SEED, f"cx/{pre}", (m, width), dtype="bf16", outliers=20, outlier_scale=30.0)
+    w = synth.normal_tensor(SEED, f"cw/{pre}", (n, k), std=0.02, dtype="f16")
+    x[:, 5] = 0  # channel with zero maximum -> s = 1
+    if pre == q.QLIN_PRE_GEGLU:
+        x[:, k + 5] = 0
+    s, inv_s = q.qlin_calibrate_fold(x.to(DEV), w.to(DEV), pre=pre)
+    torch.cuda.synchronize()
+    xf = synth.to_f64(x)
+    act = oracle.geglu(xf, k) if pre == q.QLIN_PRE_GEGLU else xf
+    s_ref = oracle.calibrate_fold(act, synth.to_f64(w))
+    assert_ok(oracle.compare_scales(s.cpu().numpy(), s_ref), "fold s")
+    assert s.cpu().numpy()[5] == 1.0
+    np.testing.assert_array_equal(inv_s.cpu().numpy(), (np.float32(1.0) / s.cpu().numpy()).astype(np.float32))
+
+
+# ---------------------------------------------------------------- whole projections
+
+
+def test_single_w4a4_linear_end_to_end():
+    """16x512x512, 4 outlier channels x20, W ~ N(0, 0.02), fold, b = 64, W4A4, fp16 out."""
+    wl = synth.CFG1
+    proj = wl.projs[0]
+    say("single W4A4 linear")
+    x = synth.activation(wl, proj, 16)
+    w = synth.weight(wl, proj)
+    xd, wd = x.to(DEV), w.to(DEV)
+    s, inv_s = q.qlin_calibrate_fold(xd, wd)
+    wq, ws = q.qlin_quantize_weights(wd, fold_s=s, had_block=64, bits=4)
+    xq, xs = q.qlin_rotate_quant_act(xd, fold_inv_s=inv_s, had_block=64, bits=4)
+    y = q.qlin_gemm_w4a4(xq, xs, wq, ws, 512, y_dtype=torch.float16)
+    torch.cuda.synchronize()
+    xf, wf = synth.to_f64(x), synth.to_f64(w)
+    s_ref = oracle.calibrate_fold(xf, wf)
+    assert_ok(oracle.compare_scales(s.cpu().numpy(), s_ref), "fold")
+    sg = s.cpu().numpy()
+    qw_ref, sw_ref, rw = oracle.quantize_weights(wf, sg, 64, 4)
+    assert_ok(oracle.compare_codes(codes_np(wq, 4), qw_ref, rw), "weight codes")
+    assert_ok(oracle.compare_scales(ws.cpu().numpy(), sw_ref), "weight scales")
+    qx_ref, sx_ref, rx = oracle.rotate_quant_act(xf, sg, 64, 4)
+    assert_ok(oracle.compare_codes(codes_np(xq, 4), qx_ref, rx), "act codes")
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), sx_ref), "act scales")
+    acc, _, y_ref = oracle.gemm(codes_np(xq, 4), xs.cpu().numpy(), codes_np(wq, 4), ws.cpu().numpy(), "f16")
+    assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+    # the quantized projection approximates the float one (reported bound, generous)
+    ref = xf @ wf.T
+    assert np.linalg.norm(f64(y) - ref) / np.linalg.norm(ref) < 0.35
+
+
+def _sample_rows(m, count, seed=7):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(m, size=min(count, m), replace=False).tolist())
+    rows.update({0, m - 1})
+    return np.array(sorted(rows))
+
+
+@pytest.mark.slow
+def test_backbone_mlp_block_stagewise_full_size():
+    """M = 816 backbone MLP block at full size: gate|up W4A4 (N = 32768,
+    K = 2048) -> GeGLU pre-op -> int8 -> down W8A8 (N = 2048, K = 16384),
+    bf16, b = 128.  Launch configuration as timed by the benchmark; sampled
+    rows are checked stage by stage."""
+    wl = synth.CFG2
+    gu, dn = wl.projs
+    m = 816
+    say("backbone MLP block: generate")
+    x = synth.activation(wl, gu, m)
+    w_gu = synth.weight(wl, gu)
+    w_dn = synth.weight(wl, dn)
+    xd, wgd, wdd = x.to(DEV), w_gu.to(DEV), w_dn.to(DEV)
+    say("backbone MLP block: gpu path")
+    s1, inv1 = q.qlin_calibrate_fold(xd, wgd)
+    wq1, ws1 = q.qlin_quantize_weights(wgd, fold_s=s1, had_block=128, bits=4)
+    xq1, xs1 = q.qlin_rotate_quant_act(xd, fold_inv_s=inv1, had_block=128, bits=4)
+    y1 = q.qlin_gemm_w4a4(xq1, xs1, wq1, ws1, 2048, y_dtype=torch.bfloat16)
+    s2, inv2 = q.qlin_calibrate_fold(y1, wdd, pre=q.QLIN_PRE_GEGLU)
+    wq2, ws2 = q.qlin_quantize_weights(wdd, fold_s=s2, had_block=128, bits=8)
+    hq, hs = q.qlin_rotate_quant_act(y1, k=16384, fold_inv_s=inv2, had_block=128, bits=8, pre=q.QLIN_PRE_GEGLU)
+    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, 16384, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    say("backbone MLP block: oracle checks")
+    xf = synth.to_f64(x)
+    s1g = s1.cpu().numpy()
+    assert_ok(oracle.compare_scales(s1g, oracle.calibrate_fold(xf, synth.to_f64(w_gu))), "fold gate|up")
+    rows_w = _sample_rows(32768, 48)
+    qw, sw, rw = oracle.quantize_weights(synth.to_f64(w_gu[rows_w]), s1g, 128, 4)
+    assert_ok(oracle.compare_codes(codes_np(wq1, 4)[rows_w], qw, rw), "gate|up weight codes")
+    assert_ok(oracle.compare_scales(ws1.cpu().numpy()[rows_w], sw), "gate|up weight scales")
+    rows = _sample_rows(m, 6)
+    qx, sx, rx = oracle.rotate_quant_act(xf[rows], s1g, 128, 4)
+    assert_ok(oracle.compare_codes(codes_np(xq1, 4)[rows], qx, rx), "act codes")
+    assert_ok(oracle.compare_scales(xs1.cpu().numpy()[rows], sx), "act scales")
+    xq1n, wq1n = codes_np(xq1, 4), codes_np(wq1, 4)
+    _, _, y1_ref = oracle.gemm(xq1n[rows], xs1.cpu().numpy()[rows], wq1n, ws1.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(y1)[rows], y1_ref), "gate|up output")
+    y1f = f64(y1)
+    s2g = s2.cpu().numpy()
+    assert_ok(oracle.compare_scales(s2g, oracle.calibrate_fold(oracle.geglu(y1f, 16384), synth.to_f64(w_dn))),
+              "fold down")
+    rows_d = _sample_rows(2048, 12)
+    qw2, sw2, rw2 = oracle.quantize_weights(synth.to_f64(w_dn[rows_d]), s2g, 128, 8)
+    assert_ok(oracle.compare_codes(codes_np(wq2, 8)[rows_d], qw2, rw2), "down weight codes")
+    qh, sh, rh = oracle.rotate_quant_act(y1f[rows], s2g, 128, 8, preop="geglu")
+    assert_ok(oracle.compare_codes(codes_np(hq, 8)[rows], qh, rh), "GeGLU act codes")
+    assert_ok(oracle.compare_scales(hs.cpu().numpy()[rows], sh), "GeGLU act scales")
+    _, _, y2_ref = oracle.gemm(codes_np(hq, 8)[rows], hs.cpu().numpy()[rows], codes_np(wq2, 8),
+                               ws2.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(y2)[rows], y2_ref), "down output")
