@@ -22,6 +22,22 @@
 
 namespace qlin {
 
+// Round-half-even of v / scale, clamped to +-qmax.  The fast path multiplies
+// by an fp32 reciprocal (relative error ~1.5 ulp); when that product lies
+// within 1e-5 * max(1, |r|) of a half-integer, the quotient is recomputed in
+// float64 so that the rounding decision is taken on the correctly rounded
+// value: with exact inputs (no fold, no rotation) the codes then match a
+// float64 reference exactly.  `div` is the exact divisor (scale * sqrt(b)).
+__device__ __forceinline__ float quant_code(float v, float mul, double div, float qmax) {
+    const float r = v * mul;
+    float q = __builtin_rintf(r);
+    const float d = fabsf(fabsf(r - q) - 0.5f);
+    if (d <= 1e-5f * fmaxf(1.f, fabsf(r))) {
+        q = static_cast<float>(__builtin_rint(static_cast<double>(v) / div));
+    }
+    return fminf(fmaxf(q, -qmax), qmax);
+}
+
 struct RowQuantParams {
     const void* x;
     int64_t m, k, ldx;
@@ -142,6 +158,7 @@ __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(RowQuantParams p
     const float amax_n = amax * nrm;
     const float scale = amax_n / qmax;
     const float mul = (scale > 0.f) ? nrm * (1.f / scale) : 0.f;
+    const double div = static_cast<double>(scale) * sqrt(static_cast<double>(b));
     if (t == 0) p.scale[row] = scale;
 
 #pragma unroll
@@ -150,11 +167,7 @@ __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(RowQuantParams p
         if (c >= p.nch || col >= p.k) continue;
         int qv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float r = __builtin_rintf(v[c][e] * mul);
-            r = fminf(fmaxf(r, -qmax), qmax);
-            qv[e] = static_cast<int>(r);
-        }
+        for (int e = 0; e < 8; ++e) qv[e] = static_cast<int>(quant_code(v[c][e], mul, div, qmax));
         if (p.bits == 8) {
             uint32_t lo = (qv[0] & 0xFF) | ((qv[1] & 0xFF) << 8) | ((qv[2] & 0xFF) << 16) |
                           (static_cast<uint32_t>(qv[3] & 0xFF) << 24);
@@ -220,9 +233,8 @@ __global__ __launch_bounds__(256) void quant_groups_w4_kernel(GroupQuantParams p
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float r = __builtin_rintf(v[i] * mul);
-        r = fminf(fmaxf(r, -7.f), 7.f);
-        w |= static_cast<uint32_t>(static_cast<int>(r) & 0xF) << (4 * i);
+        const int c = static_cast<int>(quant_code(v[i], mul, static_cast<double>(s), 7.f));
+        w |= static_cast<uint32_t>(c & 0xF) << (4 * i);
     }
     *reinterpret_cast<uint32_t*>(p.q + e0 / 2) = w;
     if ((threadIdx.x & 15) == 0) p.scale[e0 / 128] = s16;

@@ -38,7 +38,6 @@ namespace qlin {
 namespace {
 
 constexpr int STAGE_BYTES = 64;   // bytes of one row per pipeline stage
-constexpr int LDS_PITCH = 80;     // padded LDS row pitch in bytes
 
 struct GemmParams {
     const int8_t* a;      // [m][kbytes]
@@ -111,14 +110,199 @@ __device__ __forceinline__ void write_tile(const v16i (&acc)[TM][TN], const Gemm
     }
 }
 
-template <int BM, int BN, bool INT4, int OUT>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(GemmParams p) {
-    constexpr int TM = BM / 64;            // MFMA tiles per wave along M
-    constexpr int TN = BN / 64;            // ... along N
-    constexpr int ALD = BM * 4 / 256;      // 16-byte loads per lane per stage (A)
-    constexpr int BLD = BN * 4 / 256;
-    __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * LDS_PITCH];
-    __shared__ __attribute__((aligned(16))) int8_t lds_b[2][BN * LDS_PITCH];
+// LDS layout of one pipeline stage: row r of a tile holds 64 bytes as four
+// 16-byte chunks; chunk c is stored at chunk slot c ^ swz(r).  A 16-byte read
+// of chunk c by 8 (or 16) consecutive rows then touches distinct bank groups
+// whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Waits until at most N of this wave's vector-memory operations (here: the
+// DMA loads into LDS) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else static_assert(N == 0, "unsupported count");
+}
+
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, num_records
+// in bytes, dword 3 = data format 32 (raw byte addressing).
+__device__ __forceinline__ v4i make_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const int64_t n = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return v4i{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu),
+               static_cast<int>(n), 0x00020000};
+}
+
+// 16-byte load of every lane from rsrc + voff straight into LDS at
+// lds_addr + 16 * lane (LDS DMA through M0).  Offsets at or past num_records
+// fetch nothing.  Written as inline assembly so that the compiler does not
+// add its own conservative waits on LDS reads behind it: the caller orders
+// the DMA with explicit s_waitcnt vmcnt + s_barrier.  The instruction has no
+// register result; its address operand is read at issue.
+__device__ __forceinline__ void dma16(v4i rsrc, int voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds_addr)
+        : "memory", "m0");
+}
+
+// Stores a wave's (BM/2) x (BN/2) accumulator tile through LDS so that the
+// global writes are 16-byte, row-contiguous stores.  The wave owns one LDS
+// ring buffer (STAGE bytes) after the main loop.  Rows are staged RP at a
+// time; the staged row pitch is padded (16 B for 2-byte, 32 B for 4-byte
+// elements) so that the two half-waves, which write rows 4 apart, hit
+// different banks.  OUT: -1 raw int32 partial, I32 raw accumulators, else
+// the dequantized value acc * x_scale[row] * w_scale[col] rounded to OUT.
+template <int BM, int BN, bool INT4, int OUT, int STAGE>
+__device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
+                                               int64_t row0, int64_t col0, int lane, int8_t* region,
+                                               void* dst) {
+    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr bool FLOAT_OUT = (OUT == BF16 || OUT == F16 || OUT == F32);
+    constexpr int E = (OUT == BF16 || OUT == F16) ? 2 : 4;
+    constexpr int ROWB = WN * E;
+    constexpr int PITCH = ROWB + (E == 2 ? 16 : 32);
+    // staged rows per pass: the largest WM / 2^j that fits the buffer
+    constexpr int RP = (WM * PITCH <= STAGE) ? WM : (WM / 2 * PITCH <= STAGE) ? WM / 2
+                     : (WM / 4 * PITCH <= STAGE) ? WM / 4 : 32;
+    static_assert(RP >= 32 && WM % RP == 0, "staging does not fit");
+    constexpr int TPP = RP / 32;                        // MFMA row tiles per pass
+    constexpr int CPR = ROWB / 16;                      // 16-byte chunks per row
+    const int l32 = lane & 31, half = lane >> 5;
+
+    // scales through buffer loads: out-of-range rows / columns read as 0
+    const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sx), 0, static_cast<int>(FLOAT_OUT ? p.m * 4 : 0), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sw), 0, static_cast<int>(FLOAT_OUT ? p.n * 4 : 0), 0x00020000);
+    float swv[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        swv[j] = 0.f;
+        if constexpr (FLOAT_OUT)
+            swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs_w, static_cast<int>((col0 + j * 32 + l32) * 4), 0, 0));
+    }
+    const int64_t ldy = p.n;
+    const bool vec_ok = ((p.n * E) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+
+#pragma unroll
+    for (int pass = 0; pass < WM / RP; ++pass) {
+        // ---- accumulators -> LDS (MFMA layout: column lane%32, row 8(r/4) + 4(lane/32) + r%4)
+#pragma unroll
+        for (int ti = 0; ti < TPP; ++ti) {
+            const int i = pass * TPP + ti;
+            f4 sxv[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                sxv[g] = f4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (FLOAT_OUT)
+                    sxv[g] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rs_x, static_cast<int>((row0 + i * 32 + 8 * g + 4 * half) * 4), 0, 0));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = ti * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    int8_t* at = region + rl * PITCH + (j * 32 + l32) * E;
+                    int32_t a = acc[i][j][r];
+                    if constexpr (INT4) a >>= 8;
+                    if constexpr (FLOAT_OUT) {
+                        const float v = static_cast<float>(a) * sxv[r >> 2][r & 3] * swv[j];
+                        if constexpr (OUT == BF16) *reinterpret_cast<uint16_t*>(at) = f32_to_bf16_rne(v);
+                        else if constexpr (OUT == F16) *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(v);
+                        else *reinterpret_cast<float*>(at) = v;
+                    } else {
+                        *reinterpret_cast<int32_t*>(at) = a;
+                    }
+                }
+            }
+        }
+        // the wave's own LDS writes complete before it reads them back
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        // ---- LDS -> global, 16 bytes per lane
+#pragma unroll 4
+        for (int c = lane; c < RP * CPR; c += 64) {
+            const int rl = c / CPR, cc = c - rl * CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(region + rl * PITCH + cc * 16);
+            const int64_t gr = row0 + pass * RP + rl;
+            const int64_t gc = col0 + cc * (16 / E);
+            if (gr < p.m) {
+                char* out = static_cast<char*>(dst) + (gr * ldy + gc) * E;
+                if (vec_ok && gc + 16 / E <= p.n) {
+                    *reinterpret_cast<uint4*>(out) = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 16 / E; ++e) {
+                        if (gc + e < p.n) {
+                            if constexpr (E == 2)
+                                reinterpret_cast<uint16_t*>(out)[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+                            else
+                                reinterpret_cast<uint32_t*>(out)[e] = w[e];
+                        }
+                    }
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// One k-slice of MFMA work: 32 bytes of every row (32 int8 or 64 int4
+// codes) for the wave's TM x TN tiles.
+template <int TM, int TN, bool INT4>
+__device__ __forceinline__ void mma_slice(v16i (&acc)[TM][TN], const uint4 (&fa)[TM], const uint4 (&fb)[TN]) {
+    if constexpr (INT4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i oa[TM], ob[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                oa[i] = h == 0 ? unpack_lo(fa[i].x, fa[i].y, 0, 0) : unpack_lo(fa[i].z, fa[i].w, 0, 0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                ob[j] = h == 0 ? unpack_lo(fb[j].x, fb[j].y, 0, 0) : unpack_lo(fb[j].z, fb[j].w, 0, 0);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[i], ob[j], acc[i][j], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, fa[i]),
+                                                                  __builtin_bit_cast(v4i, fb[j]), acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int BM, int BN, int MINB, int NS, bool INT4, int OUT>
+__global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
+    // NS: pipeline stages (ring of LDS buffers)
+    constexpr int TM = BM / 64;                  // MFMA tiles per wave along M
+    constexpr int TN = BN / 64;                  // ... along N
+    constexpr int A_INSTR = BM / 64;             // 16-byte DMA loads per lane per stage (A)
+    constexpr int B_INSTR = BN / 64;
+    constexpr int LOADS = A_INSTR + B_INSTR;     // per lane per stage
+    constexpr int STAGE = (BM + BN) * STAGE_BYTES;
+    // The DMA is issued through inline assembly, invisible to the compiler,
+    // so one array serves the whole ring (and the epilogue staging after it).
+    __shared__ __attribute__((aligned(1024))) int8_t lds[NS * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -139,48 +323,33 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmParams p) {
     const int s_begin = split * p.stages_per_split;
     int s_end = s_begin + p.stages_per_split;
     if (s_end > p.stages) s_end = p.stages;
+    const int nst = s_end > s_begin ? s_end - s_begin : 0;
 
-    // Global loads go through buffer resources based at the tile's first
-    // row: rows past the end of the matrix fall outside num_records and read
-    // as zero, so ragged M / N tails need no clamping.  Lane tid loads row
-    // tid/4 (+64 per extra load) at byte (tid%4)*16 of the stage.
-    const int ld_row = tid >> 2;
-    const int ld_col = (tid & 3) * 16;
+    // Buffer resources based at the tile's first row: rows past the matrix
+    // are out of range (the hardware returns zeros, nothing is fetched).
     const int64_t a_rem = (p.m - m0) * p.kbytes;
     const int64_t b_rem = (p.n - n0) * p.kbytes;
-    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(p.a + m0 * p.kbytes), 0,
-        static_cast<int>(a_rem < 0x7FFFFFFF ? a_rem : 0x7FFFFFFF), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(p.b + n0 * p.kbytes), 0,
-        static_cast<int>(b_rem < 0x7FFFFFFF ? b_rem : 0x7FFFFFFF), 0x00020000);
-    const int a_voff = ld_row * static_cast<int>(p.kbytes) + ld_col;
-    const int row64 = 64 * static_cast<int>(p.kbytes);
-    const int lds_wr = ld_row * LDS_PITCH + ld_col;
+    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes, a_rem);
+    const v4i rsrc_b = make_rsrc(p.b + n0 * p.kbytes, b_rem);
 
-    uint4 ra[ALD], rb[BLD];
-    auto gload = [&](int s) {
-        const int kb = s * STAGE_BYTES;
-        // A short last stage (int4 with k % 128 == 64) must not read into the
-        // next row: its upper half gets offset 2^31, beyond every num_records.
-        const bool kin = kb + ld_col < p.kbytes;
-        const int off = a_voff + kb;
+    // DMA mapping: load instruction i of wave w fills LDS chunk slots
+    // [(4i + w) * 64, +64) of its operand, i.e. 16 rows; lane l fills slot
+    // P = (4i + w) * 64 + l = row (P >> 2), slot (P & 3), so it fetches the
+    // row's chunk (P & 3) ^ swz(row).
+    const int dma_row0 = wave * 16 + (lane >> 2);            // + 64 * i
+    const int dma_chunk = (lane & 3) ^ swz(dma_row0);        // swz(row + 64 i) == swz(row)
+    const int dma_voff = dma_row0 * static_cast<int>(p.kbytes) + dma_chunk * 16;
+    const int row64 = 64 * static_cast<int>(p.kbytes);
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int st, int8_t* buf) {
+        const int kb = (s_begin + st) * STAGE_BYTES;
+        const uint32_t a_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + wave_u * 1024;
+        const uint32_t b_dst = a_dst + BM * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < ALD; ++i)
-            ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rsrc_a, kin ? off + i * row64 : static_cast<int>(0x80000000u), 0, 0));
+        for (int i = 0; i < A_INSTR; ++i) dma16(rsrc_a, dma_voff + kb + i * row64, a_dst + i * 4096);
 #pragma unroll
-        for (int i = 0; i < BLD; ++i)
-            rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rsrc_b, kin ? off + i * row64 : static_cast<int>(0x80000000u), 0, 0));
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < ALD; ++i)
-            *reinterpret_cast<uint4*>(&lds_a[buf][lds_wr + i * 64 * LDS_PITCH]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < BLD; ++i)
-            *reinterpret_cast<uint4*>(&lds_b[buf][lds_wr + i * 64 * LDS_PITCH]) = rb[i];
+        for (int i = 0; i < B_INSTR; ++i) dma16(rsrc_b, dma_voff + kb + i * row64, b_dst + i * 4096);
     };
 
     v16i acc[TM][TN];
@@ -191,104 +360,126 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    // lane's LDS read offsets: row lane%32 of each 32-row tile, 16 bytes at
-    // byte (lane/32)*16 of each 32-byte k-slice
-    const int rd_row = lane & 31;
-    const int rd_col = (lane >> 5) * 16;
-    const int a_rd = (wm * (BM / 2) + rd_row) * LDS_PITCH + rd_col;
-    const int b_rd = (wn * (BN / 2) + rd_row) * LDS_PITCH + rd_col;
+    // MFMA operand reads: lane reads row (lane % 32) of each 32-row tile,
+    // chunk 2*ks + lane/32 of the stage's 64 bytes.
+    const int l32 = lane & 31;
+    const int hsel = lane >> 5;
+    const int sw = swz(l32);  // tile bases are multiples of 32: swz(base + l32) == swz(l32)
+    const int a_rd0 = (wm * (BM / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
+    const int a_rd1 = (wm * (BM / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
+    const int b_rd0 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
+    const int b_rd1 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
 
-    if (s_begin < s_end) {
-        gload(s_begin);
-        sstore(0);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int pst = 0; pst < NS - 1; ++pst)
+        if (pst < nst) issue(pst, lds + pst * STAGE);
 
-    for (int s = s_begin; s < s_end; ++s) {
-        const int buf = (s - s_begin) & 1;
-        if (s + 1 < s_end) gload(s + 1);
-        const int8_t* la = lds_a[buf];
-        const int8_t* lb = lds_b[buf];
+    // One stage of work from LDS buffer `st` (both 32-byte k-slices).
+    auto compute = [&](const int8_t* st) {
+        uint4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {   // two 32-byte slices per stage
-            uint4 fa[TM], fb[TN];
+        for (int i = 0; i < TM; ++i) fa0[i] = *reinterpret_cast<const uint4*>(st + a_rd0 + i * 32 * STAGE_BYTES);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[i] = *reinterpret_cast<const uint4*>(la + a_rd + i * 32 * LDS_PITCH + ks * 32);
+        for (int j = 0; j < TN; ++j) fb0[j] = *reinterpret_cast<const uint4*>(st + b_rd0 + j * 32 * STAGE_BYTES);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = *reinterpret_cast<const uint4*>(lb + b_rd + j * 32 * LDS_PITCH + ks * 32);
-            if constexpr (INT4) {
-                // 16 bytes = 32 codes per lane -> two MFMA operands
+        for (int i = 0; i < TM; ++i) fa1[i] = *reinterpret_cast<const uint4*>(st + a_rd1 + i * 32 * STAGE_BYTES);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    v4i oa[TM], ob[TN];
+        for (int j = 0; j < TN; ++j) fb1[j] = *reinterpret_cast<const uint4*>(st + b_rd1 + j * 32 * STAGE_BYTES);
+        mma_slice<TM, TN, INT4>(acc, fa0, fb0);
+        mma_slice<TM, TN, INT4>(acc, fa1, fb1);
+        // scheduling: the 2 * (TM + TN) LDS reads first, then the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
+        if constexpr (INT4) {
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        oa[i] = h == 0 ? unpack_lo(fa[i].x, fa[i].y, 0, 0) : unpack_lo(fa[i].z, fa[i].w, 0, 0);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        ob[j] = h == 0 ? unpack_lo(fb[j].x, fb[j].y, 0, 0) : unpack_lo(fb[j].z, fb[j].w, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[i], ob[j], acc[i][j], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        v4i oa = {static_cast<int>(fa[i].x), static_cast<int>(fa[i].y),
-                                  static_cast<int>(fa[i].z), static_cast<int>(fa[i].w)};
-                        v4i ob = {static_cast<int>(fb[j].x), static_cast<int>(fb[j].y),
-                                  static_cast<int>(fb[j].z), static_cast<int>(fb[j].w)};
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa, ob, acc[i][j], 0, 0, 0);
-                    }
+            for (int g = 0; g < 4 * TM * TN; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
             }
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
         }
-        if (s + 1 < s_end) sstore(buf ^ 1);
-        __syncthreads();
+    };
+    // Stage `it` has landed once at most min(NS-2, nst-1-it) later stages of
+    // this wave's DMA are outstanding; the barrier then publishes every
+    // wave's part and retires the reads of the buffer the next DMA reuses.
+    auto wait_stage = [&](int it) {
+        const int after = (nst - 1 - it) < (NS - 2) ? (nst - 1 - it) : (NS - 2);
+        if (NS >= 4 && after >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * LOADS>();
+        else if (after == 1) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // Whole groups of NS stages: the ring position is a compile-time constant.
+    const int nfull = nst - nst % NS;
+    for (int it0 = 0; it0 < nfull; it0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int it = it0 + u;
+            wait_stage(it);
+            if (it + NS - 1 < nst) issue(it + NS - 1, lds + ((u + NS - 1) % NS) * STAGE);
+            compute(lds + u * STAGE);
+        }
+    }
+    // Remaining stages (< NS); their DMA was issued by the loop above.
+    for (int it = nfull; it < nst; ++it) {
+        wait_stage(it);
+        const int u = it - nfull;
+        compute(lds + u * STAGE);
     }
 
-    // ---- epilogue ----
+    // ---- epilogue: every wave is done with the ring; each takes one buffer
+    __syncthreads();
     void* dst = (OUT == -1) ? static_cast<void*>(p.ws + static_cast<int64_t>(split) * p.m * p.n) : p.y;
-    write_tile<TM, TN, INT4, OUT>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane, dst);
+    constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
+    store_tile_lds<BM, BN, INT4, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                              lds + wave * REGION, dst);
 }
 
-// Sum of split-K partials in split order, then the epilogue.
+// Sum of split-K partials in split order (integer: bit-exact), then the
+// epilogue; four consecutive outputs per lane (n % 4 == 0), else one.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* ws, int splits, int64_t m,
                                                             int64_t n, const float* sx,
                                                             const float* sw, void* y, int y_dtype) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = m * n;
-    if (i >= total) return;
-    int32_t a = 0;
-    for (int s = 0; s < splits; ++s) a += ws[static_cast<int64_t>(s) * total + i];
-    if (y_dtype == I32) {
-        static_cast<int32_t*>(y)[i] = a;
-        return;
+    const bool vec = (n & 3) == 0;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * (vec ? 4 : 1);
+    if (i0 >= total) return;
+    const int cnt = vec ? 4 : 1;
+    int32_t a[4] = {0, 0, 0, 0};
+    for (int s = 0; s < splits; ++s) {
+        const int32_t* src = ws + static_cast<int64_t>(s) * total + i0;
+        if (vec) {
+            const int4 v = *reinterpret_cast<const int4*>(src);
+            a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
+        } else {
+            a[0] += src[0];
+        }
     }
-    const int64_t row = i / n, col = i - row * n;
-    store_out(y, i, y_dtype, static_cast<float>(a) * sx[row] * sw[col]);
+    const int64_t row = i0 / n;
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t i = i0 + e, col = i - row * n;
+        if (y_dtype == I32) static_cast<int32_t*>(y)[i] = a[e];
+        else store_out(y, i, y_dtype, static_cast<float>(a[e]) * sx[row] * sw[col]);
+    }
 }
 
-template <int BM, int BN, bool INT4, int OUT>
+template <int BM, int BN, int MINB, int NS, bool INT4, int OUT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t st) {
     dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n * p.splits));
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, INT4, OUT>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, MINB, NS, INT4, OUT>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool INT4>
+template <int BM, int BN, int MINB, int NS, bool INT4>
 hipError_t launch_out(const GemmParams& p, hipStream_t st) {
-    if (p.splits > 1) return launch_tile<BM, BN, INT4, -1>(p, st);
+    if (p.splits > 1) return launch_tile<BM, BN, MINB, NS, INT4, -1>(p, st);
     switch (p.y_dtype) {
-        case BF16: return launch_tile<BM, BN, INT4, BF16>(p, st);
-        case F16: return launch_tile<BM, BN, INT4, F16>(p, st);
-        case F32: return launch_tile<BM, BN, INT4, F32>(p, st);
-        case I32: return launch_tile<BM, BN, INT4, I32>(p, st);
+        case BF16: return launch_tile<BM, BN, MINB, NS, INT4, BF16>(p, st);
+        case F16: return launch_tile<BM, BN, MINB, NS, INT4, F16>(p, st);
+        case F32: return launch_tile<BM, BN, MINB, NS, INT4, F32>(p, st);
+        case I32: return launch_tile<BM, BN, MINB, NS, INT4, I32>(p, st);
     }
     return hipErrorInvalidValue;
 }
@@ -296,15 +487,22 @@ hipError_t launch_out(const GemmParams& p, hipStream_t st) {
 }  // namespace
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4) {
+    // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes
+    // per MFMA), two blocks per CU (one block's per-stage barrier and LDS
+    // latency is covered by the other block's MFMAs).
     GemmPlan g;
-    g.bm = (m > 128) ? 256 : 128;
-    g.bn = 256;
+    g.bm = 128;
+    g.bn = (n >= 4096) ? 256 : 128;
     const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
     const int64_t kbytes = int4 ? k / 2 : k;
     const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
+    constexpr int64_t kSlots = 512;  // 256 CUs x 2 resident blocks
     int splits = 1;
-    // fill the 256 CUs when the tile grid is small, keeping >= 8 stages per split
-    while (tiles * splits < 256 && stages / (splits * 2) >= 8) splits *= 2;
+    // split K only when the tile grid fills under half of the block slots,
+    // keeping at least 16 stages (1 KiB of k per row) in every split
+    if (tiles * 2 <= kSlots) {
+        while (tiles * splits * 2 <= kSlots && stages / (splits * 2) >= 16) splits *= 2;
+    }
     g.splits = splits;
     g.ws_bytes = (splits > 1) ? static_cast<int64_t>(splits) * m * n * 4 : 0;
     return g;
@@ -326,12 +524,13 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
     p.y_dtype = y_dtype;
     hipError_t e;
-    if (plan.bm == 256) e = int4 ? launch_out<256, 256, true>(p, st) : launch_out<256, 256, false>(p, st);
-    else e = int4 ? launch_out<128, 256, true>(p, st) : launch_out<128, 256, false>(p, st);
+    if (plan.bn == 256) e = int4 ? launch_out<128, 256, 2, 3, true>(p, st) : launch_out<128, 256, 2, 3, false>(p, st);
+    else e = int4 ? launch_out<128, 128, 2, 4, true>(p, st) : launch_out<128, 128, 2, 4, false>(p, st);
     if (e != hipSuccess) return e;
     if (plan.splits > 1) {
         const int64_t total = m * n;
-        dim3 grid(static_cast<unsigned>((total + 255) / 256));
+        const int64_t per = (n % 4 == 0) ? 4 : 1;
+        dim3 grid(static_cast<unsigned>((total / per + 255) / 256));
         hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, ws, plan.splits, m, n,
                            x_scale, w_scale, y, y_dtype);
         e = hipGetLastError();

@@ -83,7 +83,9 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_F16 && y_dtype != QLIN_BF16 && y_dtype != QLIN_F32 && y_dtype != QLIN_I32)
         return QLIN_ERR_DTYPE;
-    if (m < 0 || n < 1 || k < 64 || (k % 64) != 0) return QLIN_ERR_SHAPE;
+    // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
+    const int64_t kstep = int4 ? 128 : 64;
+    if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return QLIN_ERR_SHAPE;
     if (k > 131072) return QLIN_ERR_SHAPE;  // keeps |acc| (and 256*acc for int4) below 2^31
     if (m > 0x7FFFFFFF || n > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))

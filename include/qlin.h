@@ -147,8 +147,9 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
  *            (packed int4 for w4a4, int8 for w8a8), contiguous rows of k.
  *   y_dtype  F16, BF16, F32, or I32 (raw accumulators; the scales may then be NULL).
  *   y        out [m][n] contiguous.
- * Preconditions: m >= 0, n >= 1; k >= 64 and k % 64 == 0; k * qmax^2 < 2^31
- * (k <= 133152 for w8a8).
+ * Preconditions: m >= 0, n >= 1; k a multiple of 64 (w8a8) or of 128 (w4a4),
+ * at least one such step; k <= 131072, which keeps every int32 accumulator
+ * exact.
  */
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq,
                            const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
