@@ -17,6 +17,8 @@
 // Also here: the W4A16 group quantizer (LoopQ abstract: plain RTN, 4-bit
 // weight-only) and the channel-maximum kernels of the fold calibration.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "qlin_internal.h"
 
@@ -50,137 +52,350 @@ struct RowQuantParams {
     float* scale;       // per-row scale out
 };
 
-template <int DT, bool GEGLU>
-__device__ __forceinline__ void load_row_chunk(const RowQuantParams& p, int64_t row, int64_t col,
-                                               float v[8]) {
-    const char* base = static_cast<const char*>(p.x);
-    constexpr int ES = (DT == F32) ? 4 : 2;
-    const char* r = base + (row * p.ldx + col) * ES;
-    if constexpr (GEGLU) {
-        float g[8], u[8];
-        load8<DT>(r, g);
-        load8<DT>(r + p.k * ES, u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = gelu_erf(g[i]) * u[i];
+// Cross-lane butterfly stages.  The true transform value t is carried as
+// w = sigma * t with a per-lane sign sigma.  At lane distance D the pair
+// (a, b) must become (a + b, a - b); with s = -1 on the lane whose D bit is
+// set and sigma equal on both lanes before the stage, w += s * w_partner
+// leaves w = sigma' * t' with sigma' = s * sigma.  So each stage is a single
+// multiply-add with the partner's value taken by DPP (D = 1, 2: quad
+// permutations; D = 8: row rotation by 8; D = 4: two half-row rotations,
+// each applied to the 4-lane banks it serves), and the final sign,
+// (-1)^popcount(lane & (b/8 - 1)), is folded into the quantization scale.
+// w += s * w[partner] for the 8 values of one chunk, the partner's value read
+// through DPP (the fused v_fmac_f32_dpp reads src0 from the partner lane).
+// The leading s_nop 1 gives the two wait states a DPP read needs after a
+// VALU write of its source; inside the block each instruction reads a
+// register no earlier instruction of the block wrote.
+#define QLIN_DPP_FMAC8(CTRL)                                                           \
+    asm("s_nop 1\n\t"                                                                  \
+        "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+        "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"               \
+        : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]),     \
+          "+v"(w[6]), "+v"(w[7])                                                       \
+        : "v"(sgn))
+
+// Lane distance 4: banks 0 and 2 of a 16-lane row take lane + 4 (rotation
+// by 12), banks 1 and 3 take lane - 4 (rotation by 4), into a temporary,
+// then one multiply-add.
+#define QLIN_DPP4_ONE(I)                                                               \
+    "v_mov_b32_dpp %9, %" #I " row_ror:12 row_mask:0xf bank_mask:0x5\n\t"              \
+    "v_mov_b32_dpp %9, %" #I " row_ror:4 row_mask:0xf bank_mask:0xa\n\t"               \
+    "v_fmac_f32_e32 %" #I ", %9, %8\n\t"
+
+template <int D>
+__device__ __forceinline__ void xlane8(float (&w)[8], float sgn) {
+    if constexpr (D == 1) {
+        QLIN_DPP_FMAC8("quad_perm:[1,0,3,2]");
+    } else if constexpr (D == 2) {
+        QLIN_DPP_FMAC8("quad_perm:[2,3,0,1]");
+    } else if constexpr (D == 8) {
+        QLIN_DPP_FMAC8("row_ror:8");
+    } else if constexpr (D == 4) {
+        float t;
+        asm("s_nop 1\n\t" QLIN_DPP4_ONE(0) QLIN_DPP4_ONE(1) QLIN_DPP4_ONE(2) QLIN_DPP4_ONE(3)
+                QLIN_DPP4_ONE(4) QLIN_DPP4_ONE(5) QLIN_DPP4_ONE(6) QLIN_DPP4_ONE(7)
+            : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]),
+              "+v"(w[7]), "+v"(sgn), "=&v"(t));
     } else {
-        load8<DT>(r, v);
+        // D = 16 crosses 16-lane rows: ds_swizzle
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = fmaf(lane_xor<D>(w[e]), sgn, w[e]);
     }
 }
 
-// Butterfly across lanes at distance MASK: lane with the bit clear keeps
-// a + b, lane with the bit set keeps a - b (a = lower-index element).
-template <int MASK, int NCH>
+template <int D, int NCH>
 __device__ __forceinline__ void xlane_stage(float (&v)[NCH][8], int lane) {
-    const bool upper = (lane & MASK) != 0;
+    const float sgn = (lane & D) ? -1.f : 1.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < NCH; ++c) xlane8<D>(v[c], sgn);
+}
+
+// ---- GeLU table for bfloat16 inputs ------------------------------------------
+// gelu(g) for every bfloat16 g with 2^-12 <= |g| < 8, both signs: 15 exponents
+// x 128 mantissas x 2 signs, evaluated once per device in float64 (erf) and
+// rounded to fp32.  Smaller |g| use 0.5 g + g^2 / sqrt(2 pi) (error below
+// 1e-11 relative); |g| >= 8 gives g (positive) or 0 (negative).
+constexpr int GELU_EF0 = 127 - 12;               // first tabulated exponent field
+constexpr int GELU_NEXP = 15;
+constexpr int GELU_HALF = GELU_NEXP * 128;       // tabulated entries per sign (1920)
+constexpr int GELU_TAB = 2 * 2048;               // sign selects a 2048-entry half
+__device__ float g_gelu_bf16_tab[GELU_TAB];
+
+__global__ void gelu_table_init_kernel() {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= GELU_TAB) return;
+    const int neg = i >= 2048;
+    const int j = i & 2047;
+    if (j >= GELU_HALF) {
+        g_gelu_bf16_tab[i] = 0.f;
+        return;
+    }
+    const uint32_t a = static_cast<uint32_t>(j + (GELU_EF0 << 7));
+    const float g = __uint_as_float((a | (neg ? 0x8000u : 0u)) << 16);
+    const double x = static_cast<double>(g);
+    g_gelu_bf16_tab[i] = static_cast<float>(0.5 * x * (1.0 + erf(x * 0.70710678118654752440)));
+}
+
+// gelu of a bfloat16 value outside the table: tiny |g| by its Taylor start,
+// |g| >= 8 as g or 0.
+__device__ __forceinline__ float gelu_bf16_edge(uint32_t bits) {
+    const float g = __uint_as_float(bits << 16);
+    if (((bits & 0x7FFFu) >> 7) < static_cast<uint32_t>(GELU_EF0))
+        return fmaf(g * g, 0.39894228040143267794f, 0.5f * g);
+    return g > 0.f ? g : 0.f;
+}
+
+// Eight gelu values of gate bits w[0..3] (two bfloat16 per word).
+__device__ __forceinline__ void gelu_bf16_8(const uint32_t w[4], const float* tab, float out[8]) {
+    uint32_t idx[8];
+    uint32_t worst = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float other = lane_xor<MASK>(v[c][e]);
-            v[c][e] = upper ? (other - v[c][e]) : (v[c][e] + other);
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        const uint32_t t = (bits & 0x7FFFu) - static_cast<uint32_t>(GELU_EF0 << 7);
+        worst = worst > t ? worst : t;
+        idx[i] = t | ((bits >> 4) & 0x800u);   // sign bit 15 -> table half (bit 11)
+    }
+    if (worst < static_cast<uint32_t>(GELU_HALF)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = tab[idx[i]];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+            const uint32_t t = (bits & 0x7FFFu) - static_cast<uint32_t>(GELU_EF0 << 7);
+            out[i] = t < static_cast<uint32_t>(GELU_HALF) ? tab[idx[i]] : gelu_bf16_edge(bits);
         }
     }
 }
 
-template <int DT, int NCH, bool GEGLU>
-__global__ __launch_bounds__(256) void rotate_quant_rows_kernel(RowQuantParams p) {
-    __shared__ float red[4];
+// 8 consecutive values of a row (GeGLU: gelu(gate) * up) from their raw
+// 16-byte words: raw[0] holds the values (or the gate), raw[1] the up-half.
+template <int DT>
+__device__ __forceinline__ void decode8(const uint4* w, float f[8]) {
+    if constexpr (DT == F32) {
+        const float4 a = __builtin_bit_cast(float4, w[0]), b = __builtin_bit_cast(float4, w[1]);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+        const uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == BF16) {
+                f[2 * i] = __uint_as_float(u[i] << 16);
+                f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+            } else {
+                f[2 * i] = f16_bits_to_f32(static_cast<uint16_t>(u[i] & 0xFFFFu));
+                f[2 * i + 1] = f16_bits_to_f32(static_cast<uint16_t>(u[i] >> 16));
+            }
+        }
+    }
+}
+
+template <int DT, bool GEGLU, int SRC, int W>
+__device__ __forceinline__ void decode_chunk(const uint4 (&raw)[SRC][W], const float* gtab, float v[8]) {
+    if constexpr (GEGLU && DT == BF16) {
+        const uint32_t w[4] = {raw[0][0].x, raw[0][0].y, raw[0][0].z, raw[0][0].w};
+        float gl[8], u[8];
+        gelu_bf16_8(w, gtab, gl);
+        decode8<DT>(raw[1], u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = gl[i] * u[i];
+    } else if constexpr (GEGLU) {
+        float gg[8], u[8];
+        decode8<DT>(raw[0], gg);
+        decode8<DT>(raw[1], u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = gelu_erf(gg[i]) * u[i];
+    } else {
+        decode8<DT>(raw[0], v);
+    }
+}
+
+// Packs eight codes held as the low bits of magic-biased floats (see below):
+// int8 -> two dwords of bytes, int4 -> one dword of nibbles (element 2j in the
+// low nibble of byte j).  v_perm_b32 gathers byte 0 of its two sources.
+__device__ __forceinline__ uint2 pack8_i8(const uint32_t cb[8]) {
+    const uint32_t a = __builtin_amdgcn_perm(cb[1], cb[0], 0x0C0C0400u);
+    const uint32_t b = __builtin_amdgcn_perm(cb[3], cb[2], 0x04000C0Cu);
+    const uint32_t c = __builtin_amdgcn_perm(cb[5], cb[4], 0x0C0C0400u);
+    const uint32_t d = __builtin_amdgcn_perm(cb[7], cb[6], 0x04000C0Cu);
+    return make_uint2(a | b, c | d);
+}
+
+__device__ __forceinline__ uint32_t pack8_i4(const uint32_t cb[8]) {
+    // even elements -> bytes of E, odd elements -> bytes of O, then nibbles
+    const uint32_t e = __builtin_amdgcn_perm(cb[2], cb[0], 0x0C0C0400u) |
+                       __builtin_amdgcn_perm(cb[6], cb[4], 0x04000C0Cu);
+    const uint32_t o = __builtin_amdgcn_perm(cb[3], cb[1], 0x0C0C0400u) |
+                       __builtin_amdgcn_perm(cb[7], cb[5], 0x04000C0Cu);
+    return (e & 0x0F0F0F0Fu) | ((o << 4) & 0xF0F0F0F0u);
+}
+
+// Rows of k values; TPB lanes per block, g lanes per row (g <= TPB, RPB =
+// TPB / g rows per block and iteration), NCH chunk passes of 8 values per
+// lane.  Block i handles row groups i, i + grid, ... (the launcher gives one
+// group per block: occupancy hides the load latency better than keeping a
+// prefetched group in registers).  All of a group's loads are issued before
+// any value is used.
+template <int DT, int NCH, bool GEGLU, int TPB>
+__global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_kernel(RowQuantParams p) {
+    constexpr int NW = TPB / 64;
+    __shared__ float red[NW];
+    constexpr bool LUT = GEGLU && DT == BF16;
+    __shared__ float gtab[LUT ? GELU_TAB : 1];
+    if constexpr (LUT) {
+        for (int i = threadIdx.x; i < GELU_TAB; i += TPB) gtab[i] = g_gelu_bf16_tab[i];
+        __syncthreads();
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int g = p.g;
-    const int rows_per_block = 256 / g;
+    const int rpb = TPB / g;
     const int t = tid & (g - 1);
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * rows_per_block + tid / g;
-    const bool row_ok = row < p.m;
     const int b = p.had_block > 1 ? p.had_block : 1;
+    constexpr int ES = (DT == F32) ? 4 : 2;
+    constexpr int W = (DT == F32) ? 2 : 1;   // 16-byte words per 8 values
+    constexpr int SRC = GEGLU ? 2 : 1;
 
-    float v[NCH][8];
-    float amax = 0.f;
+    // per-lane constants: which chunks hold columns, output scaling
+    bool col_ok[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
-        const bool ok = row_ok && c < p.nch && col < p.k;
-        if (ok) {
-            load_row_chunk<DT, GEGLU>(p, row, col, v[c]);
-            if (p.mult) {
-                const float4* mp = reinterpret_cast<const float4*>(p.mult + col);
-                float4 m0 = mp[0], m1 = mp[1];
-                v[c][0] *= m0.x; v[c][1] *= m0.y; v[c][2] *= m0.z; v[c][3] *= m0.w;
-                v[c][4] *= m1.x; v[c][5] *= m1.y; v[c][6] *= m1.z; v[c][7] *= m1.w;
+    for (int c = 0; c < NCH; ++c) col_ok[c] = c < p.nch && static_cast<int64_t>(c) * g * 8 + t * 8 < p.k;
+    // fp32 of 1/sqrt(b), correctly rounded (exact for b = 4^j)
+    const float nrm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
+    const float qmax = (p.bits == 8) ? 127.f : 7.f;
+    // lane sign left by the cross-lane stages (lane bits below b/8)
+    const int lane_bits = (b > 8) ? (lane & (b / 8 - 1)) : 0;
+    const float sigma = (__builtin_popcount(lane_bits) & 1) ? -1.f : 1.f;
+
+    auto load_rows = [&](int64_t row, uint4 (&raw)[NCH][SRC][W]) {
+        const bool rok = row < p.m;
+        const char* xrow = static_cast<const char*>(p.x) + (rok ? row : 0) * p.ldx * ES;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
+            if (rok && col_ok[c]) {
+#pragma unroll
+                for (int sidx = 0; sidx < SRC; ++sidx)
+#pragma unroll
+                    for (int w = 0; w < W; ++w)
+                        raw[c][sidx][w] = reinterpret_cast<const uint4*>(xrow + (col + sidx * p.k) * ES)[w];
+            } else {
+#pragma unroll
+                for (int sidx = 0; sidx < SRC; ++sidx)
+#pragma unroll
+                    for (int w = 0; w < W; ++w) raw[c][sidx][w] = make_uint4(0, 0, 0, 0);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
         }
-        // in-register butterfly stages (distance 1, 2, 4 within the 8 values)
+    };
+
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * rpb;
+    int64_t row = static_cast<int64_t>(blockIdx.x) * rpb + tid / g;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * rpb; base < p.m; base += stride, row += stride) {
+        uint4 raw[NCH][SRC][W];
+        load_rows(row, raw);
+        float4 mlt[NCH][2];   // fold multipliers of the lane's columns
 #pragma unroll
-        for (int h = 1; h < 8; h <<= 1) {
-            if (h < b) {
+        for (int c = 0; c < NCH; ++c) {
+            mlt[c][0] = make_float4(1.f, 1.f, 1.f, 1.f);
+            mlt[c][1] = mlt[c][0];
+            if (col_ok[c] && p.mult) {
+                const float4* mp = reinterpret_cast<const float4*>(p.mult + static_cast<int64_t>(c) * g * 8 + t * 8);
+                mlt[c][0] = mp[0];
+                mlt[c][1] = mp[1];
+            }
+        }
+
+        // decode (GeGLU), fold, in-register butterflies
+        float v[NCH][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if ((e & h) == 0) {
-                        float a0 = v[c][e], a1 = v[c][e + h];
-                        v[c][e] = a0 + a1;
-                        v[c][e + h] = a0 - a1;
+        for (int c = 0; c < NCH; ++c) {
+            decode_chunk<DT, GEGLU>(raw[c], gtab, v[c]);
+            v[c][0] *= mlt[c][0].x; v[c][1] *= mlt[c][0].y; v[c][2] *= mlt[c][0].z; v[c][3] *= mlt[c][0].w;
+            v[c][4] *= mlt[c][1].x; v[c][5] *= mlt[c][1].y; v[c][6] *= mlt[c][1].z; v[c][7] *= mlt[c][1].w;
+#pragma unroll
+            for (int h = 1; h < 8; h <<= 1) {
+                if (h < b) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if ((e & h) == 0) {
+                            const float a0 = v[c][e], a1 = v[c][e + h];
+                            v[c][e] = a0 + a1;
+                            v[c][e + h] = a0 - a1;
+                        }
                     }
                 }
             }
         }
-    }
-    // cross-lane stages: lane distance 1 .. b/16 (b/8 lanes hold one block)
-    if (b > 8) xlane_stage<1, NCH>(v, lane);
-    if (b > 16) xlane_stage<2, NCH>(v, lane);
-    if (b > 32) xlane_stage<4, NCH>(v, lane);
-    if (b > 64) xlane_stage<8, NCH>(v, lane);
-    if (b > 128) xlane_stage<16, NCH>(v, lane);
+        // cross-lane stages: lane distance 1 .. b/16 (b/8 lanes hold one block)
+        if (b > 8) xlane_stage<1, NCH>(v, lane);
+        if (b > 16) xlane_stage<2, NCH>(v, lane);
+        if (b > 32) xlane_stage<4, NCH>(v, lane);
+        if (b > 64) xlane_stage<8, NCH>(v, lane);
+        if (b > 128) xlane_stage<16, NCH>(v, lane);
 
+        // row maximum: lanes, then the row's waves through LDS
+        float amax = 0.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+        for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+        amax = wave_max(amax, g < 64 ? g : 64);
+        if (g > 64) {
+            __syncthreads();   // previous group's reads of red[] are done
+            if (lane == 0) red[wave] = amax;
+            __syncthreads();
+            const int wpr = g >> 6;  // waves per row
+            const int first = (wave / wpr) * wpr;
+            amax = red[first];
+            for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[first + i]);
+        }
 
-    amax = wave_max(amax, g < 64 ? g : 64);
-    if (g > 64) {
-        if (lane == 0) red[wave] = amax;
-        __syncthreads();
-        const int wpr = g >> 6;  // waves per row
-        const int first = (wave / wpr) * wpr;
-        amax = red[first];
-        for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[first + i]);
-    }
-    if (!row_ok) return;
+        if (row < p.m) {
+            const float scale = (amax * nrm) / qmax;
+            const float mul = (scale > 0.f) ? sigma * (nrm * (1.f / scale)) : 0.f;
+            const double div = sigma * static_cast<double>(scale) * sqrt(static_cast<double>(b));
+            if (t == 0) p.scale[row] = scale;
 
-    // normalisation of the unnormalised transform: 1/sqrt(b)
-    // fp32 of 1/sqrt(b), correctly rounded (exact for b = 4^j)
-    const float nrm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
-    const float qmax = (p.bits == 8) ? 127.f : 7.f;
-    const float amax_n = amax * nrm;
-    const float scale = amax_n / qmax;
-    const float mul = (scale > 0.f) ? nrm * (1.f / scale) : 0.f;
-    const double div = static_cast<double>(scale) * sqrt(static_cast<double>(b));
-    if (t == 0) p.scale[row] = scale;
-
+            // fma(v, mul, M) with M = 1.5 * 2^23 rounds v * mul to an integer
+            // once, half to even (the fp32 spacing at M is 1); the code is the
+            // low mantissa bits in two's complement, the clamp a med3 around M.
+            constexpr float M = 12582912.f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
-        if (c >= p.nch || col >= p.k) continue;
-        int qv[8];
+            for (int c = 0; c < NCH; ++c) {
+                if (!col_ok[c]) continue;
+                const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
+                float qb[8];
+                float worst = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = static_cast<int>(quant_code(v[c][e], mul, div, qmax));
-        if (p.bits == 8) {
-            uint32_t lo = (qv[0] & 0xFF) | ((qv[1] & 0xFF) << 8) | ((qv[2] & 0xFF) << 16) |
-                          (static_cast<uint32_t>(qv[3] & 0xFF) << 24);
-            uint32_t hi = (qv[4] & 0xFF) | ((qv[5] & 0xFF) << 8) | ((qv[6] & 0xFF) << 16) |
-                          (static_cast<uint32_t>(qv[7] & 0xFF) << 24);
-            int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
-            *reinterpret_cast<uint2*>(out) = make_uint2(lo, hi);
-        } else {
-            uint32_t w = 0;
+                for (int e = 0; e < 8; ++e) {
+                    qb[e] = fmaf(v[c][e], mul, M);
+                    worst = fmaxf(worst, fabsf(fmaf(v[c][e], mul, M - qb[e])));
+                }
+                // a value within the largest boundary window (1e-5 * 128) of a
+                // half-integer: the chunk's rounding is redone on float64 quotients
+                if (worst >= 0.5f - 1.28e-3f) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w |= static_cast<uint32_t>(qv[e] & 0xF) << (4 * e);
-            uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
-            *reinterpret_cast<uint32_t*>(out) = w;
+                    for (int e = 0; e < 8; ++e) qb[e] = quant_code(v[c][e], mul, div, qmax) + M;
+                }
+                uint32_t cb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(qb[e], M - qmax, M + qmax));
+                if (p.bits == 8) {
+                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
+                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
+                } else {
+                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
+                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
+                }
+            }
         }
     }
 }
@@ -295,34 +510,67 @@ __global__ void fold_finish_kernel(float* s, float* inv_s, int64_t k) {
 
 namespace {
 
-template <int DT, bool GEGLU>
-hipError_t launch_rows_dt(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
-    const int rows_per_block = 256 / p.g;
-    dim3 grid(static_cast<unsigned>((p.m + rows_per_block - 1) / rows_per_block));
+template <int DT, bool GEGLU, int TPB>
+hipError_t launch_rows_tpb(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
+    const int rows_per_block = TPB / p.g;
+    const int64_t groups = (p.m + rows_per_block - 1) / rows_per_block;
+    // one row group per block (capped only by the grid-size limit)
+    const int64_t slots = 0x7FFFFFFFLL;
+    dim3 grid(static_cast<unsigned>(groups < slots ? groups : slots));
     switch (nch_tpl) {
-        case 1: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 1, GEGLU>), grid, dim3(256), 0, st, p); break;
-        case 2: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 2, GEGLU>), grid, dim3(256), 0, st, p); break;
-        case 4: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 4, GEGLU>), grid, dim3(256), 0, st, p); break;
-        case 8: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 8, GEGLU>), grid, dim3(256), 0, st, p); break;
-        case 16: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 16, GEGLU>), grid, dim3(256), 0, st, p); break;
+        case 1: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 1, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
+        case 2: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 2, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
+        case 4: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 4, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int DT, bool GEGLU>
+hipError_t launch_rows_dt(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
+    if (p.g > 256) return launch_rows_tpb<DT, GEGLU, 1024>(p, nch_tpl, st);
+    return launch_rows_tpb<DT, GEGLU, 256>(p, nch_tpl, st);
+}
+
 }  // namespace
 
+// Lanes per row: a power of two >= k / 8 up to 256 (several rows per block),
+// or 512 / 1024 lanes (one row per block) for longer rows.
 int row_quant_lanes(int64_t k) {
     int64_t g = 8;
-    while (g < 256 && g * 8 < k) g <<= 1;
+    while (g < 1024 && g * 8 < k) g <<= 1;
+    if (g == 512) g = 1024;
     return static_cast<int>(g);
 }
 
 int row_quant_chunks(int64_t k, int g) { return static_cast<int>((k + 8LL * g - 1) / (8LL * g)); }
 
+namespace {
+std::mutex g_tab_mu;
+bool g_tab_ready[64] = {false};
+
+// Fills the bfloat16 GeLU table on the current device (once per device).
+hipError_t ensure_gelu_table(hipStream_t st) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_tab_mu);
+    if (g_tab_ready[dev]) return hipSuccess;
+    hipLaunchKernelGGL(gelu_table_init_kernel, dim3((GELU_TAB + 255) / 256), dim3(256), 0, st);
+    e = hipGetLastError();
+    if (e == hipSuccess) g_tab_ready[dev] = true;
+    return e;
+}
+}  // namespace
+
 hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
                                bool geglu, const float* mult, int had_block, int bits, void* q,
                                float* scale, hipStream_t st) {
+    if (geglu && dtype == BF16) {
+        hipError_t e = ensure_gelu_table(st);
+        if (e != hipSuccess) return e;
+    }
     RowQuantParams p;
     p.x = x; p.m = m; p.k = k; p.ldx = ldx; p.mult = mult;
     p.g = row_quant_lanes(k);
@@ -330,7 +578,7 @@ hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, i
     p.had_block = had_block; p.bits = bits; p.q = q; p.scale = scale;
     int tpl = 1;
     while (tpl < p.nch) tpl <<= 1;
-    if (tpl > 16) return hipErrorInvalidValue;
+    if (tpl > 4) return hipErrorInvalidValue;
     if (geglu) {
         switch (dtype) {
             case F16: return launch_rows_dt<F16, true>(p, tpl, st);

@@ -217,7 +217,7 @@ qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, 
     if (m > 0 && (!x || !y)) return QLIN_ERR_NULL;
     if (!wq || !w_scale) return QLIN_ERR_NULL;
     if (group != 128) return QLIN_ERR_UNSUPPORTED;
-    if (m < 0 || m > 64 || n < 1 || k < group || (k % group) != 0) return QLIN_ERR_SHAPE;
+    if (m < 0 || m > 64 || n < 1 || k < group || (k % group) != 0 || k > 32768) return QLIN_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y)) return QLIN_ERR_ALIGN;
     const Span outs[1] = {{y, m * n * 2}};
     const Span ins[3] = {{x, m * k * 2}, {wq, n * k / 2}, {w_scale, n * (k / group) * 2}};

@@ -166,7 +166,7 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
  *   x        [m][k] fp16, contiguous.   wq: packed int4 [n][k/2].
  *   w_scale  fp16 [n][k/group] (uint16_t storage).   y: out fp16 [m][n].
  * Preconditions: 1 <= m <= 64 (m == 0 is an empty call); n >= 1;
- * group == 128; k % group == 0.
+ * group == 128; k % group == 0; k <= 32768.
  */
 qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                             int64_t n, int64_t k, int32_t group, void* y, void* stream);

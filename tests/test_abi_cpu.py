@@ -132,7 +132,8 @@ def test_gemm_raw_i32_needs_no_scales_and_empty_ok(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), q.QLIN_ERR_NULL), (dict(wq=None), q.QLIN_ERR_NULL), (dict(y=None), q.QLIN_ERR_NULL),
     (dict(group=64), q.QLIN_ERR_UNSUPPORTED), (dict(m=65), q.QLIN_ERR_SHAPE), (dict(k=200), q.QLIN_ERR_SHAPE),
-    (dict(n=0), q.QLIN_ERR_SHAPE), (dict(x=BAD), q.QLIN_ERR_ALIGN), (dict(y=P2 + 16), q.QLIN_ERR_ALIAS),
+    (dict(n=0), q.QLIN_ERR_SHAPE), (dict(k=32768 + 128), q.QLIN_ERR_SHAPE), (dict(x=BAD), q.QLIN_ERR_ALIGN),
+    (dict(y=P2 + 16), q.QLIN_ERR_ALIAS),
 ])
 def test_gemv_rejects(lib, kw, status):
     a = dict(x=P, wq=P2, ws=P3, m=1, n=256, k=4096, group=128, y=P4)
