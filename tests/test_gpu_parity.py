@@ -201,7 +201,11 @@ def test_gemm_deterministic():
 # ---------------------------------------------------------------- W4A16 GEMV
 
 GEMV_CASES = [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (3, 520, 1024), (50, 1024, 4096),
-              (64, 256, 256), (17, 1000, 2048)]
+              (64, 256, 256), (17, 1000, 2048),
+              # every chunk-slot count (k up to 32768), token-row pass size and rows-per-wave choice,
+              # ragged n and m
+              (1, 300, 128), (2, 77, 32768), (5, 130, 20480), (9, 333, 16384), (4, 250, 12288),
+              (8, 8200, 2048), (1, 9000, 5120), (64, 40, 1024), (50, 1030, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMV_CASES)
@@ -214,6 +218,25 @@ def test_gemv_w4a16_parity(m, n, k):
     torch.cuda.synchronize()
     y32, y_ref = oracle.gemv_w4a16(synth.to_f64(x), codes_np(wq, 4), ws.cpu().numpy(), 128)
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+
+
+def test_gemv_w4a16_subnormal_and_large_x():
+    # fp16 subnormal, zero and near-maximum activations (the kernel folds a
+    # per-chunk sum of x into its accumulation, which must see the same values)
+    say("gemv subnormal/large x")
+    m, n, k = 2, 520, 4096
+    x = synth.normal_tensor(SEED, "gx/sub", (m, k), dtype="f16")
+    x[0, ::3] = torch.tensor(3.0e-6, dtype=torch.float16)     # subnormal
+    x[0, 1::7] = 0
+    x[1, ::5] = torch.tensor(-2.0e3, dtype=torch.float16)     # large
+    x[1, 0], x[1, k - 1] = 6.0e4, -6.0e4                        # near the fp16 maximum
+    w = synth.normal_tensor(SEED, "gw/sub", (n, k), std=0.015, dtype="f16")
+    wq, ws = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
+    y = q.qlin_gemv_w4a16(x.to(DEV), wq, ws)
+    torch.cuda.synchronize()
+    y32, y_ref = oracle.gemv_w4a16(synth.to_f64(x), codes_np(wq, 4), ws.cpu().numpy(), 128)
+    for i in range(m):  # each row on its own scale
+        assert_ok(oracle.compare_outputs(f64(y)[i:i + 1], y_ref[i:i + 1]), f"output row {i}")
 
 
 # ---------------------------------------------------------------- fold calibration
