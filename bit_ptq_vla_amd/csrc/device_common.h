@@ -14,6 +14,15 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 enum DType { F16 = 0, BF16 = 1, F32 = 2, I32 = 3 };
 
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, num_records
+// in bytes, dword 3 = data format 32 (raw byte addressing).
+__device__ __forceinline__ v4i make_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const int64_t n = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return v4i{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu),
+               static_cast<int>(n), 0x00020000};
+}
+
 // ---- scalar storage conversions ------------------------------------------
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -129,15 +129,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     else static_assert(N == 0, "unsupported count");
 }
 
-// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, num_records
-// in bytes, dword 3 = data format 32 (raw byte addressing).
-__device__ __forceinline__ v4i make_rsrc(const void* base, int64_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const int64_t n = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-    return v4i{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu),
-               static_cast<int>(n), 0x00020000};
-}
-
 // 16-byte load of every lane from rsrc + voff straight into LDS at
 // lds_addr + 16 * lane (LDS DMA through M0).  Offsets at or past num_records
 // fetch nothing.  Written as inline assembly so that the compiler does not

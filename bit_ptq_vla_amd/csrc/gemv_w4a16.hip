@@ -35,7 +35,13 @@ namespace qlin {
 
 namespace {
 
-constexpr int kGemvLdsBytes = 65536 + 4096;  // x pieces (MT k 2 bytes) and chunk terms (MT k / 8 bytes)
+// LDS of a block: x pieces (MT k 2 bytes), chunk terms (MT k / 8 bytes) and a
+// 4 KB slot that takes the fp16 scales of its 4R rows (one 16-byte word per
+// thread; 4R k / 64 <= 4096 since R * CH <= 32).
+constexpr int64_t kGemvLdsBytes = 65536 + 4096 + 8192;
+constexpr int64_t gemv_lds_bytes(int64_t mt, int64_t /*r*/, int64_t k) {
+    return mt * (k * 2 + k / 8) + 4096;
+}
 
 // fp16 pair held in a dword.  Taken by value: a bit cast applied directly to a
 // component of an ext_vector lvalue (v.y) reads component 0 with this
@@ -64,11 +70,6 @@ __device__ __forceinline__ float chunk_dot(const v4i wv, const v4i (&xv)[4]) {
     return __builtin_fmaf(odd, 0.0625f, even);
 }
 
-// LDS layout of x: token row i, 16-byte piece q (0..3) of chunk c at v4i
-// index (i * 4 + q) * chunks + c, so the 64 lanes of a wave (consecutive
-// chunks) read consecutive 16-byte words.  A piece holds x_0..x_7 of its
-// 8 codes as the pairs (x0,x4), (x2,x6), (x1,x5), (x3,x7).  After the pieces,
-// float bias[i][c] = 1032 Sx_even + 72 Sx_odd of the chunk.
 // v + the value of another lane chosen by a DPP control (rows outside
 // ROW_MASK add 0).
 template <int CTRL, int ROW_MASK>
@@ -89,12 +90,19 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
     return v;
 }
 
+// LDS layout: token row i, 16-byte piece q (0..3) of chunk c at v4i index
+// (i * 4 + q) * chunks + c, so the 64 lanes of a wave (consecutive chunks)
+// read consecutive 16-byte words.  A piece holds x_0..x_7 of its 8 codes as
+// the pairs (x0,x4), (x2,x6), (x1,x5), (x3,x7).  After the pieces, float
+// bias[i][c] = 1032 Sx_even + 72 Sx_odd of the chunk, then the fp16 scales of
+// the block's rows as stored in w_scale.
 template <int R, int CH, int MT>
 __global__ __launch_bounds__(256) void gemv_w4a16_kernel(const _Float16* __restrict__ x,
                                                          const uint8_t* __restrict__ wq,
                                                          const _Float16* __restrict__ ws,
                                                          int64_t m, int64_t n, int64_t k,
                                                          _Float16* __restrict__ y) {
+    static_assert(R * CH <= 32, "the block's scales must fit one 16-byte word per thread");
     extern __shared__ v4i xs[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -118,25 +126,33 @@ __global__ __launch_bounds__(256) void gemv_w4a16_kernel(const _Float16* __restr
             xr[i][t] = xrow[e];
         }
     }
-    // 2. weight chunks and group scales of the wave's rows (clamped, no branch)
+    // 2. the group scales of the block's 4R rows (contiguous, at most 16 bytes
+    //    per thread; the buffer descriptor returns zeros past the last row)
+    const int64_t rb0 = static_cast<int64_t>(blockIdx.x) * 4 * R;
+    const int sbytes = static_cast<int>((n - rb0 < 4 * R ? n - rb0 : 4 * R) * groups * 2);
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16*>(ws + rb0 * groups), 0, sbytes, 0x00020000);
+    const v4i sraw = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_s, tid * 16, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);  // issued ahead of the weights: its wait leaves them in flight
+
+    // 3. weight chunks of the wave's rows (clamped, no branch)
     v4i wv[R][CH];
-    _Float16 sh[R][CH];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t row = row0 + r < n ? row0 + r : n - 1;
         const v4i* wrow = reinterpret_cast<const v4i*>(wq + row * (k / 2));
-        const _Float16* srow = ws + row * groups;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int c = lane + 64 * j < chunks ? lane + 64 * j : chunks - 1;
             wv[r][j] = __builtin_nontemporal_load(wrow + c);
-            sh[r][j] = srow[c >> 2];
         }
     }
 
     __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the LDS stores wait
-    // 3. stage x in pair order and the chunk terms 1032 Sx_even + 72 Sx_odd
+    // 4. stage x in pair order, the chunk terms 1032 Sx_even + 72 Sx_odd and the scales
     float* xbias = reinterpret_cast<float*>(xs + MT * 4 * chunks);
+    v4i* sc_lds = reinterpret_cast<v4i*>(xbias + MT * chunks);
+    sc_lds[tid] = sraw;  // unconditional: a conditional store lets the compiler sink the load
     const h2 k_even = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
     const h2 k_odd = {static_cast<_Float16>(72.0f), static_cast<_Float16>(72.0f)};
 #pragma unroll
@@ -166,7 +182,17 @@ __global__ __launch_bounds__(256) void gemv_w4a16_kernel(const _Float16* __restr
     }
     __syncthreads();
 
-    // 4. dot products; invalid chunks and rows carry a zero scale
+    // 5. dot products; invalid chunks and rows carry a zero scale
+    const _Float16* sc16 = reinterpret_cast<const _Float16*>(sc_lds) + wave * R * groups;
+    _Float16 sh[R][CH];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = lane + 64 * j < chunks ? lane + 64 * j : chunks - 1;
+            sh[r][j] = sc16[r * groups + (c >> 2)];
+        }
+    __builtin_amdgcn_sched_barrier(0);  // the LDS reads above go out back to back
     float sc[R][CH];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -210,7 +236,7 @@ template <int R, int CH, int MT>
 hipError_t launch_g(const void* x, const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
                     void* y, hipStream_t st) {
     const int64_t waves = (n + R - 1) / R;
-    const int64_t lds = static_cast<int64_t>(MT) * (k * 2 + k / 32 * 4);
+    const int64_t lds = gemv_lds_bytes(MT, R, k);
     if (lds > kGemvLdsBytes) return hipErrorInvalidValue;
     dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>((m + MT - 1) / MT));
     hipLaunchKernelGGL((gemv_w4a16_kernel<R, CH, MT>), grid, dim3(256), static_cast<size_t>(lds), st,
@@ -226,7 +252,7 @@ hipError_t launch_mt(const void* x, const void* wq, const void* ws, int64_t m, i
     // (k > (CH / 2) * 2048 bounds MT from above, so larger MT are never built)
     constexpr int kMaxMt = CH <= 2 ? 8 : CH <= 4 ? 4 : CH <= 8 ? 2 : 1;
     int mt = 1;
-    while (mt < kMaxMt && mt < m && 2 * mt * (k * 2 + k / 32 * 4) <= kGemvLdsBytes) mt *= 2;
+    while (mt < kMaxMt && mt < m && gemv_lds_bytes(2 * mt, R, k) <= kGemvLdsBytes) mt *= 2;
     if constexpr (kMaxMt >= 8) {
         if (mt == 8) return launch_g<R, CH, 8>(x, wq, ws, m, n, k, y, st);
     }
@@ -243,9 +269,9 @@ template <int CH>
 hipError_t launch_ch(const void* x, const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
                      void* y, hipStream_t st) {
     // R * CH 16-byte weight loads per lane stay in flight; R = 4 only where
-    // n still gives >= 512 blocks of four waves (two per CU)
+    // n still gives >= 256 blocks of four waves (one per CU)
     if constexpr (CH <= 4) {
-        if (n >= 4 * 4 * 512) return launch_mt<4, CH>(x, wq, ws, m, n, k, y, st);
+        if (n >= 4 * 4 * 256) return launch_mt<4, CH>(x, wq, ws, m, n, k, y, st);
     }
     return launch_mt<2, CH>(x, wq, ws, m, n, k, y, st);
 }
