@@ -32,6 +32,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+# FETCH_SIZE / WRITE_SIZE summary of the step's kernels and the gate|up GEMM's name in it
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_mlp_block_m816.txt")
+GATE_UP_KERNEL = "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,1>"
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
@@ -44,61 +47,19 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-rows", type=int, default=16, help="token rows of the oracle's CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="token rows of the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     return ap.parse_args()
 
 
-class MlpBlock:
-    """Device buffers and quantized weights of the M = 816 backbone MLP block."""
-
-    def __init__(self, dev):
-        import torch
-
-        import bit_ptq_vla_amd as q
-        from bit_ptq_vla_amd import synth
-
-        self.q = q
-        wl = synth.CFG2
-        self.gu, self.dn = wl.projs
-        self.m = wl.ms[0]
-        self.x_cpu = synth.activation(wl, self.gu, self.m)
-        self.wgu_cpu = synth.weight(wl, self.gu)
-        self.wdn_cpu = synth.weight(wl, self.dn)
-        self.x = self.x_cpu.to(dev)
-        wgu, wdn = self.wgu_cpu.to(dev), self.wdn_cpu.to(dev)
-        # offline: fold calibration and weight quantization
-        self.s1, self.inv1 = q.qlin_calibrate_fold(self.x, wgu)
-        self.wq1, self.ws1 = q.qlin_quantize_weights(wgu, fold_s=self.s1, had_block=128, bits=4)
-        self.xq = torch.empty((self.m, self.gu.k // 2), dtype=torch.uint8, device=dev)
-        self.xs = torch.empty(self.m, dtype=torch.float32, device=dev)
-        self.y1 = torch.empty((self.m, self.gu.n), dtype=torch.bfloat16, device=dev)
-        q.qlin_rotate_quant_act(self.x, fold_inv_s=self.inv1, had_block=128, bits=4, out=(self.xq, self.xs))
-        q.qlin_gemm_w4a4(self.xq, self.xs, self.wq1, self.ws1, self.gu.k, out=self.y1)
-        self.s2, self.inv2 = q.qlin_calibrate_fold(self.y1, wdn, pre=q.QLIN_PRE_GEGLU)
-        self.wq2, self.ws2 = q.qlin_quantize_weights(wdn, fold_s=self.s2, had_block=128, bits=8)
-        del wgu, wdn
-        self.hq = torch.empty((self.m, self.dn.k), dtype=torch.int8, device=dev)
-        self.hs = torch.empty(self.m, dtype=torch.float32, device=dev)
-        self.y2 = torch.empty((self.m, self.dn.n), dtype=torch.bfloat16, device=dev)
-        self.ops = 2 * self.m * (self.gu.n * self.gu.k + self.dn.n * self.dn.k)
-        self.gemm1_ops = 2 * self.m * self.gu.n * self.gu.k
-
-    def step(self, ev=None):
-        q = self.q
-        q.qlin_rotate_quant_act(self.x, fold_inv_s=self.inv1, had_block=128, bits=4, out=(self.xq, self.xs))
-        if ev is not None:
-            ev[0].record()
-        q.qlin_gemm_w4a4(self.xq, self.xs, self.wq1, self.ws1, self.gu.k, out=self.y1)
-        if ev is not None:
-            ev[1].record()
-        q.qlin_rotate_quant_act(self.y1, k=self.dn.k, fold_inv_s=self.inv2, had_block=128, bits=8,
-                                pre=q.QLIN_PRE_GEGLU, out=(self.hq, self.hs))
-        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq2, self.ws2, self.dn.k, out=self.y2)
+from bit_ptq_vla_amd.profile_step import read_traffic  # noqa: E402
+from bit_ptq_vla_amd.workload import MlpBlock  # noqa: E402
 
 
 def time_block(block, steps, warmup):
+    """Step time over `steps` steps (events on the launch stream) and the mean
+    duration of the gate|up GEMM launch inside them."""
     import torch
 
     for _ in range(warmup):
@@ -234,14 +195,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 MFMA (int4/int8 codes), fp32 rotate/epilogue, bf16 I/O",
+        "dtype": "int8",
         "data": "synthetic (seeded normals, 1% outlier channels x30; random-init weights N(0, 0.02))",
         "config": {"workload": "backbone_mlp_m816_h2048_f16384", "m": block.m, "hidden": 2048,
                    "ffn": 16384, "gate_up": "w4a4", "down": "w8a8", "hadamard_block": 128,
                    "out_dtype": "bf16", "step_gop": round(block.ops / 1e9, 2)},
         "roofline": {"kernel": "gate_up W4A4 GEMM 816x32768x2048", "bound": "mfma",
                      "achieved": round(gemm1_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(gemm1_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(gemm1_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": read_traffic(TRAFFIC_SUMMARY, GATE_UP_KERNEL),
+                     "traffic_algorithmic": block.gemm1_bytes,
                      "us_per_launch": round(gemm1_ms * 1e3, 3)},
         "frac_of_int8_peak_step": round(tops / INT8_PEAK_TOPS, 4),
         "wall_s_timed": round(wall, 3),
