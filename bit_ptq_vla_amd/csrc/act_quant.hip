@@ -24,17 +24,24 @@
 
 namespace qlin {
 
+// Distance from a half-integer below which a code is recomputed in float64.
+// The multiplier mul = fp32(fp32(1/sqrt b) * fp32(1/scale)) is within 2^-22
+// relative of the exact 1/(scale sqrt b), and fma forms v * mul exactly, so
+// the fast value of r = v / (scale sqrt b) is off by at most 127.5 * 2^-22 =
+// 3.0e-5; the window doubles that.
+constexpr float kTieWindow = 6e-5f;
+
 // Round-half-even of v / scale, clamped to +-qmax.  The fast path multiplies
-// by an fp32 reciprocal (relative error ~1.5 ulp); when that product lies
-// within 1e-5 * max(1, |r|) of a half-integer, the quotient is recomputed in
-// float64 so that the rounding decision is taken on the correctly rounded
-// value: with exact inputs (no fold, no rotation) the codes then match a
-// float64 reference exactly.  `div` is the exact divisor (scale * sqrt(b)).
+// by the fp32 multiplier; when that product lies within kTieWindow of a
+// half-integer, the quotient is recomputed in float64 so that the rounding
+// decision is taken on the correctly rounded value: with exact inputs (no
+// fold, no rotation) the codes then match a float64 reference exactly.
+// `div` is the exact divisor (scale * sqrt(b)).
 __device__ __forceinline__ float quant_code(float v, float mul, double div, float qmax) {
     const float r = v * mul;
     float q = __builtin_rintf(r);
     const float d = fabsf(fabsf(r - q) - 0.5f);
-    if (d <= 1e-5f * fmaxf(1.f, fabsf(r))) {
+    if (d <= kTieWindow) {
         q = static_cast<float>(__builtin_rint(static_cast<double>(v) / div));
     }
     return fminf(fmaxf(q, -qmax), qmax);
@@ -117,21 +124,23 @@ __device__ __forceinline__ void xlane_stage(float (&v)[NCH][8], int lane) {
 }
 
 // ---- GeLU table for bfloat16 inputs ------------------------------------------
-// gelu(g) for every bfloat16 g with 2^-12 <= |g| < 8, both signs: 15 exponents
-// x 128 mantissas x 2 signs, evaluated once per device in float64 (erf) and
-// rounded to fp32.  Smaller |g| use 0.5 g + g^2 / sqrt(2 pi) (error below
-// 1e-11 relative); |g| >= 8 gives g (positive) or 0 (negative).
-constexpr int GELU_EF0 = 127 - 12;               // first tabulated exponent field
-constexpr int GELU_NEXP = 15;
-constexpr int GELU_HALF = GELU_NEXP * 128;       // tabulated entries per sign (1920)
-constexpr int GELU_TAB = 2 * 2048;               // sign selects a 2048-entry half
+// gelu(g) for every bfloat16 g with 2^-20 <= |g| < 256, both signs: 28
+// exponents x 128 mantissas x 2 signs, evaluated once per device in float64
+// (erf) and rounded to fp32.  The range is wide enough that activations of
+// any realistic scale never leave it (a value outside it sends its wave down
+// a lane-divergent path).  Smaller |g| use 0.5 g + g^2 / sqrt(2 pi) (error
+// below 1e-11 relative); |g| >= 256 gives g (positive) or 0 (negative).
+constexpr int GELU_EF0 = 127 - 20;               // first tabulated exponent field
+constexpr int GELU_NEXP = 28;
+constexpr int GELU_HALF = GELU_NEXP * 128;       // tabulated entries per sign (3584)
+constexpr int GELU_TAB = 2 * 4096;               // sign selects a 4096-entry half
 __device__ float g_gelu_bf16_tab[GELU_TAB];
 
 __global__ void gelu_table_init_kernel() {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= GELU_TAB) return;
-    const int neg = i >= 2048;
-    const int j = i & 2047;
+    const int neg = i >= 4096;
+    const int j = i & 4095;
     if (j >= GELU_HALF) {
         g_gelu_bf16_tab[i] = 0.f;
         return;
@@ -160,7 +169,7 @@ __device__ __forceinline__ void gelu_bf16_8(const uint32_t w[4], const float* ta
         const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
         const uint32_t t = (bits & 0x7FFFu) - static_cast<uint32_t>(GELU_EF0 << 7);
         worst = worst > t ? worst : t;
-        idx[i] = t | ((bits >> 4) & 0x800u);   // sign bit 15 -> table half (bit 11)
+        idx[i] = t | ((bits >> 3) & 0x1000u);   // sign bit 15 -> table half (bit 12)
     }
     if (worst < static_cast<uint32_t>(GELU_HALF)) {
 #pragma unroll
@@ -239,14 +248,16 @@ __device__ __forceinline__ uint32_t pack8_i4(const uint32_t cb[8]) {
 
 // Rows of k values; TPB lanes per block, g lanes per row (g <= TPB, RPB =
 // TPB / g rows per block and iteration), NCH chunk passes of 8 values per
-// lane.  Block i handles row groups i, i + grid, ... (the launcher gives one
-// group per block: occupancy hides the load latency better than keeping a
-// prefetched group in registers).  All of a group's loads are issued before
-// any value is used.
+// lane.  Blocks are persistent: block i handles row groups i, i + grid, ...
+// and (where registers allow) loads the next group while it rotates and
+// quantizes the current one.  The fold multipliers of the lane's columns are
+// loaded once.  No load sits
+// behind a branch: rows past the end read the last row and columns past k
+// read column 0, and their values are replaced by zeros afterwards.
 template <int DT, int NCH, bool GEGLU, int TPB>
-__global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_kernel(RowQuantParams p) {
+__global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p) {
     constexpr int NW = TPB / 64;
-    __shared__ float red[NW];
+    __shared__ float red[2][NW];
     constexpr bool LUT = GEGLU && DT == BF16;
     __shared__ float gtab[LUT ? GELU_TAB : 1];
     if constexpr (LUT) {
@@ -263,11 +274,31 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
     constexpr int ES = (DT == F32) ? 4 : 2;
     constexpr int W = (DT == F32) ? 2 : 1;   // 16-byte words per 8 values
     constexpr int SRC = GEGLU ? 2 : 1;
+    // prefetch the next group into registers while this one is processed,
+    // where the doubled load registers still leave room without spills
+    constexpr bool PF = NCH * SRC * W <= 4;
 
-    // per-lane constants: which chunks hold columns, output scaling
+    // per-lane constants: which chunks hold columns, their fold multipliers, output scaling
     bool col_ok[NCH];
+    int64_t col_ld[NCH];   // column of each chunk's load (0 where the chunk is unused)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) col_ok[c] = c < p.nch && static_cast<int64_t>(c) * g * 8 + t * 8 < p.k;
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
+        col_ok[c] = c < p.nch && col < p.k;
+        col_ld[c] = col_ok[c] ? col : 0;
+    }
+    float mlt[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        float4 m0 = make_float4(1.f, 1.f, 1.f, 1.f), m1 = m0;
+        if (p.mult) {
+            const float4* mp = reinterpret_cast<const float4*>(p.mult + col_ld[c]);
+            m0 = mp[0];
+            m1 = mp[1];
+        }
+        mlt[c][0] = m0.x; mlt[c][1] = m0.y; mlt[c][2] = m0.z; mlt[c][3] = m0.w;
+        mlt[c][4] = m1.x; mlt[c][5] = m1.y; mlt[c][6] = m1.z; mlt[c][7] = m1.w;
+    }
     // fp32 of 1/sqrt(b), correctly rounded (exact for b = 4^j)
     const float nrm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
     const float qmax = (p.bits == 8) ? 127.f : 7.f;
@@ -276,50 +307,34 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
     const float sigma = (__builtin_popcount(lane_bits) & 1) ? -1.f : 1.f;
 
     auto load_rows = [&](int64_t row, uint4 (&raw)[NCH][SRC][W]) {
-        const bool rok = row < p.m;
-        const char* xrow = static_cast<const char*>(p.x) + (rok ? row : 0) * p.ldx * ES;
+        const int64_t r = row < p.m ? row : p.m - 1;
+        const char* xrow = static_cast<const char*>(p.x) + r * p.ldx * ES;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
-            if (rok && col_ok[c]) {
+        for (int c = 0; c < NCH; ++c)
 #pragma unroll
-                for (int sidx = 0; sidx < SRC; ++sidx)
+            for (int sidx = 0; sidx < SRC; ++sidx)
 #pragma unroll
-                    for (int w = 0; w < W; ++w)
-                        raw[c][sidx][w] = reinterpret_cast<const uint4*>(xrow + (col + sidx * p.k) * ES)[w];
-            } else {
-#pragma unroll
-                for (int sidx = 0; sidx < SRC; ++sidx)
-#pragma unroll
-                    for (int w = 0; w < W; ++w) raw[c][sidx][w] = make_uint4(0, 0, 0, 0);
-            }
-        }
+                for (int w = 0; w < W; ++w)
+                    raw[c][sidx][w] = reinterpret_cast<const uint4*>(xrow + (col_ld[c] + sidx * p.k) * ES)[w];
     };
 
     const int64_t stride = static_cast<int64_t>(gridDim.x) * rpb;
     int64_t row = static_cast<int64_t>(blockIdx.x) * rpb + tid / g;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * rpb; base < p.m; base += stride, row += stride) {
-        uint4 raw[NCH][SRC][W];
-        load_rows(row, raw);
-        float4 mlt[NCH][2];   // fold multipliers of the lane's columns
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            mlt[c][0] = make_float4(1.f, 1.f, 1.f, 1.f);
-            mlt[c][1] = mlt[c][0];
-            if (col_ok[c] && p.mult) {
-                const float4* mp = reinterpret_cast<const float4*>(p.mult + static_cast<int64_t>(c) * g * 8 + t * 8);
-                mlt[c][0] = mp[0];
-                mlt[c][1] = mp[1];
-            }
-        }
+    uint4 raw[NCH][SRC][W];
+    load_rows(row, raw);
+    int parity = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * rpb; base < p.m;
+         base += stride, row += stride, parity ^= 1) {
+        uint4 nxt[PF ? NCH : 1][SRC][W];
+        if constexpr (PF) load_rows(row + stride, nxt);   // in flight while this group is processed
 
         // decode (GeGLU), fold, in-register butterflies
         float v[NCH][8];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             decode_chunk<DT, GEGLU>(raw[c], gtab, v[c]);
-            v[c][0] *= mlt[c][0].x; v[c][1] *= mlt[c][0].y; v[c][2] *= mlt[c][0].z; v[c][3] *= mlt[c][0].w;
-            v[c][4] *= mlt[c][1].x; v[c][5] *= mlt[c][1].y; v[c][6] *= mlt[c][1].z; v[c][7] *= mlt[c][1].w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = col_ok[c] ? v[c][e] * mlt[c][e] : 0.f;
 #pragma unroll
             for (int h = 1; h < 8; h <<= 1) {
                 if (h < b) {
@@ -341,7 +356,8 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
         if (b > 64) xlane_stage<8, NCH>(v, lane);
         if (b > 128) xlane_stage<16, NCH>(v, lane);
 
-        // row maximum: lanes, then the row's waves through LDS
+        // row maximum: lanes, then the row's waves through LDS (two slots
+        // alternate between iterations, so one barrier per group suffices)
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
@@ -349,13 +365,12 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
         amax = wave_max(amax, g < 64 ? g : 64);
         if (g > 64) {
-            __syncthreads();   // previous group's reads of red[] are done
-            if (lane == 0) red[wave] = amax;
+            if (lane == 0) red[parity][wave] = amax;
             __syncthreads();
             const int wpr = g >> 6;  // waves per row
             const int first = (wave / wpr) * wpr;
-            amax = red[first];
-            for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[first + i]);
+            amax = red[parity][first];
+            for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[parity][first + i]);
         }
 
         if (row < p.m) {
@@ -371,7 +386,7 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 if (!col_ok[c]) continue;
-                const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
+                const int64_t col = col_ld[c];
                 float qb[8];
                 float worst = 0.f;
 #pragma unroll
@@ -379,9 +394,9 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
                     qb[e] = fmaf(v[c][e], mul, M);
                     worst = fmaxf(worst, fabsf(fmaf(v[c][e], mul, M - qb[e])));
                 }
-                // a value within the largest boundary window (1e-5 * 128) of a
-                // half-integer: the chunk's rounding is redone on float64 quotients
-                if (worst >= 0.5f - 1.28e-3f) {
+                // a value near a half-integer: the chunk's rounding is redone on
+                // float64 quotients
+                if (worst >= 0.5f - kTieWindow) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) qb[e] = quant_code(v[c][e], mul, div, qmax) + M;
                 }
@@ -396,6 +411,243 @@ __global__ __launch_bounds__(TPB, TPB == 1024 ? 2 : 4) void rotate_quant_rows_ke
                     *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
                 }
             }
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int sidx = 0; sidx < SRC; ++sidx)
+#pragma unroll
+                    for (int w = 0; w < W; ++w) raw[c][sidx][w] = nxt[c][sidx][w];
+        } else {
+            load_rows(row + stride, raw);
+        }
+    }
+}
+
+// ---- bfloat16 fast path ---------------------------------------------------------
+// The same computation for bfloat16 rows whose k is a whole number of chunk
+// passes, with the Hadamard block (64 or 128), the code width and the GeGLU
+// pre-op fixed at compile time.  Per element it spends about 18 VALU
+// instructions: the GeLU table index of two values at once with 16-bit
+// packed arithmetic, 3 in-lane and 3-4 cross-lane butterflies (the lane
+// distance 4 as a quad reversal plus a half-row mirror, two DPP operations),
+// max3 reductions, and no clamp (|v / scale| <= qmax by construction, so the
+// rounded code never leaves the grid).
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Lane distance 4 via quad_perm [3,2,1,0] into a temporary and a fused
+// multiply-add reading the temporary through row_half_mirror (lane l then
+// sees the value of lane l ^ 4).
+__device__ __forceinline__ void xlane4_fast(float (&w)[8], float sgn) {
+    float t0, t1, t2, t3, t4, t5, t6, t7;
+    asm("s_nop 1\n\t"
+        "v_mov_b32_dpp %0, %8 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %1, %9 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %2, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %3, %11 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %4, %12 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %5, %13 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %6, %14 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %7, %15 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf"
+        : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]));
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %8, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %12, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %13, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %14, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %15, %16 row_half_mirror row_mask:0xf bank_mask:0xf"
+        : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
+        : "v"(t0), "v"(t1), "v"(t2), "v"(t3), "v"(t4), "v"(t5), "v"(t6), "v"(t7), "v"(sgn));
+}
+
+// gelu of 8 bfloat16 gate values (four dwords) from the LDS table; values
+// outside the tabulated range take the edge formula (rare: a lane-divergent
+// branch).
+__device__ __forceinline__ void gelu8_fast(const uint4 gw, const float* tab, float out[8]) {
+    const uint32_t w[4] = {gw.x, gw.y, gw.z, gw.w};
+    const us2 base = {static_cast<unsigned short>(GELU_EF0 << 7), static_cast<unsigned short>(GELU_EF0 << 7)};
+    uint32_t idx[4];
+    us2 worst = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const us2 tt = __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu) - base;   // v_pk_sub_u16
+        worst = worst > tt ? worst : tt;                                         // v_pk_max_u16
+        idx[i] = __builtin_bit_cast(uint32_t, tt) | ((w[i] >> 3) & 0x10001000u); // sign -> table half
+    }
+    const uint32_t wmax = worst.x > worst.y ? worst.x : worst.y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = tab[idx[i] & 0xFFFFu];
+        out[2 * i + 1] = tab[idx[i] >> 16];
+    }
+    if (wmax >= static_cast<uint32_t>(GELU_HALF)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+            const uint32_t t = (bits & 0x7FFFu) - static_cast<uint32_t>(GELU_EF0 << 7);
+            if (t >= static_cast<uint32_t>(GELU_HALF)) out[i] = gelu_bf16_edge(bits);
+        }
+    }
+}
+
+template <int NCH, bool GEGLU, int HB, int BITS, int TPB>
+__global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p) {
+    static_assert(HB == 64 || HB == 128, "Hadamard block");
+    constexpr int NW = TPB / 64;
+    __shared__ float red[2][NW];
+    __shared__ float gtab[GEGLU ? GELU_TAB : 1];
+    if constexpr (GEGLU) {
+        for (int i = threadIdx.x; i < GELU_TAB; i += TPB) gtab[i] = g_gelu_bf16_tab[i];
+        __syncthreads();
+    }
+    constexpr int SRC = GEGLU ? 2 : 1;
+    constexpr bool PF = NCH * SRC <= 4;          // prefetch the next group into registers
+    constexpr float QMAX = BITS == 8 ? 127.f : 7.f;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = p.g;
+    const int rpb = TPB / g;
+    const int t = tid & (g - 1);
+
+    float mlt[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        float4 m0 = make_float4(1.f, 1.f, 1.f, 1.f), m1 = m0;
+        if (p.mult) {
+            const float4* mp = reinterpret_cast<const float4*>(p.mult + static_cast<int64_t>(c) * g * 8 + t * 8);
+            m0 = mp[0];
+            m1 = mp[1];
+        }
+        mlt[c][0] = m0.x; mlt[c][1] = m0.y; mlt[c][2] = m0.z; mlt[c][3] = m0.w;
+        mlt[c][4] = m1.x; mlt[c][5] = m1.y; mlt[c][6] = m1.z; mlt[c][7] = m1.w;
+    }
+    constexpr float NRM = HB == 64 ? 0.125f : 0.08838834764831845f;   // fp32(1/sqrt(HB))
+    const float sigma = (__builtin_popcount(lane & (HB / 8 - 1)) & 1) ? -1.f : 1.f;
+
+    auto load_rows = [&](int64_t row, uint4 (&raw)[NCH][SRC]) {
+        const int64_t r = row < p.m ? row : p.m - 1;
+        const uint16_t* xrow = static_cast<const uint16_t*>(p.x) + r * p.ldx;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int sidx = 0; sidx < SRC; ++sidx)
+                raw[c][sidx] = *reinterpret_cast<const uint4*>(xrow + static_cast<int64_t>(c) * g * 8 + t * 8 + sidx * p.k);
+    };
+
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * rpb;
+    int64_t row = static_cast<int64_t>(blockIdx.x) * rpb + tid / g;
+    uint4 raw[NCH][SRC];
+    load_rows(row, raw);
+    int parity = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * rpb; base < p.m;
+         base += stride, row += stride, parity ^= 1) {
+        uint4 nxt[PF ? NCH : 1][SRC];
+        if constexpr (PF) load_rows(row + stride, nxt);
+
+        float v[NCH][8];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint32_t u[4] = {raw[c][SRC - 1].x, raw[c][SRC - 1].y, raw[c][SRC - 1].z, raw[c][SRC - 1].w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(u[i] << 16);
+                x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+            }
+            if constexpr (GEGLU) {
+                float gl[8];
+                gelu8_fast(raw[c][0], gtab, gl);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= gl[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = x[e] * mlt[c][e];
+#pragma unroll
+            for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((e & h) == 0) {
+                        const float a0 = v[c][e], a1 = v[c][e + h];
+                        v[c][e] = a0 + a1;
+                        v[c][e + h] = a0 - a1;
+                    }
+                }
+            }
+        }
+        {
+            const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f;
+            const float s4 = (lane & 4) ? -1.f : 1.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                xlane8<1>(v[c], s1);
+                xlane8<2>(v[c], s2);
+                xlane4_fast(v[c], s4);
+                if constexpr (HB == 128) xlane8<8>(v[c], (lane & 8) ? -1.f : 1.f);
+            }
+        }
+
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) amax = fmaxf(amax, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+        amax = wave_max(amax, g < 64 ? g : 64);
+        if (g > 64) {
+            if (lane == 0) red[parity][wave] = amax;
+            __syncthreads();
+            const int wpr = g >> 6;
+            const int first = (wave / wpr) * wpr;
+            amax = red[parity][first];
+            for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[parity][first + i]);
+        }
+
+        if (row < p.m) {
+            const float scale = (amax * NRM) / QMAX;
+            const float mul = (scale > 0.f) ? sigma * (NRM * (1.f / scale)) : 0.f;
+            if (t == 0) p.scale[row] = scale;
+            constexpr float M = 12582912.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int64_t col = static_cast<int64_t>(c) * g * 8 + t * 8;
+                float qb[8];
+                float worst = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[e] = fmaf(v[c][e], mul, M);
+#pragma unroll
+                for (int e = 0; e < 8; e += 2)
+                    worst = fmaxf(worst, fmaxf(fabsf(fmaf(v[c][e], mul, M - qb[e])),
+                                               fabsf(fmaf(v[c][e + 1], mul, M - qb[e + 1]))));
+                if (worst >= 0.5f - kTieWindow) {
+                    const double div = sigma * static_cast<double>(scale) * (HB == 64 ? 8.0 : 11.313708498984761);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qb[e] = quant_code(v[c][e], mul, div, QMAX) + M;
+                }
+                uint32_t cb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(qb[e]);
+                if constexpr (BITS == 8) {
+                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
+                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
+                } else {
+                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
+                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
+                }
+            }
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int sidx = 0; sidx < SRC; ++sidx) raw[c][sidx] = nxt[c][sidx];
+        } else {
+            load_rows(row + stride, raw);
         }
     }
 }
@@ -510,20 +762,89 @@ __global__ void fold_finish_kernel(float* s, float* inv_s, int64_t k) {
 
 namespace {
 
-template <int DT, bool GEGLU, int TPB>
-hipError_t launch_rows_tpb(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int DT, int NCH, bool GEGLU, int TPB>
+hipError_t launch_rows_nch(const RowQuantParams& p, hipStream_t st) {
+    auto kern = rotate_quant_rows_kernel<DT, NCH, GEGLU, TPB>;
+    // resident blocks per CU of this instantiation (queried once)
+    static const int per_cu = [&] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, TPB, 0) != hipSuccess || n <= 0) n = 1;
+        return n;
+    }();
     const int rows_per_block = TPB / p.g;
     const int64_t groups = (p.m + rows_per_block - 1) / rows_per_block;
-    // one row group per block (capped only by the grid-size limit)
-    const int64_t slots = 0x7FFFFFFFLL;
+    // persistent blocks: as many as are resident at once, at most one per row group
+    const int64_t slots = static_cast<int64_t>(device_cus()) * per_cu;
     dim3 grid(static_cast<unsigned>(groups < slots ? groups : slots));
+    hipLaunchKernelGGL(kern, grid, dim3(TPB), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int DT, bool GEGLU, int TPB>
+hipError_t launch_rows_tpb(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
     switch (nch_tpl) {
-        case 1: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 1, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
-        case 2: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 2, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
-        case 4: hipLaunchKernelGGL((rotate_quant_rows_kernel<DT, 4, GEGLU, TPB>), grid, dim3(TPB), 0, st, p); break;
+        case 1: return launch_rows_nch<DT, 1, GEGLU, TPB>(p, st);
+        case 2: return launch_rows_nch<DT, 2, GEGLU, TPB>(p, st);
+        case 4: return launch_rows_nch<DT, 4, GEGLU, TPB>(p, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int NCH, bool GEGLU, int HB, int BITS, int TPB>
+hipError_t launch_fast(const RowQuantParams& p, hipStream_t st) {
+    auto kern = rotate_quant_bf16_kernel<NCH, GEGLU, HB, BITS, TPB>;
+    static const int per_cu = [&] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, TPB, 0) != hipSuccess || n <= 0) n = 1;
+        return n;
+    }();
+    const int rows_per_block = TPB / p.g;
+    const int64_t groups = (p.m + rows_per_block - 1) / rows_per_block;
+    const int64_t slots = static_cast<int64_t>(device_cus()) * per_cu;
+    dim3 grid(static_cast<unsigned>(groups < slots ? groups : slots));
+    hipLaunchKernelGGL(kern, grid, dim3(TPB), 0, st, p);
     return hipGetLastError();
+}
+
+template <bool GEGLU, int HB, int BITS, int TPB>
+hipError_t launch_fast_nch(const RowQuantParams& p, hipStream_t st) {
+    switch (p.nch) {
+        case 1: return launch_fast<1, GEGLU, HB, BITS, TPB>(p, st);
+        case 2: return launch_fast<2, GEGLU, HB, BITS, TPB>(p, st);
+        case 4: return launch_fast<4, GEGLU, HB, BITS, TPB>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool GEGLU, int HB, int BITS>
+hipError_t launch_fast_tpb(const RowQuantParams& p, hipStream_t st) {
+    if (p.g > 256) return launch_fast_nch<GEGLU, HB, BITS, 1024>(p, st);
+    return launch_fast_nch<GEGLU, HB, BITS, 256>(p, st);
+}
+
+template <bool GEGLU>
+hipError_t launch_fast_geglu(const RowQuantParams& p, hipStream_t st) {
+    if (p.had_block == 64) return p.bits == 8 ? launch_fast_tpb<GEGLU, 64, 8>(p, st) : launch_fast_tpb<GEGLU, 64, 4>(p, st);
+    return p.bits == 8 ? launch_fast_tpb<GEGLU, 128, 8>(p, st) : launch_fast_tpb<GEGLU, 128, 4>(p, st);
+}
+
+hipError_t launch_bf16_fast(const RowQuantParams& p, bool geglu, hipStream_t st) {
+    return geglu ? launch_fast_geglu<true>(p, st) : launch_fast_geglu<false>(p, st);
 }
 
 template <int DT, bool GEGLU>
@@ -579,6 +900,10 @@ hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, i
     int tpl = 1;
     while (tpl < p.nch) tpl <<= 1;
     if (tpl > 4) return hipErrorInvalidValue;
+    // bfloat16 rows made of whole chunk passes, Hadamard block 64 or 128
+    if (dtype == BF16 && (had_block == 64 || had_block == 128) && tpl == p.nch &&
+        static_cast<int64_t>(p.nch) * 8 * p.g == k && p.g >= had_block / 8)
+        return launch_bf16_fast(p, geglu, st);
     if (geglu) {
         switch (dtype) {
             case F16: return launch_rows_dt<F16, true>(p, tpl, st);

@@ -31,9 +31,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 // float -> bfloat16 bits, round half to even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt_pk_bf16_f32
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {

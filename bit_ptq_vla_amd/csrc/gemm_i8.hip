@@ -21,12 +21,16 @@
 // Tiling: a 256-lane block (4 waves, 2 x 2) owns a BM x BN output tile; each
 // wave owns (BM/2) x (BN/2) as (BM/64) x (BN/64) MFMA tiles held in
 // accumulator registers.  K advances in stages of 64 bytes per row (64 int8
-// or 128 int4 codes): 16-byte global loads into registers for stage s+1 are
-// in flight while stage s is read from LDS (double buffer, rows padded to 80
-// bytes so that 16-byte LDS reads of 8 consecutive rows hit distinct banks).
+// or 128 int4 codes).  Stages land in a ring of NS LDS buffers by LDS DMA
+// (buffer_load ... lds, 16 bytes per lane, no register round trip), issued
+// NS-1 stages ahead; one s_waitcnt + s_barrier per stage publishes a stage
+// and retires the buffer the next DMA overwrites.  Within a stage buffer the
+// four 16-byte chunks of a row are XOR-swizzled so that the MFMA operand
+// reads (ds_read_b128, 32 rows x one chunk) are bank-conflict free.
 // Block indices are remapped so that each XCD (dispatch is round-robin over
 // the 8 XCDs) works on a contiguous range of tiles with M fastest, which
 // keeps a weight tile in one XCD's L2 while it is reused.
+// The epilogue stages each wave's tile through LDS and writes 16-byte rows.
 // Split-K writes int32 partial tiles; a second kernel sums them in a fixed
 // order (integer addition: bit-exact) and applies the epilogue.
 
@@ -54,8 +58,9 @@ struct GemmParams {
     int y_dtype;
 };
 
-__device__ __forceinline__ v4i unpack_lo(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-    (void)w2; (void)w3;
+// 16 packed int4 codes (two dwords) -> one MFMA operand of 16 int8 values 16 * code:
+// the even codes of both dwords, then the odd codes.
+__device__ __forceinline__ v4i unpack_int4(uint32_t w0, uint32_t w1) {
     return v4i{static_cast<int>((w0 << 4) & 0xF0F0F0F0u), static_cast<int>((w1 << 4) & 0xF0F0F0F0u),
                static_cast<int>(w0 & 0xF0F0F0F0u), static_cast<int>(w1 & 0xF0F0F0F0u)};
 }
@@ -67,46 +72,6 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, int dt, float v)
         static_cast<uint16_t*>(y)[idx] = f32_to_f16_bits(v);
     } else {
         static_cast<float*>(y)[idx] = v;
-    }
-}
-
-// Stores one wave's accumulator tiles.  OUT = -1 writes raw int32 partials
-// (split-K), I32 raw accumulators, else the dequantized value in that dtype.
-// Accumulator r of a 32x32 MFMA tile sits at column lane%32 and row
-// 8*(r/4) + 4*(lane/32) + r%4.
-template <int TM, int TN, bool INT4, int OUT>
-__device__ __forceinline__ void write_tile(const v16i (&acc)[TM][TN], const GemmParams& p,
-                                           int64_t row_base, int64_t col_base, int lane, void* dst) {
-    const int col_in = lane & 31;
-    const int row_in = (lane >> 5) * 4;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int64_t col = col_base + j * 32 + col_in;
-        const bool col_ok = col < p.n;
-        float swv = 0.f;
-        if constexpr (OUT == BF16 || OUT == F16 || OUT == F32) swv = col_ok ? p.sw[col] : 0.f;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = row_base + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
-                int32_t a = acc[i][j][r];
-                if constexpr (INT4) a >>= 8;
-                if (col_ok && row < p.m) {
-                    const int64_t idx = row * p.n + col;
-                    if constexpr (OUT == -1 || OUT == I32) {
-                        static_cast<int32_t*>(dst)[idx] = a;
-                    } else {
-                        const float v = static_cast<float>(a) * p.sx[row] * swv;
-                        if constexpr (OUT == BF16) static_cast<uint16_t*>(dst)[idx] = f32_to_bf16_rne(v);
-                        else if constexpr (OUT == F16) static_cast<uint16_t*>(dst)[idx] = f32_to_f16_bits(v);
-                        else static_cast<float*>(dst)[idx] = v;
-                    }
-                }
-            }
-            // keep the scheduler from hoisting every accumulator read at once
-            __builtin_amdgcn_sched_barrier(0);
-        }
     }
 }
 
@@ -182,6 +147,9 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
         if constexpr (FLOAT_OUT)
             swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                 rs_w, static_cast<int>((col0 + j * 32 + l32) * 4), 0, 0));
+        // int4: the accumulator holds 256 * acc; fp32(256 * acc) is exact (acc has
+        // at most 17 significant bits), so the 1/256 joins the column scale
+        if constexpr (FLOAT_OUT && INT4) swv[j] *= 0.00390625f;
     }
     const int64_t ldy = p.n;
     const bool vec_ok = ((p.n * E) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
@@ -207,13 +175,13 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
                     const int rl = ti * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     int8_t* at = region + rl * PITCH + (j * 32 + l32) * E;
                     int32_t a = acc[i][j][r];
-                    if constexpr (INT4) a >>= 8;
                     if constexpr (FLOAT_OUT) {
                         const float v = static_cast<float>(a) * sxv[r >> 2][r & 3] * swv[j];
                         if constexpr (OUT == BF16) *reinterpret_cast<uint16_t*>(at) = f32_to_bf16_rne(v);
                         else if constexpr (OUT == F16) *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(v);
                         else *reinterpret_cast<float*>(at) = v;
                     } else {
+                        if constexpr (INT4) a >>= 8;
                         *reinterpret_cast<int32_t*>(at) = a;
                     }
                 }
@@ -262,10 +230,10 @@ __device__ __forceinline__ void mma_slice(v16i (&acc)[TM][TN], const uint4 (&fa)
             v4i oa[TM], ob[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                oa[i] = h == 0 ? unpack_lo(fa[i].x, fa[i].y, 0, 0) : unpack_lo(fa[i].z, fa[i].w, 0, 0);
+                oa[i] = h == 0 ? unpack_int4(fa[i].x, fa[i].y) : unpack_int4(fa[i].z, fa[i].w);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                ob[j] = h == 0 ? unpack_lo(fb[j].x, fb[j].y, 0, 0) : unpack_lo(fb[j].z, fb[j].w, 0, 0);
+                ob[j] = h == 0 ? unpack_int4(fb[j].x, fb[j].y) : unpack_int4(fb[j].z, fb[j].w);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
