@@ -200,7 +200,7 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
             if (gr < p.m) {
                 char* out = static_cast<char*>(dst) + (gr * ldy + gc) * E;
                 if (vec_ok && gc + 16 / E <= p.n) {
-                    *reinterpret_cast<uint4*>(out) = v;
+                    __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(out));
                 } else {
                     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -217,36 +217,6 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_wave_barrier();
-    }
-}
-
-// One k-slice of MFMA work: 32 bytes of every row (32 int8 or 64 int4
-// codes) for the wave's TM x TN tiles.
-template <int TM, int TN, bool INT4>
-__device__ __forceinline__ void mma_slice(v16i (&acc)[TM][TN], const uint4 (&fa)[TM], const uint4 (&fb)[TN]) {
-    if constexpr (INT4) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v4i oa[TM], ob[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                oa[i] = h == 0 ? unpack_int4(fa[i].x, fa[i].y) : unpack_int4(fa[i].z, fa[i].w);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                ob[j] = h == 0 ? unpack_int4(fb[j].x, fb[j].y) : unpack_int4(fb[j].z, fb[j].w);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[i], ob[j], acc[i][j], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, fa[i]),
-                                                                  __builtin_bit_cast(v4i, fb[j]), acc[i][j], 0, 0, 0);
     }
 }
 
@@ -329,63 +299,127 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     const int b_rd0 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
     const int b_rd1 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
 
+    // Pipeline unit: what one 16-byte LDS read per operand fragment feeds.
+    // int4: one chunk (two MFMA k-slices once unpacked), two units per stage;
+    // int8: the whole stage (two chunks, one k-slice each), one unit per stage.
+    // The reads of unit u+1 are in flight while unit u's MFMAs run, and for
+    // int4 the unpacking of the next k-slice runs under the current MFMAs.
+    constexpr int UPS = INT4 ? 2 : 1;
+    constexpr int FR = INT4 ? 1 : 2;
+    struct Unit {
+        uint4 a[FR][TM];
+        uint4 b[FR][TN];
+    };
+    auto read_unit = [&](const int8_t* st, int ks0, Unit& u) {
 #pragma unroll
-    for (int pst = 0; pst < NS - 1; ++pst)
-        if (pst < nst) issue(pst, lds + pst * STAGE);
-
-    // One stage of work from LDS buffer `st` (both 32-byte k-slices).
-    auto compute = [&](const int8_t* st) {
-        uint4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        for (int f = 0; f < FR; ++f) {
+            const int ar = (ks0 + f) == 0 ? a_rd0 : a_rd1;
+            const int br = (ks0 + f) == 0 ? b_rd0 : b_rd1;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa0[i] = *reinterpret_cast<const uint4*>(st + a_rd0 + i * 32 * STAGE_BYTES);
+            for (int i = 0; i < TM; ++i) u.a[f][i] = *reinterpret_cast<const uint4*>(st + ar + i * 32 * STAGE_BYTES);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb0[j] = *reinterpret_cast<const uint4*>(st + b_rd0 + j * 32 * STAGE_BYTES);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa1[i] = *reinterpret_cast<const uint4*>(st + a_rd1 + i * 32 * STAGE_BYTES);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb1[j] = *reinterpret_cast<const uint4*>(st + b_rd1 + j * 32 * STAGE_BYTES);
-        mma_slice<TM, TN, INT4>(acc, fa0, fb0);
-        mma_slice<TM, TN, INT4>(acc, fa1, fb1);
-        // scheduling: the 2 * (TM + TN) LDS reads first, then the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
-        if constexpr (INT4) {
-#pragma unroll
-            for (int g = 0; g < 4 * TM * TN; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-            }
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
+            for (int j = 0; j < TN; ++j) u.b[f][j] = *reinterpret_cast<const uint4*>(st + br + j * 32 * STAGE_BYTES);
         }
     };
-    // Stage `it` has landed once at most min(NS-2, nst-1-it) later stages of
-    // this wave's DMA are outstanding; the barrier then publishes every
-    // wave's part and retires the reads of the buffer the next DMA reuses.
-    auto wait_stage = [&](int it) {
-        const int after = (nst - 1 - it) < (NS - 2) ? (nst - 1 - it) : (NS - 2);
-        if (NS >= 4 && after >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * LOADS>();
-        else if (after == 1) wait_vmcnt<LOADS>();
+    // int4 k-slice h (0: dwords x,y; 1: z,w) of a unit as MFMA operands
+    auto unpack = [&](const Unit& u, int h, v4i (&oa)[TM], v4i (&ob)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            oa[i] = h == 0 ? unpack_int4(u.a[0][i].x, u.a[0][i].y) : unpack_int4(u.a[0][i].z, u.a[0][i].w);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            ob[j] = h == 0 ? unpack_int4(u.b[0][j].x, u.b[0][j].y) : unpack_int4(u.b[0][j].z, u.b[0][j].w);
+    };
+    auto mfma_slice = [&](const v4i (&oa)[TM], const v4i (&ob)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[i], ob[j], acc[i][j], 0, 0, 0);
+    };
+
+    // prologue: NS stages in flight, stage 0 published, its first unit read
+    {
+        const int pro = nst < NS ? nst : NS;
+#pragma unroll
+        for (int pst = 0; pst < NS; ++pst)
+            if (pst < pro) issue(pst, lds + pst * STAGE);
+        // stage 0 has landed once at most pro - 1 stages are outstanding
+        if (pro == NS) wait_vmcnt<(NS - 1) * LOADS>();
+        else if (pro >= 3) wait_vmcnt<2 * LOADS>();
+        else if (pro == 2) wait_vmcnt<LOADS>();
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+    }
+    Unit cur;
+    v4i op_a[TM], op_b[TN];   // int4: unpacked k-slice 0 of `cur`
+    read_unit(lds, 0, cur);
+    if constexpr (INT4) unpack(cur, 0, op_a, op_b);
+
+    // One stage: its units in turn.  Before the last unit's MFMAs the next
+    // stage is published (this wave's DMA for it landed + barrier, after every
+    // read of this stage's buffer has completed), the buffer of this stage
+    // takes the DMA of stage it + NS, and the next stage's first unit is read.
+    auto stage_step = [&](int it, int8_t* buf, int8_t* nbuf) {
+#pragma unroll
+        for (int ks = 0; ks < UPS; ++ks) {
+            const bool last = ks == UPS - 1;
+            Unit nxt;
+            if (!last) {
+                read_unit(buf, ks + 1, nxt);
+            } else {
+                if (it + 1 < nst) {
+                    // stage it+1 has landed once at most min(NS-2, nst-2-it) later stages are outstanding
+                    const int after = (nst - 2 - it) < (NS - 2) ? (nst - 2 - it) : (NS - 2);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    if (after >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * LOADS>();
+                    else if (after == 1) wait_vmcnt<LOADS>();
+                    else wait_vmcnt<0>();
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    if (it + NS < nst) issue(it + NS, buf);
+                }
+                // after the final stage this reads stale LDS that nothing uses
+                read_unit(nbuf, 0, nxt);
+            }
+            if constexpr (INT4) {
+                v4i o1a[TM], o1b[TN];
+                unpack(cur, 1, o1a, o1b);
+                mfma_slice(op_a, op_b);
+                unpack(nxt, 0, op_a, op_b);   // unused after the last unit (no branch: one schedule)
+                mfma_slice(o1a, o1b);
+                // scheduling: next unit's reads first, then each MFMA with ~4 VALU of unpacking
+                __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+                for (int g = 0; g < 2 * TM * TN; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            } else {
+                v4i a0[TM], b0[TN], a1[TM], b1[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) { a0[i] = __builtin_bit_cast(v4i, cur.a[0][i]); a1[i] = __builtin_bit_cast(v4i, cur.a[1][i]); }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) { b0[j] = __builtin_bit_cast(v4i, cur.b[0][j]); b1[j] = __builtin_bit_cast(v4i, cur.b[1][j]); }
+                mfma_slice(a0, b0);
+                mfma_slice(a1, b1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
+            }
+            cur = nxt;
+        }
     };
 
-    // Whole groups of NS stages: the ring position is a compile-time constant.
+    // Whole groups of NS stages: the ring positions are compile-time constants.
     const int nfull = nst - nst % NS;
     for (int it0 = 0; it0 < nfull; it0 += NS) {
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            const int it = it0 + u;
-            wait_stage(it);
-            if (it + NS - 1 < nst) issue(it + NS - 1, lds + ((u + NS - 1) % NS) * STAGE);
-            compute(lds + u * STAGE);
-        }
+        for (int u = 0; u < NS; ++u) stage_step(it0 + u, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
     }
-    // Remaining stages (< NS); their DMA was issued by the loop above.
     for (int it = nfull; it < nst; ++it) {
-        wait_stage(it);
         const int u = it - nfull;
-        compute(lds + u * STAGE);
+        stage_step(it, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
     }
 
     // ---- epilogue: every wave is done with the ring; each takes one buffer
