@@ -47,6 +47,7 @@ SIGNATURES = {
     "qlin_rotate_quant_act": [_P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P],
     "qlin_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w8a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
 }
 
@@ -182,6 +183,31 @@ def qlin_gemm_w4a4(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out
 def qlin_gemm_w8a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
     """y [m][n] from int8 codes xq [m][k], wq [n][k]."""
     return _gemm("qlin_gemm_w8a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
+
+
+def qlin_gemm_w4a4_geglu(xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """h [m][n2/2] = gelu(gate) * up from packed int4 codes xq [m][k/2] and the
+    gate|up weight codes wq [n2][k/2] with rows interleaved in blocks of 32."""
+    lib = load()
+    _dev_tensor(wq, "wq")
+    m, n2 = xq.shape[0], wq.shape[0]
+    h = out if out is not None else torch.empty((m, n2 // 2), dtype=h_dtype, device=wq.device)
+    st = lib.qlin_gemm_w4a4_geglu(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n2, k,
+                                  h.data_ptr(), _TORCH_TO_QLIN[h.dtype], _stream(wq.device))
+    _check(st, "qlin_gemm_w4a4_geglu")
+    return h
+
+
+def interleave_gate_up(gate: torch.Tensor, up: torch.Tensor, block: int = 32) -> torch.Tensor:
+    """Rows of the fused gate|up weight (layout of qlin_gemm_w4a4_geglu): blocks
+    of `block` gate rows, each followed by the same rows of up.  Pure data
+    movement (torch ops), for preparing weights before quantization."""
+    f = gate.shape[0]
+    if up.shape[0] != f or f % block:
+        raise ValueError("gate and up need the same row count, a multiple of the block")
+    tail = tuple(gate.shape[1:])
+    return torch.cat([gate.reshape((f // block, block) + tail), up.reshape((f // block, block) + tail)],
+                     dim=1).reshape((2 * f,) + tail)
 
 
 def qlin_gemv_w4a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, group: int = 128,

@@ -34,6 +34,8 @@
 // Split-K writes int32 partial tiles; a second kernel sums them in a fixed
 // order (integer addition: bit-exact) and applies the epilogue.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "qlin_internal.h"
 
@@ -57,6 +59,10 @@ struct GemmParams {
     int tiles_m, tiles_n, splits;
     int y_dtype;
 };
+
+// OUT codes of the epilogue: -1 raw int32 split-K partials, a dtype (F16,
+// BF16, F32, I32), or OUT_GEGLU + dtype for the fused GeGLU output.
+constexpr int OUT_GEGLU = 16;
 
 // 16 packed int4 codes (two dwords) -> one MFMA operand of 16 int8 values 16 * code:
 // the even codes of both dwords, then the odd codes.
@@ -108,6 +114,156 @@ __device__ __forceinline__ void dma16(v4i rsrc, int voff, uint32_t lds_addr) {
         :
         : "v"(voff), "s"(rsrc), "s"(lds_addr)
         : "memory", "m0");
+}
+
+// ---- GeLU for the fused GeGLU epilogue -------------------------------------
+// T(x) = x * Phi(-x) = -gelu(-x) for the bfloat16 values 2^-12 <= x < 16
+// (16 exponents x 128 mantissas, 8 KB), evaluated in float64 through erfc
+// and rounded to fp32.  Then gelu(g) = -T(|g|) for g < 0 and g - T(g) for
+// g > 0: both within about one fp32 rounding of the exact value (T is the
+// small part of gelu(g) = g - T for g > 0, so the subtraction loses nothing).
+// |g| < 2^-12: g/2 + g^2/sqrt(2 pi) (the next term is 2^-36 relative);
+// |g| >= 16: g or 0 (T(16) ~ 1e-56).
+constexpr int GTAB_EF0 = 127 - 12;
+constexpr int GTAB_N = 16 * 128;
+constexpr int GTAB_BYTES = GTAB_N * 4;
+
+__device__ float g_gelu_neg_tab[GTAB_N];
+
+__global__ void gelu_neg_tab_init_kernel() {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= GTAB_N) return;
+    const double x = static_cast<double>(__uint_as_float(static_cast<uint32_t>(i + (GTAB_EF0 << 7)) << 16));
+    g_gelu_neg_tab[i] = static_cast<float>(0.5 * x * erfc(x * 0.70710678118654752440));
+}
+
+// gelu of a bfloat16 value (bits) that the table does not cover
+__device__ __forceinline__ float gelu_outside_tab(uint32_t bits) {
+    const float g = __uint_as_float(bits << 16);
+    const float tiny = fmaf(g * g, 0.39894228040143267794f, 0.5f * g);
+    const float big = g > 0.f ? g : (g == g ? 0.f : g);
+    return (((bits & 0x7FFFu) >> 7) < static_cast<uint32_t>(GTAB_EF0)) ? tiny : big;
+}
+
+// GeGLU epilogue of a wave's (BM/2) x (BN/2) tile whose columns are gate and
+// up rows of W interleaved in blocks of 32: MFMA column tiles 2q (gate) and
+// 2q+1 (up) hold the same output channels, so a lane has g and u of one
+// element in registers.  g and u are dequantized in fp32 and rounded to
+// bfloat16 (as the unfused chain stores them), gelu(g) is formed from the
+// T table kept in LDS (16 table reads in flight per group, one branch per
+// group for values outside it), h = gelu(g) * u is rounded to the output
+// dtype and staged through LDS for 16-byte row stores of the (BM/2) x (BN/4)
+// h tile.
+template <int BM, int BN, bool INT4, int ODT, int STAGE>
+__device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
+                                                 int64_t row0, int64_t col0, int lane, const float* tab,
+                                                 int8_t* region) {
+    constexpr int TM = BM / 64, TN = BN / 64;
+    static_assert(TN % 2 == 0, "gate/up column tiles come in pairs");
+    constexpr int WM = BM / 2, WH = BN / 4;              // wave tile rows, h columns
+    constexpr int E = (ODT == BF16 || ODT == F16) ? 2 : 4;
+    constexpr int ROWB = WH * E;
+    constexpr int PITCH = ROWB + (E == 2 ? 16 : 32);
+    constexpr int RP = (WM * PITCH <= STAGE) ? WM : (WM / 2 * PITCH <= STAGE) ? WM / 2 : 16;
+    static_assert(RP >= 16 && WM % RP == 0 && RP * PITCH <= STAGE, "staging does not fit");
+    constexpr int CPR = ROWB / 16;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int64_t nh = p.n / 2;                          // h columns
+    const int64_t hcol0 = col0 / 2;
+
+    const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sx), 0, static_cast<int>(p.m * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.sw), 0, static_cast<int>(p.n * 4), 0x00020000);
+    float swg[TN / 2], swu[TN / 2];
+#pragma unroll
+    for (int q = 0; q < TN / 2; ++q) {
+        swg[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            rs_w, static_cast<int>((col0 + 64 * q + l32) * 4), 0, 0));
+        swu[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            rs_w, static_cast<int>((col0 + 64 * q + 32 + l32) * 4), 0, 0));
+        if constexpr (INT4) { swg[q] *= 0.00390625f; swu[q] *= 0.00390625f; }   // 256 * acc, exact
+    }
+    const bool vec_ok = ((nh * E) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+
+#pragma unroll
+    for (int pass = 0; pass < WM / RP; ++pass) {
+#pragma unroll
+        for (int rr = 0; rr < RP; rr += 32) {
+            const int i = (pass * RP + rr) / 32;
+            f4 sxv[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                sxv[g4] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs_x, static_cast<int>((row0 + i * 32 + 8 * g4 + 4 * half) * 4), 0, 0));
+#pragma unroll
+            for (int q = 0; q < TN / 2; ++q) {
+                // the 16 values of a lane: all table reads in flight together,
+                // one branch per group for values outside the table
+                uint32_t gb[16], idx[16];
+                float ub[16], gl[16];
+                bool all_in = true;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float sx = sxv[r >> 2][r & 3];
+                    const float g = static_cast<float>(acc[i][2 * q][r]) * sx * swg[q];
+                    const float u = static_cast<float>(acc[i][2 * q + 1][r]) * sx * swu[q];
+                    gb[r] = f32_to_bf16_rne(g);
+                    ub[r] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(u)) << 16);
+                    idx[r] = (gb[r] & 0x7FFFu) - static_cast<uint32_t>(GTAB_EF0 << 7);
+                    all_in = all_in && idx[r] < static_cast<uint32_t>(GTAB_N);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float t = tab[idx[r] & (GTAB_N - 1)];
+                    gl[r] = (gb[r] & 0x8000u) ? -t : __uint_as_float(gb[r] << 16) - t;
+                }
+                if (!all_in) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (idx[r] >= static_cast<uint32_t>(GTAB_N)) gl[r] = gelu_outside_tab(gb[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rl = rr + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (RP < 32 && rl >= RP) continue;
+                    const float h = gl[r] * ub[r];
+                    int8_t* at = region + rl * PITCH + (q * 32 + l32) * E;
+                    if constexpr (ODT == BF16) *reinterpret_cast<uint16_t*>(at) = f32_to_bf16_rne(h);
+                    else if constexpr (ODT == F16) *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(h);
+                    else *reinterpret_cast<float*>(at) = h;
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+        for (int c = lane; c < RP * CPR; c += 64) {
+            const int rl = c / CPR, cc = c - rl * CPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(region + rl * PITCH + cc * 16);
+            const int64_t gr = row0 + pass * RP + rl;
+            const int64_t gc = hcol0 + cc * (16 / E);
+            if (gr < p.m) {
+                char* out = static_cast<char*>(p.y) + (gr * nh + gc) * E;
+                if (vec_ok && gc + 16 / E <= nh) {
+                    __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(out));
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 16 / E; ++e) {
+                        if (gc + e < nh) {
+                            if constexpr (E == 2)
+                                reinterpret_cast<uint16_t*>(out)[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+                            else
+                                reinterpret_cast<uint32_t*>(out)[e] = w[e];
+                        }
+                    }
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // Stores a wave's (BM/2) x (BN/2) accumulator tile through LDS so that the
@@ -231,7 +387,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     constexpr int STAGE = (BM + BN) * STAGE_BYTES;
     // The DMA is issued through inline assembly, invisible to the compiler,
     // so one array serves the whole ring (and the epilogue staging after it).
-    __shared__ __attribute__((aligned(1024))) int8_t lds[NS * STAGE];
+    // The fused GeGLU epilogue keeps its GeLU table after the ring from the start.
+    constexpr bool GEGLU = OUT >= OUT_GEGLU;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[NS * STAGE + (GEGLU ? GTAB_BYTES : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -338,6 +496,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[i], ob[j], acc[i][j], 0, 0, 0);
     };
 
+    // GeGLU: the table's DMA goes first, so the prologue's wait for stage 0
+    // (loads complete in issue order) covers it, and its barrier publishes it.
+    if constexpr (GEGLU) {
+        static_assert(GTAB_BYTES == 2 * 4 * 1024, "two 16-byte loads per lane");
+        const v4i rsrc_t = make_rsrc(reinterpret_cast<const int8_t*>(g_gelu_neg_tab), GTAB_BYTES);
+        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + NS * STAGE)) + wave_u * 1024;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(rsrc_t, (i * 4 + wave) * 1024 + lane * 16, t_dst + i * 4096);
+    }
+
     // prologue: NS stages in flight, stage 0 published, its first unit read
     {
         const int pro = nst < NS ? nst : NS;
@@ -424,10 +592,17 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
 
     // ---- epilogue: every wave is done with the ring; each takes one buffer
     __syncthreads();
-    void* dst = (OUT == -1) ? static_cast<void*>(p.ws + static_cast<int64_t>(split) * p.m * p.n) : p.y;
-    constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
-    store_tile_lds<BM, BN, INT4, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
-                                              lds + wave * REGION, dst);
+    if constexpr (GEGLU) {
+        constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
+        store_tile_geglu<BM, BN, INT4, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),
+                                                                lane, reinterpret_cast<const float*>(lds + NS * STAGE),
+                                                                lds + wave * REGION);
+    } else {
+        void* dst = (OUT == -1) ? static_cast<void*>(p.ws + static_cast<int64_t>(split) * p.m * p.n) : p.y;
+        constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
+        store_tile_lds<BM, BN, INT4, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                                  lds + wave * REGION, dst);
+    }
 }
 
 // Sum of split-K partials in split order (integer: bit-exact), then the
@@ -475,6 +650,34 @@ hipError_t launch_out(const GemmParams& p, hipStream_t st) {
         case I32: return launch_tile<BM, BN, MINB, NS, INT4, I32>(p, st);
     }
     return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int MINB, int NS, bool INT4>
+hipError_t launch_geglu_out(const GemmParams& p, hipStream_t st) {
+    switch (p.y_dtype) {
+        case BF16: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + BF16>(p, st);
+        case F16: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + F16>(p, st);
+        case F32: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + F32>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+std::mutex g_gtab_mu;
+bool g_gtab_ready[64] = {false};
+
+// Fills the fused epilogue's GeLU table on the current device (once per device,
+// on the caller's stream, ahead of the first GEMM that reads it).
+hipError_t ensure_gelu_neg_tab(hipStream_t st) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_gtab_mu);
+    if (g_gtab_ready[dev]) return hipSuccess;
+    hipLaunchKernelGGL(gelu_neg_tab_init_kernel, dim3((GTAB_N + 255) / 256), dim3(256), 0, st);
+    e = hipGetLastError();
+    if (e == hipSuccess) g_gtab_ready[dev] = true;
+    return e;
 }
 
 }  // namespace
@@ -529,6 +732,29 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
         e = hipGetLastError();
     }
     return e;
+}
+
+hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                             int64_t m, int64_t n, int64_t k, bool int4, void* y, int y_dtype,
+                             hipStream_t st) {
+    if (!int4) return hipErrorInvalidValue;   // the gate|up projections run at W4A4
+    hipError_t e = ensure_gelu_neg_tab(st);
+    if (e != hipSuccess) return e;
+    const GemmPlan plan = plan_gemm(m, n, k, int4);   // tile shape; the fused epilogue takes no split
+    GemmParams p;
+    p.a = static_cast<const int8_t*>(xq);
+    p.b = static_cast<const int8_t*>(wq);
+    p.sx = x_scale; p.sw = w_scale; p.y = y; p.ws = nullptr;
+    p.m = m; p.n = n;
+    p.kbytes = int4 ? k / 2 : k;
+    p.stages = static_cast<int>((p.kbytes + STAGE_BYTES - 1) / STAGE_BYTES);
+    p.splits = 1;
+    p.stages_per_split = p.stages;
+    p.tiles_m = static_cast<int>((m + plan.bm - 1) / plan.bm);
+    p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
+    p.y_dtype = y_dtype;
+    if (plan.bn == 256) return launch_geglu_out<128, 256, 2, 3, true>(p, st);
+    return launch_geglu_out<128, 128, 2, 4, true>(p, st);
 }
 
 }  // namespace qlin

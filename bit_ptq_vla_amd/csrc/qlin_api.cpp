@@ -212,6 +212,26 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
     return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, false);
 }
 
+qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                                 int64_t m, int64_t n2, int64_t k, void* h, qlin_dtype h_dtype, void* stream) {
+    if (!xq && m > 0) return QLIN_ERR_NULL;
+    if (!wq || !h || !w_scale || (!x_scale && m > 0)) return QLIN_ERR_NULL;
+    if (h_dtype != QLIN_F16 && h_dtype != QLIN_BF16 && h_dtype != QLIN_F32) return QLIN_ERR_DTYPE;
+    if (m < 0 || n2 < 64 || (n2 % 64) != 0 || k < 128 || (k % 128) != 0 || k > 131072) return QLIN_ERR_SHAPE;
+    if (m > 0x7FFFFFFF || n2 > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(h) || !aligned16(x_scale) || !aligned16(w_scale))
+        return QLIN_ERR_ALIGN;
+    const int64_t kb = k / 2;
+    const Span outs[1] = {{h, m * (n2 / 2) * dtype_size(h_dtype)}};
+    const Span ins[4] = {{xq, m * kb}, {wq, n2 * kb}, {x_scale, m * 4}, {w_scale, n2 * 4}};
+    if (any_overlap(outs, 1, ins, 4)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    hipStream_t s = as_stream(stream);
+    return map_err(qlin::launch_gemm_geglu(xq, x_scale, wq, w_scale, m, n2, k, true, h, h_dtype, s));
+}
+
 qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m, int64_t n,
                             int64_t k, int32_t group, void* y, void* stream) {
     if (m > 0 && (!x || !y)) return QLIN_ERR_NULL;

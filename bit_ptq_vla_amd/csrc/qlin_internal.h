@@ -31,6 +31,11 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4);
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
                        const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st);
+// Gate|up GEMM with the GeGLU epilogue: n interleaved rows (blocks of 32 gate
+// rows then 32 up rows), y [m][n/2] = gelu(g) * u.  int4 only, no split-K.
+hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                             int64_t m, int64_t n, int64_t k, bool int4, void* y, int y_dtype,
+                             hipStream_t st);
 
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st);

@@ -159,6 +159,31 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
                            qlin_dtype y_dtype, void* stream);
 
 /*
+ * qlin_gemm_w4a4_geglu -- the backbone MLP's gate and up projections with the
+ * gated GeLU fused into the epilogue (FoldQuantVLA abstract: the projections
+ * run natively in integer arithmetic; the gated GeLU joins them here so that
+ * only h, not gate and up, goes to memory).
+ *   wq, w_scale: the gate and up weights quantized together (qlin_quantize_weights
+ *            with bits 4), their rows interleaved in blocks of 32: rows
+ *            64c .. 64c+31 are gate rows 32c .. 32c+31 and rows 64c+32 .. 64c+63
+ *            are up rows 32c .. 32c+31.  n2 = 2 f rows.
+ *   g, u     = fp32(acc) * x_scale[m] * w_scale[row], each rounded to bfloat16
+ *            (as an unfused chain would store them);
+ *   h[m][c]  = round_{h_dtype}(gelu(g[m][c]) * u[m][c]), c = 0 .. f-1, h
+ *            contiguous [m][f]; gelu is the erf form, evaluated in fp32 to
+ *            within about one fp32 rounding; h_dtype F16, BF16 or F32.
+ * Preconditions: m >= 0; n2 a multiple of 64; k a multiple of 128, at most
+ * 131072.  Errors: NULL pointers (QLIN_ERR_NULL), other dtypes
+ * (QLIN_ERR_DTYPE), shapes (QLIN_ERR_SHAPE), pointers not 16-byte aligned
+ * (QLIN_ERR_ALIGN), h overlapping an input (QLIN_ERR_ALIAS); m == 0 returns
+ * QLIN_OK without touching the device.  Never allocates; the first call on a
+ * device also fills a static 8 KB table there (on the same stream).
+ */
+qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq,
+                                 const float* w_scale, int64_t m, int64_t n2, int64_t k, void* h,
+                                 qlin_dtype h_dtype, void* stream);
+
+/*
  * qlin_gemv_w4a16 -- weight-only int4 projection for small batches (LoopQ
  * abstract: batch-1 weight-only kernels of the memory-bound action expert).
  *   y[m][n] = fp16_rne( sum_k x[m][k] * code[n][k] * s16[n][k / group] ),

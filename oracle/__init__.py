@@ -14,6 +14,9 @@ Blocchi"; LoopQ abstract for plain RTN weights and the W4A16 weight-only form):
   quantize        per-row symmetric, round-half-even   (per-token dynamic / RTN)
   integer GEMM    int64 dot products of the codes
   epilogue        acc * s_x[m] * s_w[n]  -> f32 -> f16/bf16 (RNE)
+  GeGLU epilogue  gate|up rows interleaved in blocks of 32; h = gelu(g) * u
+                  from the bf16-rounded dequantized g, u (the fused form of the
+                  backbone MLP's gated GeLU)
   W4A16 GEMV      f64 dot products against q * s16[group]
 
 Floating point is float64 throughout, integers are int64.  Every function is
@@ -38,6 +41,10 @@ from .qlin_ref import (  # noqa: F401
     int_gemm,
     dequant_epilogue,
     gemm,
+    GEGLU_BLOCK,
+    interleave_gate_up,
+    split_gate_up,
+    gemm_geglu,
     gemv_w4a16,
     round_to_bf16_bits,
     bf16_bits_to_f64,

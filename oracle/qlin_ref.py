@@ -335,6 +335,54 @@ def gemm(qx, x_scale, qw, w_scale, out_dtype: str):
     return acc, y32, round_output(y32, out_dtype)
 
 
+# --------------------------------------------------------------------------
+# Fused gate|up projection with the GeGLU epilogue
+# --------------------------------------------------------------------------
+
+GEGLU_BLOCK = 32   # gate and up rows alternate in blocks of this many rows
+
+
+def interleave_gate_up(gate: np.ndarray, up: np.ndarray, block: int = GEGLU_BLOCK) -> np.ndarray:
+    """Rows of the fused gate|up weight (or its per-row scales): block j of
+    gate rows (rows block*j .. block*j + block - 1) followed by the same block
+    of up rows.  gate and up have f rows each, f a multiple of block."""
+    gate = np.asarray(gate)
+    up = np.asarray(up)
+    f = gate.shape[0]
+    if up.shape[0] != f or f % block:
+        raise ValueError("gate and up need the same row count, a multiple of the block")
+    tail = gate.shape[1:]
+    g = gate.reshape((f // block, block) + tail)
+    u = up.reshape((f // block, block) + tail)
+    return np.concatenate([g, u], axis=1).reshape((2 * f,) + tail)
+
+
+def split_gate_up(y: np.ndarray, block: int = GEGLU_BLOCK):
+    """Inverse of interleave_gate_up along the last axis (output columns)."""
+    y = np.asarray(y)
+    n2 = y.shape[-1]
+    v = y.reshape(y.shape[:-1] + (n2 // (2 * block), 2, block))
+    return v[..., 0, :].reshape(y.shape[:-1] + (n2 // 2,)), v[..., 1, :].reshape(y.shape[:-1] + (n2 // 2,))
+
+
+def gemm_geglu(qx, x_scale, qw, w_scale, out_dtype: str, block: int = GEGLU_BLOCK):
+    """Gate|up projection with GeGLU in the epilogue (the fused form of the
+    backbone MLP's gated GeLU).  qw / w_scale hold the gate and up rows
+    interleaved (interleave_gate_up).  Reading: the dequantized gate and up
+    values are rounded to bfloat16 first, as the unfused chain stores them,
+    then h = gelu(g) * u in float64, float32, then out_dtype (RNE).
+
+    Returns (acc int64 [M][2F], h32 float32 [M][F], h_ref float64).
+    """
+    acc = int_gemm(qx, qw)
+    y32 = dequant_epilogue(acc, x_scale, w_scale)
+    g32, u32 = split_gate_up(y32, block)
+    g = bf16_bits_to_f64(round_to_bf16_bits(g32))
+    u = bf16_bits_to_f64(round_to_bf16_bits(u32))
+    h32 = (gelu(g) * u).astype(np.float32)
+    return acc, h32, round_output(h32, out_dtype)
+
+
 def gemv_w4a16(x, qw, s16, group: int):
     """Weight-only product y[m, n] = sum_k x[m, k] * q[n, k] * s16[n, k//group]
     in float64, then float32, then float16 (RNE).  [LQ] abstract: batch-1

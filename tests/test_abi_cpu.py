@@ -37,7 +37,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("qlin_rotate_quant_act", "qlin_quantize_weights", "qlin_gemm_w4a4", "qlin_gemm_w8a8",
-              "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version", "qlin_status_string"):
+              "qlin_gemm_w4a4_geglu", "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version",
+              "qlin_status_string"):
         assert n in names
 
 
@@ -125,6 +126,28 @@ def test_gemm_rejects(lib, fn, kw, status):
 def test_gemm_raw_i32_needs_no_scales_and_empty_ok(lib):
     # no scales with I32 output passes validation; m == 0 then returns before any HIP call
     assert lib.qlin_gemm_w8a8(None, None, P2, None, 0, 64, 512, 0x70000000, 3, None) == q.QLIN_OK
+
+
+# ---- qlin_gemm_w4a4_geglu(xq, sx, wq, sw, m, n2, k, h, hdt, stream)
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xq=None), q.QLIN_ERR_NULL), (dict(wq=None), q.QLIN_ERR_NULL), (dict(h=None), q.QLIN_ERR_NULL),
+    (dict(sx=None), q.QLIN_ERR_NULL), (dict(sw=None), q.QLIN_ERR_NULL),
+    (dict(hdt=3), q.QLIN_ERR_DTYPE), (dict(hdt=9), q.QLIN_ERR_DTYPE),
+    (dict(n2=96), q.QLIN_ERR_SHAPE), (dict(n2=32), q.QLIN_ERR_SHAPE), (dict(k=192), q.QLIN_ERR_SHAPE),
+    (dict(k=64), q.QLIN_ERR_SHAPE), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=131072 + 128), q.QLIN_ERR_SHAPE),
+    (dict(xq=BAD), q.QLIN_ERR_ALIGN), (dict(h=BAD), q.QLIN_ERR_ALIGN),
+    (dict(h=P + 64), q.QLIN_ERR_ALIAS),
+])
+def test_gemm_geglu_rejects(lib, kw, status):
+    a = dict(xq=P, sx=P3, wq=P2, sw=P4, m=16, n2=128, k=512, h=0x70000000, hdt=1)
+    a.update(kw)
+    assert lib.qlin_gemm_w4a4_geglu(a["xq"], a["sx"], a["wq"], a["sw"], a["m"], a["n2"], a["k"], a["h"],
+                                    a["hdt"], None) == status
+
+
+def test_gemm_geglu_empty_is_ok(lib):
+    assert lib.qlin_gemm_w4a4_geglu(None, None, P2, P4, 0, 128, 512, 0x70000000, 1, None) == q.QLIN_OK
 
 
 # ---- qlin_gemv_w4a16(x, wq, ws, m, n, k, group, y, stream)

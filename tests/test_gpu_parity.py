@@ -186,6 +186,38 @@ def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
 
 
+GEGLU_SHAPES = [
+    # m, f (h columns; n2 = 2 f interleaved weight rows), k
+    (50, 64, 256),       # 128-wide tiles
+    (130, 2048, 512),    # 256-wide tiles, ragged m
+    (1, 32, 128),        # one token, one gate/up pair, ragged n tile
+    (300, 4096, 1024),
+]
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,f,k", GEGLU_SHAPES)
+def test_gemm_w4a4_geglu(m, f, k, out):
+    say(f"gemm geglu {out} {m}x{f}x{k}")
+    n2 = 2 * f
+    a = synth.random_codes(SEED, f"Ag/{m}/{k}", m, k, 4)
+    b = synth.random_codes(SEED, f"Bg/{n2}/{k}", n2, k, 4)   # any codes: rows already in fused order
+    sx = synth.random_scales(SEED, f"sxg/{m}", m)
+    sw = synth.random_scales(SEED, f"swg/{n2}", n2)
+    h = q.qlin_gemm_w4a4_geglu(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, h_dtype=DT[out])
+    torch.cuda.synchronize()
+    assert h.shape == (m, f)
+    _, _, h_ref = oracle.gemm_geglu(codes_np(a, 4), sx.numpy(), codes_np(b, 4), sw.numpy(), out)
+    assert_ok(oracle.compare_outputs(f64(h), h_ref), "h")
+
+
+def test_interleave_binding_matches_oracle():
+    g = torch.arange(64 * 3, dtype=torch.int32).reshape(64, 3)
+    u = -g
+    got = q.interleave_gate_up(g, u).numpy()
+    assert np.array_equal(got, oracle.interleave_gate_up(g.numpy(), u.numpy()))
+
+
 def test_gemm_deterministic():
     say("gemm determinism")
     a = synth.random_codes(SEED, "Ad", 129, 16384, 8).to(DEV)
@@ -351,6 +383,46 @@ def test_backbone_mlp_block_stagewise_full_size():
     qh, sh, rh = oracle.rotate_quant_act(y1f[rows], s2g, 128, 8, preop="geglu")
     assert_ok(oracle.compare_codes(codes_np(hq, 8)[rows], qh, rh), "GeGLU act codes")
     assert_ok(oracle.compare_scales(hs.cpu().numpy()[rows], sh), "GeGLU act scales")
+    _, _, y2_ref = oracle.gemm(codes_np(hq, 8)[rows], hs.cpu().numpy()[rows], codes_np(wq2, 8),
+                               ws2.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(y2)[rows], y2_ref), "down output")
+
+
+@pytest.mark.slow
+def test_backbone_mlp_block_fused_geglu_full_size():
+    """The benchmark's chain: X -> int4 -> gate|up W4A4 GEMM with the GeGLU
+    epilogue (weights interleaved in blocks of 32 rows) -> h bf16 -> fold,
+    Hadamard 128, int8 -> down W8A8 -> bf16; sampled rows stage by stage."""
+    wl = synth.CFG2
+    gu, dn = wl.projs
+    m, f = 816, dn.k
+    say("fused MLP block: generate")
+    x = synth.activation(wl, gu, m)
+    w_gu = synth.weight(wl, gu)
+    w_dn = synth.weight(wl, dn)
+    w_int = q.interleave_gate_up(w_gu[:f], w_gu[f:])
+    xd, wgd, wdd = x.to(DEV), w_int.to(DEV), w_dn.to(DEV)
+    say("fused MLP block: gpu path")
+    s1, inv1 = q.qlin_calibrate_fold(xd, wgd)
+    wq1, ws1 = q.qlin_quantize_weights(wgd, fold_s=s1, had_block=128, bits=4)
+    xq1, xs1 = q.qlin_rotate_quant_act(xd, fold_inv_s=inv1, had_block=128, bits=4)
+    h = q.qlin_gemm_w4a4_geglu(xq1, xs1, wq1, ws1, 2048, h_dtype=torch.bfloat16)
+    s2, inv2 = q.qlin_calibrate_fold(h, wdd)
+    wq2, ws2 = q.qlin_quantize_weights(wdd, fold_s=s2, had_block=128, bits=8)
+    hq, hs = q.qlin_rotate_quant_act(h, fold_inv_s=inv2, had_block=128, bits=8)
+    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, f, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    say("fused MLP block: oracle checks")
+    rows = _sample_rows(m, 6)
+    xq1n, wq1n = codes_np(xq1, 4), codes_np(wq1, 4)
+    _, _, h_ref = oracle.gemm_geglu(xq1n[rows], xs1.cpu().numpy()[rows], wq1n, ws1.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(h)[rows], h_ref), "h")
+    hf = f64(h)
+    s2g = s2.cpu().numpy()
+    assert_ok(oracle.compare_scales(s2g, oracle.calibrate_fold(hf, synth.to_f64(w_dn))), "fold down")
+    qh, sh, rh = oracle.rotate_quant_act(hf[rows], s2g, 128, 8)
+    assert_ok(oracle.compare_codes(codes_np(hq, 8)[rows], qh, rh), "h codes")
+    assert_ok(oracle.compare_scales(hs.cpu().numpy()[rows], sh), "h scales")
     _, _, y2_ref = oracle.gemm(codes_np(hq, 8)[rows], hs.cpu().numpy()[rows], codes_np(wq2, 8),
                                ws2.cpu().numpy(), "bf16")
     assert_ok(oracle.compare_outputs(f64(y2)[rows], y2_ref), "down output")

@@ -282,6 +282,52 @@ def test_gelu_matches_library_and_identities():
     np.testing.assert_allclose(oracle.geglu(x, 10)[0], oracle.gelu(g) * u, rtol=1e-15)
 
 
+# ---------------------------------------------------------------- fused gate|up + GeGLU
+
+
+def test_interleave_gate_up_order():
+    # hand-built order at block 2: gate rows 0,1 | up rows 0,1 | gate rows 2,3 | up rows 2,3
+    gate = np.array([[0], [1], [2], [3]])
+    up = np.array([[10], [11], [12], [13]])
+    got = oracle.interleave_gate_up(gate, up, block=2)[:, 0]
+    assert got.tolist() == [0, 1, 10, 11, 2, 3, 12, 13]
+    g2, u2 = oracle.split_gate_up(got[None, :], block=2)
+    assert g2[0].tolist() == [0, 1, 2, 3] and u2[0].tolist() == [10, 11, 12, 13]
+    with pytest.raises(ValueError):
+        oracle.interleave_gate_up(gate[:3], up[:3], block=2)
+
+
+def test_gemm_geglu_matches_torch_composition():
+    # against torch: int64 matmul, float64 scaling, torch bf16 casts and torch's erf GeLU
+    rng = np.random.default_rng(7)
+    m, f, k = 5, 64, 96
+    qx = rng.integers(-7, 8, size=(m, k))
+    qg = rng.integers(-7, 8, size=(f, k))
+    qu = rng.integers(-7, 8, size=(f, k))
+    sx = (rng.random(m) * 0.1 + 0.01).astype(np.float32)
+    sg = (rng.random(f) * 0.01 + 0.001).astype(np.float32)
+    su = (rng.random(f) * 0.01 + 0.001).astype(np.float32)
+    qw = oracle.interleave_gate_up(qg, qu)
+    sw = oracle.interleave_gate_up(sg[:, None], su[:, None])[:, 0]
+    acc, h32, h_ref = oracle.gemm_geglu(qx, sx, qw, sw, "bf16")
+
+    def deq(q, s):
+        a = torch.from_numpy(qx).to(torch.int64) @ torch.from_numpy(q).to(torch.int64).T
+        return (a.double() * torch.from_numpy(sx).double()[:, None] * torch.from_numpy(s).double()[None, :]).float()
+
+    g = deq(qg, sg).to(torch.bfloat16).double()
+    u = deq(qu, su).to(torch.bfloat16).double()
+    h = (torch.nn.functional.gelu(g, approximate="none") * u).float()
+    np.testing.assert_allclose(h32, h.numpy(), rtol=2.5e-7, atol=1e-30)
+    ref = h.to(torch.bfloat16).double().numpy()
+    # equal except where the float32 values straddle a bfloat16 rounding point
+    assert np.mean(h_ref != ref) < 0.01
+    np.testing.assert_allclose(h_ref, ref, rtol=2 ** -7)
+    # the accumulators are the plain integer products in the interleaved column order
+    g_acc, u_acc = oracle.split_gate_up(acc)
+    assert np.array_equal(g_acc, qx @ qg.T) and np.array_equal(u_acc, qx @ qu.T)
+
+
 # ---------------------------------------------------------------- compare rules
 
 
