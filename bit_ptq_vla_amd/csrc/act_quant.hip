@@ -760,8 +760,6 @@ __global__ void fold_finish_kernel(float* s, float* inv_s, int64_t k) {
 
 // ---- host launchers ----------------------------------------------------------
 
-namespace {
-
 // Compute units of the current device (cached per device).
 int device_cus() {
     static std::mutex mu;
@@ -776,6 +774,8 @@ int device_cus() {
     }
     return cus[dev];
 }
+
+namespace {
 
 template <int DT, int NCH, bool GEGLU, int TPB>
 hipError_t launch_rows_nch(const RowQuantParams& p, hipStream_t st) {

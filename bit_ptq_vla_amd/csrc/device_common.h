@@ -34,6 +34,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt_pk_bf16_f32
 }
 
+// Two floats rounded to bfloat16 (RNE) by one conversion: a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
     _Float16 h = static_cast<_Float16>(f);  // v_cvt_f16_f32, round to nearest even
     return __builtin_bit_cast(uint16_t, h);

@@ -82,22 +82,31 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, int dt, float v)
 }
 
 // LDS layout of one pipeline stage: row r of a tile holds 64 bytes as four
-// 16-byte chunks; chunk c is stored at chunk slot c ^ swz(r).  A 16-byte read
-// of chunk c by 8 (or 16) consecutive rows then touches distinct bank groups
-// whether the LDS serves 128 or 256 bytes per clock.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 16-byte chunks; chunk c is stored at chunk slot c ^ swz(r).  The MFMA
+// operand read (ds_read_b128: lane l reads chunk c (+1 for l >= 32) of row
+// l % 32) is free of bank conflicts with this choice of swz on gfx950, by
+// counter measurement (SQ_LDS_BANK_CONFLICT zero, against two-way conflicts
+// for ((r >> 1) ^ (r >> 3)) & 3 and four-way without a swizzle).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 // Waits until at most N of this wave's vector-memory operations (here: the
 // DMA loads into LDS) are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else static_assert(N == 0, "unsupported count");
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until at most `after` groups of L loads are outstanding, for a
+// runtime after <= A (compile-time counts: one s_waitcnt per branch).
+template <int L, int A>
+__device__ __forceinline__ void wait_groups(int after) {
+    if constexpr (A <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (after >= A) wait_vmcnt<A * L>();
+        else wait_groups<L, A - 1>(after);
+    }
 }
 
 // 16-byte load of every lane from rsrc + voff straight into LDS at
@@ -198,40 +207,53 @@ __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN /
                     rs_x, static_cast<int>((row0 + i * 32 + 8 * g4 + 4 * half) * 4), 0, 0));
 #pragma unroll
             for (int q = 0; q < TN / 2; ++q) {
-                // the 16 values of a lane: all table reads in flight together,
-                // one branch per group for values outside the table
-                uint32_t gb[16], idx[16];
-                float ub[16], gl[16];
-                bool all_in = true;
+                // The 16 values of a lane: g and u rounded to bfloat16 by one
+                // conversion (g low half, u high half), the table byte offset of
+                // |g| formed from that word, all table reads in flight together.
+                // toff = 4 * (|g| bits - first tabulated) keeps bits 13..16 clear
+                // exactly when the table covers |g| (a borrow or an overflow sets
+                // them); one branch per group for values outside the table.
+                uint32_t pk[16], toff[16];
+                uint32_t any = 0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sx = sxv[r >> 2][r & 3];
                     const float g = static_cast<float>(acc[i][2 * q][r]) * sx * swg[q];
                     const float u = static_cast<float>(acc[i][2 * q + 1][r]) * sx * swu[q];
-                    gb[r] = f32_to_bf16_rne(g);
-                    ub[r] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_rne(u)) << 16);
-                    idx[r] = (gb[r] & 0x7FFFu) - static_cast<uint32_t>(GTAB_EF0 << 7);
-                    all_in = all_in && idx[r] < static_cast<uint32_t>(GTAB_N);
+                    pk[r] = pk_bf16(g, u);
+                    toff[r] = (pk[r] << 2) - static_cast<uint32_t>(GTAB_EF0 << 9);
+                    any |= toff[r];
                 }
+                float gl[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float t = tab[idx[r] & (GTAB_N - 1)];
-                    gl[r] = (gb[r] & 0x8000u) ? -t : __uint_as_float(gb[r] << 16) - t;
+                    const float t = *reinterpret_cast<const float*>(reinterpret_cast<const int8_t*>(tab) +
+                                                                    (toff[r] & 0x1FFCu));
+                    gl[r] = fmaxf(__uint_as_float(pk[r] << 16), 0.f) - t;   // relu(g) - T(|g|)
                 }
-                if (!all_in) {
+                if (any & 0x1E000u) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (idx[r] >= static_cast<uint32_t>(GTAB_N)) gl[r] = gelu_outside_tab(gb[r]);
+                        if (toff[r] & 0x1E000u) gl[r] = gelu_outside_tab(pk[r] & 0xFFFFu);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rl = rr + 8 * (r >> 2) + 4 * half + (r & 3);
+                for (int r = 0; r < 16; r += 2) {
+                    const int rl = rr + 8 * (r >> 2) + 4 * half + (r & 3);   // rows rl, rl + 1
                     if (RP < 32 && rl >= RP) continue;
-                    const float h = gl[r] * ub[r];
+                    const float h0 = gl[r] * __uint_as_float(pk[r] & 0xFFFF0000u);
+                    const float h1 = gl[r + 1] * __uint_as_float(pk[r + 1] & 0xFFFF0000u);
                     int8_t* at = region + rl * PITCH + (q * 32 + l32) * E;
-                    if constexpr (ODT == BF16) *reinterpret_cast<uint16_t*>(at) = f32_to_bf16_rne(h);
-                    else if constexpr (ODT == F16) *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(h);
-                    else *reinterpret_cast<float*>(at) = h;
+                    if constexpr (ODT == BF16) {
+                        const uint32_t hp = pk_bf16(h0, h1);
+                        *reinterpret_cast<uint16_t*>(at) = static_cast<uint16_t>(hp);
+                        *reinterpret_cast<uint16_t*>(at + PITCH) = static_cast<uint16_t>(hp >> 16);
+                    } else if constexpr (ODT == F16) {
+                        *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(h0);
+                        *reinterpret_cast<uint16_t*>(at + PITCH) = f32_to_f16_bits(h1);
+                    } else {
+                        *reinterpret_cast<float*>(at) = h0;
+                        *reinterpret_cast<float*>(at + PITCH) = h1;
+                    }
                 }
             }
         }
@@ -327,18 +349,29 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 16; r += 2) {
+                    // rows rl and rl + 1 of this lane's column
                     const int rl = ti * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     int8_t* at = region + rl * PITCH + (j * 32 + l32) * E;
-                    int32_t a = acc[i][j][r];
+                    int32_t a0 = acc[i][j][r], a1 = acc[i][j][r + 1];
                     if constexpr (FLOAT_OUT) {
-                        const float v = static_cast<float>(a) * sxv[r >> 2][r & 3] * swv[j];
-                        if constexpr (OUT == BF16) *reinterpret_cast<uint16_t*>(at) = f32_to_bf16_rne(v);
-                        else if constexpr (OUT == F16) *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(v);
-                        else *reinterpret_cast<float*>(at) = v;
+                        const float v0 = static_cast<float>(a0) * sxv[r >> 2][r & 3] * swv[j];
+                        const float v1 = static_cast<float>(a1) * sxv[r >> 2][(r & 3) + 1] * swv[j];
+                        if constexpr (OUT == BF16) {
+                            const uint32_t vp = pk_bf16(v0, v1);
+                            *reinterpret_cast<uint16_t*>(at) = static_cast<uint16_t>(vp);
+                            *reinterpret_cast<uint16_t*>(at + PITCH) = static_cast<uint16_t>(vp >> 16);
+                        } else if constexpr (OUT == F16) {
+                            *reinterpret_cast<uint16_t*>(at) = f32_to_f16_bits(v0);
+                            *reinterpret_cast<uint16_t*>(at + PITCH) = f32_to_f16_bits(v1);
+                        } else {
+                            *reinterpret_cast<float*>(at) = v0;
+                            *reinterpret_cast<float*>(at + PITCH) = v1;
+                        }
                     } else {
-                        if constexpr (INT4) a >>= 8;
-                        *reinterpret_cast<int32_t*>(at) = a;
+                        if constexpr (INT4) { a0 >>= 8; a1 >>= 8; }
+                        *reinterpret_cast<int32_t*>(at) = a0;
+                        *reinterpret_cast<int32_t*>(at + PITCH) = a1;
                     }
                 }
             }
@@ -387,9 +420,12 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     constexpr int STAGE = (BM + BN) * STAGE_BYTES;
     // The DMA is issued through inline assembly, invisible to the compiler,
     // so one array serves the whole ring (and the epilogue staging after it).
-    // The fused GeGLU epilogue keeps its GeLU table after the ring from the start.
+    // The fused GeGLU epilogue keeps its GeLU table at LDS offset 0 (table reads
+    // then take no base address) from the start; the ring follows it.
     constexpr bool GEGLU = OUT >= OUT_GEGLU;
-    __shared__ __attribute__((aligned(1024))) int8_t lds[NS * STAGE + (GEGLU ? GTAB_BYTES : 0)];
+    constexpr int RING0 = GEGLU ? GTAB_BYTES : 0;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING0 + NS * STAGE];
+    int8_t* const ring = lds + RING0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -501,7 +537,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     if constexpr (GEGLU) {
         static_assert(GTAB_BYTES == 2 * 4 * 1024, "two 16-byte loads per lane");
         const v4i rsrc_t = make_rsrc(reinterpret_cast<const int8_t*>(g_gelu_neg_tab), GTAB_BYTES);
-        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds + NS * STAGE)) + wave_u * 1024;
+        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave_u * 1024;
 #pragma unroll
         for (int i = 0; i < 2; ++i) dma16(rsrc_t, (i * 4 + wave) * 1024 + lane * 16, t_dst + i * 4096);
     }
@@ -511,18 +547,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
         const int pro = nst < NS ? nst : NS;
 #pragma unroll
         for (int pst = 0; pst < NS; ++pst)
-            if (pst < pro) issue(pst, lds + pst * STAGE);
+            if (pst < pro) issue(pst, ring + pst * STAGE);
         // stage 0 has landed once at most pro - 1 stages are outstanding
-        if (pro == NS) wait_vmcnt<(NS - 1) * LOADS>();
-        else if (pro >= 3) wait_vmcnt<2 * LOADS>();
-        else if (pro == 2) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
+        wait_groups<LOADS, NS - 1>(pro - 1);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
     Unit cur;
     v4i op_a[TM], op_b[TN];   // int4: unpacked k-slice 0 of `cur`
-    read_unit(lds, 0, cur);
+    read_unit(ring, 0, cur);
     if constexpr (INT4) unpack(cur, 0, op_a, op_b);
 
     // One stage: its units in turn.  Before the last unit's MFMAs the next
@@ -541,9 +574,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
                     // stage it+1 has landed once at most min(NS-2, nst-2-it) later stages are outstanding
                     const int after = (nst - 2 - it) < (NS - 2) ? (nst - 2 - it) : (NS - 2);
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    if (after >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * LOADS>();
-                    else if (after == 1) wait_vmcnt<LOADS>();
-                    else wait_vmcnt<0>();
+                    wait_groups<LOADS, NS - 2>(after);
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                     if (it + NS < nst) issue(it + NS, buf);
@@ -583,11 +614,11 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     const int nfull = nst - nst % NS;
     for (int it0 = 0; it0 < nfull; it0 += NS) {
 #pragma unroll
-        for (int u = 0; u < NS; ++u) stage_step(it0 + u, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
+        for (int u = 0; u < NS; ++u) stage_step(it0 + u, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
     }
     for (int it = nfull; it < nst; ++it) {
         const int u = it - nfull;
-        stage_step(it, lds + u * STAGE, lds + ((u + 1) % NS) * STAGE);
+        stage_step(it, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
     }
 
     // ---- epilogue: every wave is done with the ring; each takes one buffer
@@ -595,13 +626,13 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     if constexpr (GEGLU) {
         constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
         store_tile_geglu<BM, BN, INT4, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),
-                                                                lane, reinterpret_cast<const float*>(lds + NS * STAGE),
-                                                                lds + wave * REGION);
+                                                                lane, reinterpret_cast<const float*>(lds),
+                                                                ring + wave * REGION);
     } else {
         void* dst = (OUT == -1) ? static_cast<void*>(p.ws + static_cast<int64_t>(split) * p.m * p.n) : p.y;
         constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
         store_tile_lds<BM, BN, INT4, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
-                                                  lds + wave * REGION, dst);
+                                                  ring + wave * REGION, dst);
     }
 }
 
@@ -686,20 +717,25 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4) {
     // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes
     // per MFMA), two blocks per CU (one block's per-stage barrier and LDS
     // latency is covered by the other block's MFMAs).
+    // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per CU.)
     GemmPlan g;
     g.bm = 128;
-    g.bn = (n >= 4096) ? 256 : 128;
+    g.bn = (n >= 4096 && int4) ? 256 : 128;
     const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
     const int64_t kbytes = int4 ? k / 2 : k;
     const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
-    constexpr int64_t kSlots = 512;  // 256 CUs x 2 resident blocks
+    const int64_t cus = device_cus();
+    const int64_t slots = 2 * cus;   // two resident blocks per CU
     int splits = 1;
     // split K only when the tile grid fills under half of the block slots,
     // keeping at least 16 stages (1 KiB of k per row) in every split
-    if (tiles * 2 <= kSlots) {
-        while (tiles * splits * 2 <= kSlots && stages / (splits * 2) >= 16) splits *= 2;
+    if (tiles * 2 <= slots) {
+        while (tiles * splits * 2 <= slots && stages / (splits * 2) >= 16) splits *= 2;
     }
     g.splits = splits;
+    // A grid of at most one block per CU gets the whole LDS for a deeper ring:
+    // with one wave per SIMD nothing else covers the DMA latency.
+    g.deep = tiles * splits <= cus;
     g.ws_bytes = (splits > 1) ? static_cast<int64_t>(splits) * m * n * 4 : 0;
     return g;
 }
@@ -720,8 +756,14 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
     p.y_dtype = y_dtype;
     hipError_t e;
-    if (plan.bn == 256) e = int4 ? launch_out<128, 256, 2, 3, true>(p, st) : launch_out<128, 256, 2, 3, false>(p, st);
-    else e = int4 ? launch_out<128, 128, 2, 4, true>(p, st) : launch_out<128, 128, 2, 4, false>(p, st);
+    if (plan.bn == 256) {
+        if (!int4) return hipErrorInvalidValue;
+        e = plan.deep ? launch_out<128, 256, 1, 6, true>(p, st) : launch_out<128, 256, 2, 3, true>(p, st);
+    } else if (plan.deep) {
+        e = int4 ? launch_out<128, 128, 1, 8, true>(p, st) : launch_out<128, 128, 1, 8, false>(p, st);
+    } else {
+        e = int4 ? launch_out<128, 128, 2, 4, true>(p, st) : launch_out<128, 128, 2, 4, false>(p, st);
+    }
     if (e != hipSuccess) return e;
     if (plan.splits > 1) {
         const int64_t total = m * n;
@@ -753,8 +795,9 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
     p.tiles_m = static_cast<int>((m + plan.bm - 1) / plan.bm);
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
     p.y_dtype = y_dtype;
-    if (plan.bn == 256) return launch_geglu_out<128, 256, 2, 3, true>(p, st);
-    return launch_geglu_out<128, 128, 2, 4, true>(p, st);
+    if (plan.bn == 256)
+        return plan.deep ? launch_geglu_out<128, 256, 1, 6, true>(p, st) : launch_geglu_out<128, 256, 2, 3, true>(p, st);
+    return plan.deep ? launch_geglu_out<128, 128, 1, 8, true>(p, st) : launch_geglu_out<128, 128, 2, 4, true>(p, st);
 }
 
 }  // namespace qlin

@@ -6,6 +6,9 @@
 
 namespace qlin {
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus();
+
 int row_quant_lanes(int64_t k);
 int row_quant_chunks(int64_t k, int g);
 
@@ -25,6 +28,7 @@ hipError_t launch_calibrate_fold(const void* x, int x_dtype, int64_t m, int64_t 
 struct GemmPlan {
     int bm, bn;     // block tile
     int splits;     // split-K factor (1 = fused epilogue)
+    bool deep;      // grid fits one block per CU: one block per CU with a deeper DMA ring
     int64_t ws_bytes;
 };
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4);

@@ -169,6 +169,46 @@ def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
 
+# Grids above one block per CU (256 CUs): the launch with two resident blocks
+# per CU and the shorter DMA ring; the smaller shapes above take the one-block
+# deep-ring launch.  Sampled rows (first, last, random) against the oracle.
+BIG_GRID_SHAPES = [
+    ("w8a8", 1100, 3968, 256),    # 9 x 31 tiles of 128 x 128
+    ("w4a4", 1100, 3968, 256),    # 9 x 31 tiles of 128 x 128
+    ("w4a4", 2100, 4096, 256),    # 17 x 16 tiles of 128 x 256
+]
+
+
+@pytest.mark.parametrize("scheme,m,n,k", BIG_GRID_SHAPES)
+def test_gemm_big_grid_sampled_rows(scheme, m, n, k):
+    say(f"gemm i32 big grid {scheme} {m}x{n}x{k}")
+    bits = 4 if scheme == "w4a4" else 8
+    a = synth.random_codes(SEED, f"Abig/{m}/{k}/{bits}", m, k, bits)
+    b = synth.random_codes(SEED, f"Bbig/{n}/{k}/{bits}", n, k, bits)
+    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
+    acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rows = _sample_rows(m, 24)
+    ref = oracle.int_gemm(codes_np(a, bits)[rows], codes_np(b, bits))
+    got = acc.cpu().numpy().astype(np.int64)[rows]
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
+
+
+@pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256)])
+def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
+    say(f"gemm geglu big grid {m}x{f}x{k}")
+    n2 = 2 * f
+    a = synth.random_codes(SEED, f"Agbig/{m}/{k}", m, k, 4)
+    b = synth.random_codes(SEED, f"Bgbig/{n2}/{k}", n2, k, 4)
+    sx = synth.random_scales(SEED, f"sxgbig/{m}", m)
+    sw = synth.random_scales(SEED, f"swgbig/{n2}", n2)
+    h = q.qlin_gemm_w4a4_geglu(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, h_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(m, 24)
+    _, _, h_ref = oracle.gemm_geglu(codes_np(a, 4)[rows], sx.numpy()[rows], codes_np(b, 4), sw.numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(h)[rows], h_ref), "h")
+
+
 @pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scheme,m,n,k", [("w4a4", 300, 520, 1024), ("w8a8", 129, 384, 4096),
                                           ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512)])
