@@ -5,12 +5,18 @@ A step is one pass of the whole hot path over one batch: the backbone-shaped
 MLP block at M = 816 tokens (hidden 2048, gate|up 2 x 16384, down 2048):
 
   rotate+quantize X (bf16, fold, Hadamard 128, int4)
-  -> gate|up W4A4 GEMM (816 x 32768 x 2048) -> bf16
-  -> GeGLU + fold + Hadamard 128 + int8 quantize (816 x 16384)
+  -> gate|up W4A4 GEMM (816 x 32768 x 2048) with GeGLU in its epilogue
+     (gate/up weight rows interleaved in blocks of 32) -> h bf16 [816][16384]
+  -> fold + Hadamard 128 + int8 quantize of h
   -> down W8A8 GEMM (816 x 2048 x 16384) -> bf16
 
+(--unfused: the gate|up GEMM writes both halves and the int8 quantizer
+applies GeGLU on the way in.)
+
 Weights are quantized once before timing (offline).  Inputs are synthetic,
-seeded, resident in HBM before the timed region.  value = integer GEMM ops of
+seeded, resident in HBM before the timed region.  Before the W warm-up steps
+the step runs untimed for 0.5 s so that the GPU clocks settle; the timed
+region is bracketed by HIP events created without a system-scope fence.  value = integer GEMM ops of
 the step (2*M*N*K summed) / step time, in TOPS.  Also reported: the
 batch-1 W4A16 GEMV of a 7B-decoder layer (hidden 4096, MLP 11008) in GB/s
 with distinct weight copies rotated to defeat the 256 MB Infinity Cache, the
@@ -34,7 +40,8 @@ if ROOT not in sys.path:
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 # FETCH_SIZE / WRITE_SIZE summary of the step's kernels and the gate|up GEMM's name in it
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_mlp_block_m816.txt")
-GATE_UP_KERNEL = "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,1>"
+GATE_UP_KERNEL = {True: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,17>",
+                  False: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,1>"}
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
@@ -50,6 +57,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=256, help="token rows of the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="GeGLU in the int8 quantizer, not the GEMM epilogue")
     return ap.parse_args()
 
 
@@ -57,17 +65,58 @@ from bit_ptq_vla_amd.profile_step import read_traffic  # noqa: E402
 from bit_ptq_vla_amd.workload import MlpBlock  # noqa: E402
 
 
-def time_block(block, steps, warmup):
-    """Step time over `steps` steps (events on the launch stream) and the mean
-    duration of the gate|up GEMM launch inside them."""
+class HipEvent:
+    """A HIP event on the launch stream, created with hipEventDisableSystemFence:
+    recording it adds no system-scope cache flush between the kernels it
+    brackets (a default event's flush slows the next kernel measurably)."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream):
+        import ctypes
+
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        self.stream = ctypes.c_void_p(stream)
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        if HipEvent._hip.hipEventRecord(self.ev, self.stream):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end) -> float:
+        ms = self._ct.c_float()
+        if HipEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
+def time_block(block, steps, warmup, settle_s=0.5):
+    """Step time over `steps` steps (HIP events on the launch stream) and the
+    mean duration of the gate|up GEMM launch inside them.  Before the warm-up
+    steps the GPU runs the step for settle_s seconds so that its clocks reach
+    their loaded state (the first milliseconds of a burst run slower)."""
     import torch
 
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            block.step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         block.step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [(HipEvent(stream), HipEvent(stream)) for _ in range(steps)]
+    t0, t1 = HipEvent(stream), HipEvent(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
@@ -76,8 +125,8 @@ def time_block(block, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / steps
-    gemm1_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    ms_step = t0.elapsed_ms(t1) / steps
+    gemm1_ms = sum(a.elapsed_ms(b) for a, b in evs) / steps
     return ms_step, gemm1_ms, wall
 
 
@@ -152,13 +201,21 @@ def cpu_baseline(block, rows):
     with threadpool_limits(limits=1):
         s1 = block.s1.cpu().numpy()
         s2 = block.s2.cpu().numpy()
-        qw1, sw1, _ = oracle.quantize_weights(synth.to_f64(block.wgu_cpu), s1, 128, 4)
+        wgu = synth.to_f64(block.wgu_cpu)
+        f = block.dn.k
+        if block.fused:
+            wgu = oracle.interleave_gate_up(wgu[:f], wgu[f:])
+        qw1, sw1, _ = oracle.quantize_weights(wgu, s1, 128, 4)
         qw2, sw2, _ = oracle.quantize_weights(synth.to_f64(block.wdn_cpu), s2, 128, 8)
         x = synth.to_f64(block.x_cpu[:rows])
         t0 = time.perf_counter()
         qx, sx, _ = oracle.rotate_quant_act(x, s1, 128, 4)
-        _, y32, y1 = oracle.gemm(qx, sx, qw1, sw1, "bf16")
-        qh, sh, _ = oracle.rotate_quant_act(y1, s2, 128, 8, preop="geglu")
+        if block.fused:
+            _, _, h = oracle.gemm_geglu(qx, sx, qw1, sw1, "bf16")
+            qh, sh, _ = oracle.rotate_quant_act(h, s2, 128, 8)
+        else:
+            _, _, y1 = oracle.gemm(qx, sx, qw1, sw1, "bf16")
+            qh, sh, _ = oracle.rotate_quant_act(y1, s2, 128, 8, preop="geglu")
         oracle.gemm(qh, sh, qw2, sw2, "bf16")
         dt = time.perf_counter() - t0
     ops = 2 * rows * (block.gu.n * block.gu.k + block.dn.n * block.dn.k)
@@ -178,7 +235,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("bench: preparing the MLP block (weights quantized offline)")
-    block = MlpBlock(dev)
+    block = MlpBlock(dev, fused=not args.unfused)
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
     ms_step, gemm1_ms, wall = time_block(block, args.steps, args.warmup)
@@ -199,11 +256,13 @@ def main():
         "data": "synthetic (seeded normals, 1% outlier channels x30; random-init weights N(0, 0.02))",
         "config": {"workload": "backbone_mlp_m816_h2048_f16384", "m": block.m, "hidden": 2048,
                    "ffn": 16384, "gate_up": "w4a4", "down": "w8a8", "hadamard_block": 128,
+                   "geglu": "gate_up GEMM epilogue" if block.fused else "int8 quantizer pre-op",
                    "out_dtype": "bf16", "step_gop": round(block.ops / 1e9, 2)},
-        "roofline": {"kernel": "gate_up W4A4 GEMM 816x32768x2048", "bound": "mfma",
+        "roofline": {"kernel": "gate_up W4A4 GEMM 816x32768x2048" + (" + GeGLU epilogue" if block.fused else ""),
+                     "bound": "mfma",
                      "achieved": round(gemm1_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(gemm1_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": read_traffic(TRAFFIC_SUMMARY, GATE_UP_KERNEL),
+                     "traffic": read_traffic(TRAFFIC_SUMMARY, GATE_UP_KERNEL[block.fused]),
                      "traffic_algorithmic": block.gemm1_bytes,
                      "us_per_launch": round(gemm1_ms * 1e3, 3)},
         "frac_of_int8_peak_step": round(tops / INT8_PEAK_TOPS, 4),

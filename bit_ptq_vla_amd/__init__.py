@@ -102,6 +102,18 @@ def _dev_tensor(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _need(t, nbytes: int, name: str) -> None:
+    """A buffer handed to the library: a contiguous device tensor of at least
+    nbytes (the library sees only its pointer)."""
+    if t is None:
+        return
+    _dev_tensor(t, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
+
+
 # --------------------------------------------------------------------------
 # entry points
 # --------------------------------------------------------------------------
@@ -151,12 +163,16 @@ def qlin_rotate_quant_act(x: torch.Tensor, k: Optional[int] = None, fold_inv_s: 
     m = x.shape[0]
     if k is None:
         k = x.shape[1] // 2 if pre == QLIN_PRE_GEGLU else x.shape[1]
+    if x.dim() != 2 or x.stride(1) != 1 or (2 * k if pre == QLIN_PRE_GEGLU else k) > x.shape[1]:
+        raise ValueError("x must be a row-major [m][>= k] tensor ([m][>= 2k] with the GeGLU pre-op)")
     if out is None:
         xq = torch.empty((m, k // 2) if bits == 4 else (m, k), dtype=torch.uint8 if bits == 4 else torch.int8,
                          device=x.device)
         xs = torch.empty(m, dtype=torch.float32, device=x.device)
     else:
         xq, xs = out
+    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    _need(xs, m * 4, "x_scale")
     st = lib.qlin_rotate_quant_act(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0), pre,
                                    _ptr(fold_inv_s), had_block, bits, xq.data_ptr(), xs.data_ptr(),
                                    _stream(x.device))
@@ -168,7 +184,13 @@ def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):
     lib = load()
     _dev_tensor(wq, "wq")
     m, n = xq.shape[0], wq.shape[0]
+    kb = k // 2 if fn_name == "qlin_gemm_w4a4" else k
+    _need(xq, m * kb, "xq")
+    _need(wq, n * kb, "wq")
+    _need(x_scale, m * 4, "x_scale")
+    _need(w_scale, n * 4, "w_scale")
     y = out if out is not None else torch.empty((m, n), dtype=y_dtype, device=wq.device)
+    _need(y, m * n * y.element_size(), "y")
     st = getattr(lib, fn_name)(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
                                y.data_ptr(), _TORCH_TO_QLIN[y.dtype], _stream(wq.device))
     _check(st, fn_name)
@@ -191,7 +213,12 @@ def qlin_gemm_w4a4_geglu(xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat1
     lib = load()
     _dev_tensor(wq, "wq")
     m, n2 = xq.shape[0], wq.shape[0]
+    _need(xq, m * (k // 2), "xq")
+    _need(wq, n2 * (k // 2), "wq")
+    _need(x_scale, m * 4, "x_scale")
+    _need(w_scale, n2 * 4, "w_scale")
     h = out if out is not None else torch.empty((m, n2 // 2), dtype=h_dtype, device=wq.device)
+    _need(h, m * (n2 // 2) * h.element_size(), "h")
     st = lib.qlin_gemm_w4a4_geglu(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n2, k,
                                   h.data_ptr(), _TORCH_TO_QLIN[h.dtype], _stream(wq.device))
     _check(st, "qlin_gemm_w4a4_geglu")
@@ -217,7 +244,11 @@ def qlin_gemv_w4a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, gr
     _dev_tensor(x, "x")
     m, k = x.shape
     n = wq.shape[0]
+    _need(x, m * k * 2, "x")
+    _need(wq, n * (k // 2), "wq")
+    _need(w_scale, n * (k // group) * 2 if group > 0 else 0, "w_scale")
     y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _need(y, m * n * 2, "y")
     st = lib.qlin_gemv_w4a16(x.data_ptr(), wq.data_ptr(), w_scale.data_ptr(), m, n, k, group, y.data_ptr(),
                              _stream(x.device))
     _check(st, "qlin_gemv_w4a16")

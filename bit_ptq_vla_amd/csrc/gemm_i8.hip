@@ -664,6 +664,52 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* ws, i
     }
 }
 
+// The same for n % 8 == 0: eight consecutive outputs per lane, 32-byte
+// partial reads, one 16-byte (or two) output store.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce8_kernel(const int32_t* ws, int splits, int64_t m,
+                                                             int64_t n, const float* sx,
+                                                             const float* sw, void* y) {
+    const int64_t total = m * n;
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+    if (i0 >= total) return;
+    v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+    for (int s = 0; s < splits; ++s) {
+        const v4i* src = reinterpret_cast<const v4i*>(ws + static_cast<int64_t>(s) * total + i0);
+        a0 += __builtin_nontemporal_load(src);
+        a1 += __builtin_nontemporal_load(src + 1);
+    }
+    const int32_t a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    if constexpr (DT == I32) {
+        reinterpret_cast<v4i*>(y)[i0 / 4] = a0;
+        reinterpret_cast<v4i*>(y)[i0 / 4 + 1] = a1;
+    } else {
+        const int64_t row = i0 / n, col = i0 - row * n;
+        const float sxr = sx[row];
+        const f4 w0 = *reinterpret_cast<const f4*>(sw + col);
+        const f4 w1 = *reinterpret_cast<const f4*>(sw + col + 4);
+        const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(a[e]) * sxr * wv[e];
+        if constexpr (DT == BF16) {
+            const v4i o = {static_cast<int>(pk_bf16(v[0], v[1])), static_cast<int>(pk_bf16(v[2], v[3])),
+                           static_cast<int>(pk_bf16(v[4], v[5])), static_cast<int>(pk_bf16(v[6], v[7]))};
+            reinterpret_cast<v4i*>(y)[i0 / 8] = o;
+        } else if constexpr (DT == F16) {
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = f32_to_f16_bits(v[2 * e]) | (static_cast<uint32_t>(f32_to_f16_bits(v[2 * e + 1])) << 16);
+            reinterpret_cast<v4i*>(y)[i0 / 8] = v4i{static_cast<int>(o[0]), static_cast<int>(o[1]),
+                                                    static_cast<int>(o[2]), static_cast<int>(o[3])};
+        } else {
+            reinterpret_cast<f4*>(y)[i0 / 4] = f4{v[0], v[1], v[2], v[3]};
+            reinterpret_cast<f4*>(y)[i0 / 4 + 1] = f4{v[4], v[5], v[6], v[7]};
+        }
+    }
+}
+
 template <int BM, int BN, int MINB, int NS, bool INT4, int OUT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t st) {
     dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n * p.splits));
@@ -767,10 +813,22 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     if (e != hipSuccess) return e;
     if (plan.splits > 1) {
         const int64_t total = m * n;
-        const int64_t per = (n % 4 == 0) ? 4 : 1;
-        dim3 grid(static_cast<unsigned>((total / per + 255) / 256));
-        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, ws, plan.splits, m, n,
-                           x_scale, w_scale, y, y_dtype);
+        const bool v8 = n % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                        (reinterpret_cast<uintptr_t>(w_scale) & 15) == 0;
+        if (v8) {
+            dim3 grid(static_cast<unsigned>((total / 8 + 255) / 256));
+            switch (y_dtype) {
+                case BF16: hipLaunchKernelGGL(splitk_reduce8_kernel<BF16>, grid, dim3(256), 0, st, ws, plan.splits, m, n, x_scale, w_scale, y); break;
+                case F16: hipLaunchKernelGGL(splitk_reduce8_kernel<F16>, grid, dim3(256), 0, st, ws, plan.splits, m, n, x_scale, w_scale, y); break;
+                case F32: hipLaunchKernelGGL(splitk_reduce8_kernel<F32>, grid, dim3(256), 0, st, ws, plan.splits, m, n, x_scale, w_scale, y); break;
+                default: hipLaunchKernelGGL(splitk_reduce8_kernel<I32>, grid, dim3(256), 0, st, ws, plan.splits, m, n, x_scale, w_scale, y); break;
+            }
+        } else {
+            const int64_t per = (n % 4 == 0) ? 4 : 1;
+            dim3 grid(static_cast<unsigned>((total / per + 255) / 256));
+            hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, ws, plan.splits, m, n,
+                               x_scale, w_scale, y, y_dtype);
+        }
         e = hipGetLastError();
     }
     return e;

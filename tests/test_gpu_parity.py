@@ -149,6 +149,8 @@ GEMM_SHAPES = [
     (1, 96, 128),        # one token
     (257, 256, 2048),
     (33, 64, 192),       # k % 128 == 64: w8a8 only (w4a4 needs k % 128 == 0)
+    (40, 100, 4096),     # split-K, n % 8 == 4: four outputs per reduce lane
+    (17, 99, 2048),      # split-K, odd n: one output per reduce lane
 ]
 
 
@@ -211,7 +213,8 @@ def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
 
 @pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scheme,m,n,k", [("w4a4", 300, 520, 1024), ("w8a8", 129, 384, 4096),
-                                          ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512)])
+                                          ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512),
+                                          ("w8a8", 40, 100, 4096), ("w4a4", 17, 99, 2048)])
 def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     say(f"gemm {out} {scheme} {m}x{n}x{k}")
     bits = 4 if scheme == "w4a4" else 8
