@@ -35,6 +35,7 @@
 // order (integer addition: bit-exact) and applies the epilogue.
 
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "qlin_internal.h"
@@ -553,22 +554,30 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     }
+    // A wave whose rows all lie past m (the lower half of a ragged last M tile)
+    // still takes part in the DMA and the barriers, but reads no fragments and
+    // issues no MFMA: its SIMD's MFMA time goes to the co-resident block.
+    const bool wave_active = m0 + wm * (BM / 2) < p.m;
+
     Unit cur;
     v4i op_a[TM], op_b[TN];   // int4: unpacked k-slice 0 of `cur`
-    read_unit(ring, 0, cur);
-    if constexpr (INT4) unpack(cur, 0, op_a, op_b);
+    if (wave_active) {
+        read_unit(ring, 0, cur);
+        if constexpr (INT4) unpack(cur, 0, op_a, op_b);
+    }
 
     // One stage: its units in turn.  Before the last unit's MFMAs the next
     // stage is published (this wave's DMA for it landed + barrier, after every
     // read of this stage's buffer has completed), the buffer of this stage
     // takes the DMA of stage it + NS, and the next stage's first unit is read.
-    auto stage_step = [&](int it, int8_t* buf, int8_t* nbuf) {
+    auto stage_step = [&](auto mf, int it, int8_t* buf, int8_t* nbuf) {
+        constexpr bool MF = decltype(mf)::value;   // this wave computes
 #pragma unroll
         for (int ks = 0; ks < UPS; ++ks) {
             const bool last = ks == UPS - 1;
             Unit nxt;
             if (!last) {
-                read_unit(buf, ks + 1, nxt);
+                if constexpr (MF) read_unit(buf, ks + 1, nxt);
             } else {
                 if (it + 1 < nst) {
                     // stage it+1 has landed once at most min(NS-2, nst-2-it) later stages are outstanding
@@ -580,9 +589,11 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
                     if (it + NS < nst) issue(it + NS, buf);
                 }
                 // after the final stage this reads stale LDS that nothing uses
-                read_unit(nbuf, 0, nxt);
+                if constexpr (MF) read_unit(nbuf, 0, nxt);
             }
-            if constexpr (INT4) {
+            if constexpr (!MF) {
+                // no fragments, no MFMA
+            } else if constexpr (INT4) {
                 v4i o1a[TM], o1b[TN];
                 unpack(cur, 1, o1a, o1b);
                 mfma_slice(op_a, op_b);
@@ -606,23 +617,28 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);
             }
-            cur = nxt;
+            if constexpr (MF) cur = nxt;
         }
     };
 
     // Whole groups of NS stages: the ring positions are compile-time constants.
-    const int nfull = nst - nst % NS;
-    for (int it0 = 0; it0 < nfull; it0 += NS) {
+    auto main_loop = [&](auto mf) {
+        const int nfull = nst - nst % NS;
+        for (int it0 = 0; it0 < nfull; it0 += NS) {
 #pragma unroll
-        for (int u = 0; u < NS; ++u) stage_step(it0 + u, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
-    }
-    for (int it = nfull; it < nst; ++it) {
-        const int u = it - nfull;
-        stage_step(it, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
-    }
+            for (int u = 0; u < NS; ++u) stage_step(mf, it0 + u, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
+        }
+        for (int it = nfull; it < nst; ++it) {
+            const int u = it - nfull;
+            stage_step(mf, it, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
+        }
+    };
+    if (wave_active) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
 
     // ---- epilogue: every wave is done with the ring; each takes one buffer
     __syncthreads();
+    if (!wave_active) return;   // no output rows (no block-wide barrier follows)
     if constexpr (GEGLU) {
         constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
         store_tile_geglu<BM, BN, INT4, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),

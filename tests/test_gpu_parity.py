@@ -57,6 +57,8 @@ ACT_CASES = [
     (33, 4096, 256, 8, "f16", True),
     (2, 128, 2, 4, "bf16", False),
     (300, 256, 128, 4, "bf16", True),   # several rows per block
+    (3, 14336, 128, 8, "bf16", True),   # 512 lanes, chunk count 4 (not a power-of-two row)
+    (4, 32768, 128, 4, "bf16", True),   # longest rows: 1024 lanes, 4 chunks
 ]
 
 
