@@ -20,6 +20,7 @@ region is bracketed by HIP events created without a system-scope fence.  value =
 the step (2*M*N*K summed) / step time, in TOPS.  Also reported: the
 batch-1 W4A16 GEMV of a 7B-decoder layer (hidden 4096, MLP 11008) in GB/s
 with distinct weight copies rotated to defeat the 256 MB Infinity Cache, the
+W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape, the
 dominant kernel's roofline fraction, and the CPU oracle on a row sample.
 
 Prints ONE JSON line.
@@ -40,8 +41,8 @@ if ROOT not in sys.path:
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 # FETCH_SIZE / WRITE_SIZE summary of the step's kernels and the gate|up GEMM's name in it
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_mlp_block_m816.txt")
-GATE_UP_KERNEL = {True: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,17>",
-                  False: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,1>"}
+GATE_UP_KERNEL = {True: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,17,false>",
+                  False: "voidqlin::(anonymousnamespace)::gemm_i8_kernel<128,256,2,3,true,1,false>"}
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 
 
@@ -188,6 +189,35 @@ def gemv_leg(dev, reps=5):
             "shapes": shapes}
 
 
+def w4a8_leg(block, steps):
+    """The W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape
+    816 x 32768 x 2048: X rotated and quantized to int8 with the block's fold,
+    the block's int4 gate|up weights; mean launch time over `steps` launches
+    between fence-free HIP events."""
+    import torch
+
+    import bit_ptq_vla_amd as q
+
+    m, k, n = block.m, block.gu.k, block.gu.n
+    xq8, xs8 = q.qlin_rotate_quant_act(block.x, fold_inv_s=block.inv1, had_block=128, bits=8)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=block.x.device)
+    for _ in range(5):
+        q.qlin_gemm_w4a8(xq8, xs8, block.wq1, block.ws1, k, out=y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = HipEvent(stream), HipEvent(stream)
+    e0.record()
+    for _ in range(steps):
+        q.qlin_gemm_w4a8(xq8, xs8, block.wq1, block.ws1, k, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_ms(e1) * 1e3 / steps
+    tops = 2 * m * n * k / (us * 1e-6) / 1e12
+    return {"shape": f"{m}x{n}x{k}", "us_per_launch": round(us, 3), "TOPS": round(tops, 2),
+            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "bound": "mfma",
+            "note": "back-to-back launches of the GEMM alone (bf16 out)"}
+
+
 def cpu_baseline(block, rows):
     """The oracle as it stands on a row sample of the same step (single
     thread: NumPy's int64 matmul does not use BLAS; BLAS is pinned to one
@@ -268,6 +298,8 @@ def main():
         "frac_of_int8_peak_step": round(tops / INT8_PEAK_TOPS, 4),
         "wall_s_timed": round(wall, 3),
     }
+    log("bench: W4A8 GEMM leg")
+    out["w4a8"] = w4a8_leg(block, args.steps)
     if not args.no_gemv:
         log("bench: batch-1 W4A16 GEMV leg")
         out["gemv"] = gemv_leg(dev)

@@ -47,6 +47,7 @@ SIGNATURES = {
     "qlin_rotate_quant_act": [_P, _I32, _I64, _I64, _I64, _I32, _P, _I32, _I32, _P, _P, _P],
     "qlin_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w8a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemm_w4a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
 }
@@ -184,8 +185,9 @@ def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):
     lib = load()
     _dev_tensor(wq, "wq")
     m, n = xq.shape[0], wq.shape[0]
-    kb = k // 2 if fn_name == "qlin_gemm_w4a4" else k
-    _need(xq, m * kb, "xq")
+    ka = k // 2 if fn_name == "qlin_gemm_w4a4" else k
+    kb = k if fn_name == "qlin_gemm_w8a8" else k // 2
+    _need(xq, m * ka, "xq")
     _need(wq, n * kb, "wq")
     _need(x_scale, m * 4, "x_scale")
     _need(w_scale, n * 4, "w_scale")
@@ -205,6 +207,11 @@ def qlin_gemm_w4a4(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out
 def qlin_gemm_w8a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
     """y [m][n] from int8 codes xq [m][k], wq [n][k]."""
     return _gemm("qlin_gemm_w8a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
+
+
+def qlin_gemm_w4a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """y [m][n] from int8 activation codes xq [m][k] and packed int4 weight codes wq [n][k/2]."""
+    return _gemm("qlin_gemm_w4a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
 
 
 def qlin_gemm_w4a4_geglu(xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat16, out=None) -> torch.Tensor:

@@ -54,7 +54,8 @@ struct GemmParams {
     void* y;              // [m][n]
     int32_t* ws;          // split-K partials [splits][m][n]
     int64_t m, n;
-    int64_t kbytes;       // bytes per row of A and B
+    int64_t kbytes;       // bytes per row of B (and of A, except W4A8)
+    int64_t kbytes_a;     // bytes per row of A
     int stages;           // ceil(kbytes / 64)
     int stages_per_split;
     int tiles_m, tiles_n, splits;
@@ -70,6 +71,15 @@ constexpr int OUT_GEGLU = 16;
 __device__ __forceinline__ v4i unpack_int4(uint32_t w0, uint32_t w1) {
     return v4i{static_cast<int>((w0 << 4) & 0xF0F0F0F0u), static_cast<int>((w1 << 4) & 0xF0F0F0F0u),
                static_cast<int>(w0 & 0xF0F0F0F0u), static_cast<int>(w1 & 0xF0F0F0F0u)};
+}
+
+// 16 int8 values k0..k15 (W4A8 activations) in the k order of unpack_int4:
+// k 0 2 4 6 | 8 10 12 14 | 1 3 5 7 | 9 11 13 15 (v_perm_b32 byte selects).
+__device__ __forceinline__ v4i order_int8_as_int4(uint4 d) {
+    return v4i{static_cast<int>(__builtin_amdgcn_perm(d.y, d.x, 0x06040200u)),
+               static_cast<int>(__builtin_amdgcn_perm(d.w, d.z, 0x06040200u)),
+               static_cast<int>(__builtin_amdgcn_perm(d.y, d.x, 0x07050301u)),
+               static_cast<int>(__builtin_amdgcn_perm(d.w, d.z, 0x07050301u))};
 }
 
 __device__ __forceinline__ void store_out(void* y, int64_t idx, int dt, float v) {
@@ -89,6 +99,9 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, int dt, float v)
 // counter measurement (SQ_LDS_BANK_CONFLICT zero, against two-way conflicts
 // for ((r >> 1) ^ (r >> 3)) & 3 and four-way without a swizzle).
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// The same for 128-byte rows (eight chunks, W4A8's A operand), also measured
+// conflict-free: (r >> 1) & 7.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // Waits until at most N of this wave's vector-memory operations (here: the
 // DMA loads into LDS) are outstanding.
@@ -164,7 +177,7 @@ __device__ __forceinline__ float gelu_outside_tab(uint32_t bits) {
 // group for values outside it), h = gelu(g) * u is rounded to the output
 // dtype and staged through LDS for 16-byte row stores of the (BM/2) x (BN/4)
 // h tile.
-template <int BM, int BN, bool INT4, int ODT, int STAGE>
+template <int BM, int BN, int ASH, int ODT, int STAGE>
 __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
                                                  int64_t row0, int64_t col0, int lane, const float* tab,
                                                  int8_t* region) {
@@ -192,7 +205,10 @@ __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN /
             rs_w, static_cast<int>((col0 + 64 * q + l32) * 4), 0, 0));
         swu[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
             rs_w, static_cast<int>((col0 + 64 * q + 32 + l32) * 4), 0, 0));
-        if constexpr (INT4) { swg[q] *= 0.00390625f; swu[q] *= 0.00390625f; }   // 256 * acc, exact
+        if constexpr (ASH > 0) {   // the accumulator holds 2^ASH * acc; the power of two is exact
+            swg[q] *= 1.0f / static_cast<float>(1 << ASH);
+            swu[q] *= 1.0f / static_cast<float>(1 << ASH);
+        }
     }
     const bool vec_ok = ((nh * E) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
 
@@ -296,7 +312,7 @@ __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN /
 // elements) so that the two half-waves, which write rows 4 apart, hit
 // different banks.  OUT: -1 raw int32 partial, I32 raw accumulators, else
 // the dequantized value acc * x_scale[row] * w_scale[col] rounded to OUT.
-template <int BM, int BN, bool INT4, int OUT, int STAGE>
+template <int BM, int BN, int ASH, int OUT, int STAGE>
 __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
                                                int64_t row0, int64_t col0, int lane, int8_t* region,
                                                void* dst) {
@@ -326,9 +342,9 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
         if constexpr (FLOAT_OUT)
             swv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                 rs_w, static_cast<int>((col0 + j * 32 + l32) * 4), 0, 0));
-        // int4: the accumulator holds 256 * acc; fp32(256 * acc) is exact (acc has
-        // at most 17 significant bits), so the 1/256 joins the column scale
-        if constexpr (FLOAT_OUT && INT4) swv[j] *= 0.00390625f;
+        // int4 operands: the accumulator holds 2^ASH * acc; scaling by a power of
+        // two commutes with fp32 rounding, so 2^-ASH joins the column scale exactly
+        if constexpr (FLOAT_OUT && ASH > 0) swv[j] *= 1.0f / static_cast<float>(1 << ASH);
     }
     const int64_t ldy = p.n;
     const bool vec_ok = ((p.n * E) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
@@ -370,7 +386,7 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
                             *reinterpret_cast<float*>(at + PITCH) = v1;
                         }
                     } else {
-                        if constexpr (INT4) { a0 >>= 8; a1 >>= 8; }
+                        if constexpr (ASH > 0) { a0 >>= ASH; a1 >>= ASH; }
                         *reinterpret_cast<int32_t*>(at) = a0;
                         *reinterpret_cast<int32_t*>(at + PITCH) = a1;
                     }
@@ -410,15 +426,21 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
     }
 }
 
-template <int BM, int BN, int MINB, int NS, bool INT4, int OUT>
+// INT4: B (weights) is packed int4.  A8 (with INT4): A (activations) is
+// int8 while B is int4 (W4A8); a stage then holds 128 k: 128 bytes of an A
+// row and 64 bytes of a B row.
+template <int BM, int BN, int MINB, int NS, bool INT4, int OUT, bool A8 = false>
 __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
+    static_assert(!A8 || INT4, "W4A8 takes int4 weights");
     // NS: pipeline stages (ring of LDS buffers)
     constexpr int TM = BM / 64;                  // MFMA tiles per wave along M
     constexpr int TN = BN / 64;                  // ... along N
-    constexpr int A_INSTR = BM / 64;             // 16-byte DMA loads per lane per stage (A)
+    constexpr int SA = A8 ? 2 * STAGE_BYTES : STAGE_BYTES;   // A bytes per row per stage
+    constexpr int A_INSTR = BM * SA / 4096;      // 16-byte DMA loads per lane per stage (A)
     constexpr int B_INSTR = BN / 64;
     constexpr int LOADS = A_INSTR + B_INSTR;     // per lane per stage
-    constexpr int STAGE = (BM + BN) * STAGE_BYTES;
+    constexpr int STAGE = BM * SA + BN * STAGE_BYTES;
+    constexpr int ASH = A8 ? 4 : (INT4 ? 8 : 0);   // accumulator = 2^ASH * acc
     // The DMA is issued through inline assembly, invisible to the compiler,
     // so one array serves the whole ring (and the epilogue staging after it).
     // The fused GeGLU epilogue keeps its GeLU table at LDS offset 0 (table reads
@@ -451,27 +473,34 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
 
     // Buffer resources based at the tile's first row: rows past the matrix
     // are out of range (the hardware returns zeros, nothing is fetched).
-    const int64_t a_rem = (p.m - m0) * p.kbytes;
+    const int64_t a_rem = (p.m - m0) * p.kbytes_a;
     const int64_t b_rem = (p.n - n0) * p.kbytes;
-    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes, a_rem);
+    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes_a, a_rem);
     const v4i rsrc_b = make_rsrc(p.b + n0 * p.kbytes, b_rem);
 
     // DMA mapping: load instruction i of wave w fills LDS chunk slots
     // [(4i + w) * 64, +64) of its operand, i.e. 16 rows; lane l fills slot
     // P = (4i + w) * 64 + l = row (P >> 2), slot (P & 3), so it fetches the
     // row's chunk (P & 3) ^ swz(row).
+    // W4A8's 128-byte A rows: eight chunks, 8 rows per instruction and wave,
+    // slot P -> row P >> 3, chunk (P & 7) ^ swz8(row).
     const int dma_row0 = wave * 16 + (lane >> 2);            // + 64 * i
     const int dma_chunk = (lane & 3) ^ swz(dma_row0);        // swz(row + 64 i) == swz(row)
     const int dma_voff = dma_row0 * static_cast<int>(p.kbytes) + dma_chunk * 16;
     const int row64 = 64 * static_cast<int>(p.kbytes);
+    const int dma_row0_a = A8 ? wave * 8 + (lane >> 3) : dma_row0;   // + 32 * i (A8)
+    const int dma_chunk_a = A8 ? (lane & 7) ^ swz8(dma_row0_a) : dma_chunk;   // swz8(row + 32 i) == swz8(row)
+    const int dma_voff_a = dma_row0_a * static_cast<int>(p.kbytes_a) + dma_chunk_a * 16;
+    const int rowstep_a = (A8 ? 32 : 64) * static_cast<int>(p.kbytes_a);
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int st, int8_t* buf) {
         const int kb = (s_begin + st) * STAGE_BYTES;
+        const int ka = (s_begin + st) * SA;
         const uint32_t a_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + wave_u * 1024;
-        const uint32_t b_dst = a_dst + BM * STAGE_BYTES;
+        const uint32_t b_dst = a_dst + BM * SA;
 #pragma unroll
-        for (int i = 0; i < A_INSTR; ++i) dma16(rsrc_a, dma_voff + kb + i * row64, a_dst + i * 4096);
+        for (int i = 0; i < A_INSTR; ++i) dma16(rsrc_a, dma_voff_a + ka + i * rowstep_a, a_dst + i * 4096);
 #pragma unroll
         for (int i = 0; i < B_INSTR; ++i) dma16(rsrc_b, dma_voff + kb + i * row64, b_dst + i * 4096);
     };
@@ -489,10 +518,14 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     const int l32 = lane & 31;
     const int hsel = lane >> 5;
     const int sw = swz(l32);  // tile bases are multiples of 32: swz(base + l32) == swz(l32)
-    const int a_rd0 = (wm * (BM / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
-    const int a_rd1 = (wm * (BM / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
-    const int b_rd0 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
-    const int b_rd1 = BM * STAGE_BYTES + (wn * (BN / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
+    const int a_rd0 = (wm * (BM / 2) + l32) * SA + ((0 + hsel) ^ sw) * 16;
+    const int a_rd1 = (wm * (BM / 2) + l32) * SA + ((2 + hsel) ^ sw) * 16;
+    const int b_rd0 = BM * SA + (wn * (BN / 2) + l32) * STAGE_BYTES + ((0 + hsel) ^ sw) * 16;
+    const int b_rd1 = BM * SA + (wn * (BN / 2) + l32) * STAGE_BYTES + ((2 + hsel) ^ sw) * 16;
+    // W4A8: the int8 A values of B chunk c = 2 ks + hsel, k-slice h, are A
+    // chunk 2 c + h of the 128-byte A row
+    const int sw8 = swz8(l32);
+    const int a8_row = (wm * (BM / 2) + l32) * SA;
 
     // Pipeline unit: what one 16-byte LDS read per operand fragment feeds.
     // int4: one chunk (two MFMA k-slices once unpacked), two units per stage;
@@ -501,8 +534,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     // int4 the unpacking of the next k-slice runs under the current MFMAs.
     constexpr int UPS = INT4 ? 2 : 1;
     constexpr int FR = INT4 ? 1 : 2;
+    constexpr int FRA = A8 ? 2 : FR;   // A reads per unit and row tile
     struct Unit {
-        uint4 a[FR][TM];
+        uint4 a[FRA][TM];
         uint4 b[FR][TN];
     };
     auto read_unit = [&](const int8_t* st, int ks0, Unit& u) {
@@ -510,17 +544,33 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
         for (int f = 0; f < FR; ++f) {
             const int ar = (ks0 + f) == 0 ? a_rd0 : a_rd1;
             const int br = (ks0 + f) == 0 ? b_rd0 : b_rd1;
+            if constexpr (!A8) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) u.a[f][i] = *reinterpret_cast<const uint4*>(st + ar + i * 32 * STAGE_BYTES);
+                for (int i = 0; i < TM; ++i) u.a[f][i] = *reinterpret_cast<const uint4*>(st + ar + i * 32 * SA);
+            }
 #pragma unroll
             for (int j = 0; j < TN; ++j) u.b[f][j] = *reinterpret_cast<const uint4*>(st + br + j * 32 * STAGE_BYTES);
         }
+        if constexpr (A8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ch = (2 * (2 * ks0 + hsel) + h) ^ sw8;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    u.a[h][i] = *reinterpret_cast<const uint4*>(st + a8_row + ch * 16 + i * 32 * SA);
+            }
+        }
     };
-    // int4 k-slice h (0: dwords x,y; 1: z,w) of a unit as MFMA operands
+    // int4 k-slice h (0: dwords x,y; 1: z,w) of a unit as MFMA operands; the
+    // int8 A of W4A8 is put into the same k order as the unpacked nibbles
     auto unpack = [&](const Unit& u, int h, v4i (&oa)[TM], v4i (&ob)[TN]) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            oa[i] = h == 0 ? unpack_int4(u.a[0][i].x, u.a[0][i].y) : unpack_int4(u.a[0][i].z, u.a[0][i].w);
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (A8)
+                oa[i] = order_int8_as_int4(u.a[h][i]);
+            else
+                oa[i] = h == 0 ? unpack_int4(u.a[0][i].x, u.a[0][i].y) : unpack_int4(u.a[0][i].z, u.a[0][i].w);
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             ob[j] = h == 0 ? unpack_int4(u.b[0][j].x, u.b[0][j].y) : unpack_int4(u.b[0][j].z, u.b[0][j].w);
@@ -641,13 +691,13 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     if (!wave_active) return;   // no output rows (no block-wide barrier follows)
     if constexpr (GEGLU) {
         constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
-        store_tile_geglu<BM, BN, INT4, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),
+        store_tile_geglu<BM, BN, ASH, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),
                                                                 lane, reinterpret_cast<const float*>(lds),
                                                                 ring + wave * REGION);
     } else {
         void* dst = (OUT == -1) ? static_cast<void*>(p.ws + static_cast<int64_t>(split) * p.m * p.n) : p.y;
         constexpr int REGION = NS * STAGE / 4 / 16 * 16;  // per-wave staging bytes
-        store_tile_lds<BM, BN, INT4, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+        store_tile_lds<BM, BN, ASH, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
                                                   ring + wave * REGION, dst);
     }
 }
@@ -726,21 +776,21 @@ __global__ __launch_bounds__(256) void splitk_reduce8_kernel(const int32_t* ws, 
     }
 }
 
-template <int BM, int BN, int MINB, int NS, bool INT4, int OUT>
+template <int BM, int BN, int MINB, int NS, bool INT4, int OUT, bool A8 = false>
 hipError_t launch_tile(const GemmParams& p, hipStream_t st) {
     dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n * p.splits));
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, MINB, NS, INT4, OUT>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, MINB, NS, INT4, OUT, A8>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int MINB, int NS, bool INT4>
+template <int BM, int BN, int MINB, int NS, bool INT4, bool A8 = false>
 hipError_t launch_out(const GemmParams& p, hipStream_t st) {
-    if (p.splits > 1) return launch_tile<BM, BN, MINB, NS, INT4, -1>(p, st);
+    if (p.splits > 1) return launch_tile<BM, BN, MINB, NS, INT4, -1, A8>(p, st);
     switch (p.y_dtype) {
-        case BF16: return launch_tile<BM, BN, MINB, NS, INT4, BF16>(p, st);
-        case F16: return launch_tile<BM, BN, MINB, NS, INT4, F16>(p, st);
-        case F32: return launch_tile<BM, BN, MINB, NS, INT4, F32>(p, st);
-        case I32: return launch_tile<BM, BN, MINB, NS, INT4, I32>(p, st);
+        case BF16: return launch_tile<BM, BN, MINB, NS, INT4, BF16, A8>(p, st);
+        case F16: return launch_tile<BM, BN, MINB, NS, INT4, F16, A8>(p, st);
+        case F32: return launch_tile<BM, BN, MINB, NS, INT4, F32, A8>(p, st);
+        case I32: return launch_tile<BM, BN, MINB, NS, INT4, I32, A8>(p, st);
     }
     return hipErrorInvalidValue;
 }
@@ -775,14 +825,15 @@ hipError_t ensure_gelu_neg_tab(hipStream_t st) {
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4) {
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
     // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes
     // per MFMA), two blocks per CU (one block's per-stage barrier and LDS
     // latency is covered by the other block's MFMAs).
-    // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per CU.)
+    // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per
+    // CU; so does W4A8, whose 128 x 256 stage would not leave room for 3 stages.)
     GemmPlan g;
     g.bm = 128;
-    g.bn = (n >= 4096 && int4) ? 256 : 128;
+    g.bn = (n >= 4096 && int4 && !a8) ? 256 : 128;
     const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
     const int64_t kbytes = int4 ? k / 2 : k;
     const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
@@ -803,7 +854,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4) {
 }
 
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
-                       const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, void* y,
+                       const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st) {
     GemmParams p;
     p.a = static_cast<const int8_t*>(xq);
@@ -811,6 +862,7 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     p.sx = x_scale; p.sw = w_scale; p.y = y; p.ws = ws;
     p.m = m; p.n = n;
     p.kbytes = int4 ? k / 2 : k;
+    p.kbytes_a = (int4 && !a8) ? k / 2 : k;
     p.stages = static_cast<int>((p.kbytes + STAGE_BYTES - 1) / STAGE_BYTES);
     p.splits = plan.splits;
     p.stages_per_split = (p.stages + plan.splits - 1) / plan.splits;
@@ -818,7 +870,10 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
     p.y_dtype = y_dtype;
     hipError_t e;
-    if (plan.bn == 256) {
+    if (a8) {
+        if (!int4 || plan.bn != 128) return hipErrorInvalidValue;
+        e = plan.deep ? launch_out<128, 128, 1, 6, true, true>(p, st) : launch_out<128, 128, 2, 3, true, true>(p, st);
+    } else if (plan.bn == 256) {
         if (!int4) return hipErrorInvalidValue;
         e = plan.deep ? launch_out<128, 256, 1, 6, true>(p, st) : launch_out<128, 256, 2, 3, true>(p, st);
     } else if (plan.deep) {
@@ -856,13 +911,14 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
     if (!int4) return hipErrorInvalidValue;   // the gate|up projections run at W4A4
     hipError_t e = ensure_gelu_neg_tab(st);
     if (e != hipSuccess) return e;
-    const GemmPlan plan = plan_gemm(m, n, k, int4);   // tile shape; the fused epilogue takes no split
+    const GemmPlan plan = plan_gemm(m, n, k, int4, false);   // tile shape; the fused epilogue takes no split
     GemmParams p;
     p.a = static_cast<const int8_t*>(xq);
     p.b = static_cast<const int8_t*>(wq);
     p.sx = x_scale; p.sw = w_scale; p.y = y; p.ws = nullptr;
     p.m = m; p.n = n;
     p.kbytes = int4 ? k / 2 : k;
+    p.kbytes_a = p.kbytes;
     p.stages = static_cast<int>((p.kbytes + STAGE_BYTES - 1) / STAGE_BYTES);
     p.splits = 1;
     p.stages_per_split = p.stages;

@@ -77,7 +77,7 @@ constexpr int64_t kMaxRowK = 32768;
 
 qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                         int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream,
-                        bool int4) {
+                        bool int4, bool a8) {
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !y) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
@@ -86,25 +86,26 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
     const int64_t kstep = int4 ? 128 : 64;
     if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return QLIN_ERR_SHAPE;
-    if (k > 131072) return QLIN_ERR_SHAPE;  // keeps |acc| (and 256*acc for int4) below 2^31
+    if (k > 131072) return QLIN_ERR_SHAPE;  // keeps |acc| (256*acc for int4, 16*acc W4A8) below 2^31
     if (m > 0x7FFFFFFF || n > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))
         return QLIN_ERR_ALIGN;
     const int64_t kb = int4 ? k / 2 : k;
+    const int64_t ka = (int4 && !a8) ? k / 2 : k;
     const Span outs[1] = {{y, m * n * dtype_size(y_dtype)}};
-    const Span ins[4] = {{xq, m * kb}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
+    const Span ins[4] = {{xq, m * ka}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
     if (any_overlap(outs, 1, ins, 4)) return QLIN_ERR_ALIAS;
     if (m == 0) return QLIN_OK;
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
-    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4);
+    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8);
     hipStream_t s = as_stream(stream);
     int32_t* ws = nullptr;
     if (plan.ws_bytes > 0) {
         if (hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.ws_bytes), s) != hipSuccess)
             return QLIN_ERR_DEVICE;
     }
-    hipError_t e = qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, y, y_dtype, ws, s);
+    hipError_t e = qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, ws, s);
     if (ws) {
         if (hipFreeAsync(ws, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
     }
@@ -204,12 +205,17 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true, false);
 }
 
 qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, false, false);
+}
+
+qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                           int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true, true);
 }
 
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

@@ -23,7 +23,8 @@ hipError_t launch_calibrate_fold(const void* x, int x_dtype, int64_t m, int64_t 
                                  bool geglu, const void* w, int w_dtype, int64_t n, float* s,
                                  float* inv_s, hipStream_t st);
 
-// Integer GEMM.  int4 == true: both operands are packed int4 codes.
+// Integer GEMM.  int4 == true: the weights are packed int4 codes, and so are
+// the activations unless a8.
 // ws: int32 workspace of splits * m * n elements when splits > 1.
 struct GemmPlan {
     int bm, bn;     // block tile
@@ -31,9 +32,10 @@ struct GemmPlan {
     bool deep;      // grid fits one block per CU: one block per CU with a deeper DMA ring
     int64_t ws_bytes;
 };
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4);
+// a8 (with int4): int8 activations against int4 weights (W4A8).
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8);
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
-                       const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, void* y,
+                       const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st);
 // Gate|up GEMM with the GeGLU epilogue: n interleaved rows (blocks of 32 gate
 // rows then 32 up rows), y [m][n/2] = gelu(g) * u.  int4 only, no split-K.

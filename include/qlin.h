@@ -159,6 +159,21 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
                            qlin_dtype y_dtype, void* stream);
 
 /*
+ * qlin_gemm_w4a8 -- W4A8: int8 activation codes against packed int4 weight
+ * codes (QuantVLA summary, "4. 実験結果": the setting it is evaluated in,
+ * 4-bit weights and 8-bit activations).
+ *   xq:      int8 [m][k] (qlin_rotate_quant_act with bits 8);
+ *   wq:      uint8 [n][k/2] packed int4 (qlin_quantize_weights with bits 4);
+ *   acc, y, scales, dtypes, stream and errors exactly as qlin_gemm_w4a4.
+ * Preconditions: k a multiple of 128, at most 131072; otherwise those of
+ * qlin_gemm_w4a4.  May take a split-K workspace from the stream-ordered
+ * allocator, as the other GEMMs.
+ */
+qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
+                           const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                           qlin_dtype y_dtype, void* stream);
+
+/*
  * qlin_gemm_w4a4_geglu -- the backbone MLP's gate and up projections with the
  * gated GeLU fused into the epilogue (FoldQuantVLA abstract: the projections
  * run natively in integer arithmetic; the gated GeLU joins them here so that

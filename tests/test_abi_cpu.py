@@ -36,7 +36,7 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for n in ("qlin_rotate_quant_act", "qlin_quantize_weights", "qlin_gemm_w4a4", "qlin_gemm_w8a8",
+    for n in ("qlin_rotate_quant_act", "qlin_quantize_weights", "qlin_gemm_w4a4", "qlin_gemm_w8a8", "qlin_gemm_w4a8",
               "qlin_gemm_w4a4_geglu", "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version",
               "qlin_status_string"):
         assert n in names
@@ -105,7 +105,7 @@ def test_quantize_weights_rejects(lib, kw, status):
 
 # ---- qlin_gemm_*(xq, sx, wq, sw, m, n, k, y, ydt, stream)
 
-@pytest.mark.parametrize("fn", ["qlin_gemm_w4a4", "qlin_gemm_w8a8"])
+@pytest.mark.parametrize("fn", ["qlin_gemm_w4a4", "qlin_gemm_w8a8", "qlin_gemm_w4a8"])
 @pytest.mark.parametrize("kw,status", [
     (dict(xq=None), q.QLIN_ERR_NULL), (dict(wq=None), q.QLIN_ERR_NULL), (dict(y=None), q.QLIN_ERR_NULL),
     (dict(sx=None), q.QLIN_ERR_NULL), (dict(sw=None), q.QLIN_ERR_NULL),
@@ -121,6 +121,13 @@ def test_gemm_rejects(lib, fn, kw, status):
     f = getattr(lib, fn)
     assert f(args["xq"], args["sx"], args["wq"], args["sw"], args["m"], args["n"], args["k"], args["y"],
              args["ydt"], None) == status
+
+
+@pytest.mark.parametrize("fn,k,status", [("qlin_gemm_w8a8", 192, q.QLIN_OK), ("qlin_gemm_w4a8", 192, q.QLIN_ERR_SHAPE),
+                                         ("qlin_gemm_w4a4", 192, q.QLIN_ERR_SHAPE)])
+def test_gemm_k_step_per_scheme(lib, fn, k, status):
+    # int4 weights take k in multiples of 128; int8 x int8 in multiples of 64 (m = 0: no device call)
+    assert getattr(lib, fn)(None, None, P2, P4, 0, 64, k, 0x70000000, 1, None) == status
 
 
 def test_gemm_raw_i32_needs_no_scales_and_empty_ok(lib):

@@ -156,19 +156,27 @@ GEMM_SHAPES = [
 ]
 
 
+# scheme -> (activation bits, weight bits, entry point)
+SCHEMES = {"w4a4": (4, 4, "qlin_gemm_w4a4"), "w8a8": (8, 8, "qlin_gemm_w8a8"), "w4a8": (8, 4, "qlin_gemm_w4a8")}
+
+
+def scheme_codes(scheme, tag, m, n, k):
+    abits, wbits, fn = SCHEMES[scheme]
+    a = synth.random_codes(SEED, f"A{tag}/{m}/{k}/{abits}", m, k, abits)
+    b = synth.random_codes(SEED, f"B{tag}/{n}/{k}/{wbits}", n, k, wbits)
+    return a, b, abits, wbits, getattr(q, fn)
+
+
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
-@pytest.mark.parametrize("scheme", ["w4a4", "w8a8"])
+@pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
 def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k):
     say(f"gemm i32 {scheme} {m}x{n}x{k}")
-    bits = 4 if scheme == "w4a4" else 8
-    if bits == 4 and k % 128:
-        pytest.skip("w4a4 takes k in multiples of 128")
-    a = synth.random_codes(SEED, f"A/{m}/{k}/{bits}", m, k, bits)
-    b = synth.random_codes(SEED, f"B/{n}/{k}/{bits}", n, k, bits)
-    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
+    if scheme != "w8a8" and k % 128:
+        pytest.skip("int4 weights take k in multiples of 128")
+    a, b, abits, wbits, fn = scheme_codes(scheme, "", m, n, k)
     acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
     torch.cuda.synchronize()
-    ref = oracle.int_gemm(codes_np(a, bits), codes_np(b, bits))
+    ref = oracle.int_gemm(codes_np(a, abits), codes_np(b, wbits))
     got = acc.cpu().numpy().astype(np.int64)
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
@@ -180,20 +188,18 @@ BIG_GRID_SHAPES = [
     ("w8a8", 1100, 3968, 256),    # 9 x 31 tiles of 128 x 128
     ("w4a4", 1100, 3968, 256),    # 9 x 31 tiles of 128 x 128
     ("w4a4", 2100, 4096, 256),    # 17 x 16 tiles of 128 x 256
+    ("w4a8", 1100, 3968, 512),    # 9 x 31 tiles of 128 x 128
 ]
 
 
 @pytest.mark.parametrize("scheme,m,n,k", BIG_GRID_SHAPES)
 def test_gemm_big_grid_sampled_rows(scheme, m, n, k):
     say(f"gemm i32 big grid {scheme} {m}x{n}x{k}")
-    bits = 4 if scheme == "w4a4" else 8
-    a = synth.random_codes(SEED, f"Abig/{m}/{k}/{bits}", m, k, bits)
-    b = synth.random_codes(SEED, f"Bbig/{n}/{k}/{bits}", n, k, bits)
-    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
+    a, b, abits, wbits, fn = scheme_codes(scheme, "big", m, n, k)
     acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
     torch.cuda.synchronize()
     rows = _sample_rows(m, 24)
-    ref = oracle.int_gemm(codes_np(a, bits)[rows], codes_np(b, bits))
+    ref = oracle.int_gemm(codes_np(a, abits)[rows], codes_np(b, wbits))
     got = acc.cpu().numpy().astype(np.int64)[rows]
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
@@ -216,18 +222,17 @@ def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
 @pytest.mark.parametrize("out", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scheme,m,n,k", [("w4a4", 300, 520, 1024), ("w8a8", 129, 384, 4096),
                                           ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512),
-                                          ("w8a8", 40, 100, 4096), ("w4a4", 17, 99, 2048)])
+                                          ("w8a8", 40, 100, 4096), ("w4a4", 17, 99, 2048),
+                                          ("w4a8", 300, 520, 1024), ("w4a8", 64, 256, 16384),
+                                          ("w4a8", 17, 99, 2048)])
 def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     say(f"gemm {out} {scheme} {m}x{n}x{k}")
-    bits = 4 if scheme == "w4a4" else 8
-    a = synth.random_codes(SEED, f"Ae/{m}/{k}/{bits}", m, k, bits)
-    b = synth.random_codes(SEED, f"Be/{n}/{k}/{bits}", n, k, bits)
+    a, b, abits, wbits, fn = scheme_codes(scheme, "e", m, n, k)
     sx = synth.random_scales(SEED, f"sx/{m}", m)
     sw = synth.random_scales(SEED, f"sw/{n}", n)
-    fn = q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8
     y = fn(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, y_dtype=DT[out])
     torch.cuda.synchronize()
-    _, _, y_ref = oracle.gemm(codes_np(a, bits), sx.numpy(), codes_np(b, bits), sw.numpy(), out)
+    _, _, y_ref = oracle.gemm(codes_np(a, abits), sx.numpy(), codes_np(b, wbits), sw.numpy(), out)
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
 
 
