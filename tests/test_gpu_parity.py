@@ -476,3 +476,115 @@ def test_backbone_mlp_block_fused_geglu_full_size():
     _, _, y2_ref = oracle.gemm(codes_np(hq, 8)[rows], hs.cpu().numpy()[rows], codes_np(wq2, 8),
                                ws2.cpu().numpy(), "bf16")
     assert_ok(oracle.compare_outputs(f64(y2)[rows], y2_ref), "down output")
+
+
+def _check_linear(x, w, s, b, bits, out, rows=None, scheme_fn=None):
+    """One quantized projection on the GPU, checked stage by stage against the
+    oracle: weight codes and scales, activation codes and scales, output (on
+    sampled rows when `rows` is given)."""
+    xd, wd = x.to(DEV), w.to(DEV)
+    sd = None if s is None else s.to(DEV)
+    inv = None if s is None else (1.0 / s).to(DEV)
+    wq, ws = q.qlin_quantize_weights(wd, fold_s=sd, had_block=b, bits=bits)
+    xq, xs = q.qlin_rotate_quant_act(xd, fold_inv_s=inv, had_block=b, bits=bits)
+    fn = scheme_fn or (q.qlin_gemm_w4a4 if bits == 4 else q.qlin_gemm_w8a8)
+    y = fn(xq, xs, wq, ws, x.shape[1], y_dtype=DT[out])
+    torch.cuda.synchronize()
+    sg = None if s is None else s.numpy()
+    r = np.arange(x.shape[0]) if rows is None else rows
+    rd = torch.as_tensor(r, device=DEV)
+    rw = _sample_rows(w.shape[0], 32)
+    qw_ref, sw_ref, rr = oracle.quantize_weights(synth.to_f64(w[rw]), sg, b, bits)
+    assert_ok(oracle.compare_codes(codes_np(wq, bits)[rw], qw_ref, rr), "weight codes")
+    assert_ok(oracle.compare_scales(ws.cpu().numpy()[rw], sw_ref), "weight scales")
+    qx_ref, sx_ref, rx = oracle.rotate_quant_act(synth.to_f64(x[r]), sg, b, bits)
+    xq_r = codes_np(xq[rd], bits)
+    xs_r = xs[rd].cpu().numpy()
+    assert_ok(oracle.compare_codes(xq_r, qx_ref, rx), "act codes")
+    assert_ok(oracle.compare_scales(xs_r, sx_ref), "act scales")
+    _, _, y_ref = oracle.gemm(xq_r, xs_r, codes_np(wq, bits), ws.cpu().numpy(), out)
+    assert_ok(oracle.compare_outputs(f64(y[rd]), y_ref), "output")
+
+
+@pytest.mark.slow
+def test_action_expert_denoising_steps():
+    """Action expert (M = 50; q, k, v, o 1024x1024, up 4096x1024, down
+    1024x4096) at denoising steps 0, 4 and 9: X_t ~ N(0, sigma_t^2) per
+    projection and step, the fold calibrated on step 0, W4A4 with b = 64,
+    fp16 out; and the W4A16 g128 GEMV on the same weights and inputs."""
+    wl = synth.CFG3
+    for proj in wl.projs:
+        w = synth.weight(wl, proj)
+        x0 = synth.activation(wl, proj, 50, tag="/t0", std=synth.cfg3_sigma(0))
+        s = oracle.calibrate_fold(synth.to_f64(x0), synth.to_f64(w)).astype(np.float32)
+        wq16, ws16 = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
+        for t in (0, 4, 9):
+            say(f"action expert {proj.name} step {t}")
+            x = synth.activation(wl, proj, 50, tag=f"/t{t}", std=synth.cfg3_sigma(t))
+            _check_linear(x, w, torch.from_numpy(s), 64, 4, "f16")
+            y16 = q.qlin_gemv_w4a16(x.to(DEV), wq16, ws16)
+            torch.cuda.synchronize()
+            _, y16_ref = oracle.gemv_w4a16(synth.to_f64(x), codes_np(wq16, 4), ws16.cpu().numpy(), 128)
+            assert_ok(oracle.compare_outputs(f64(y16), y16_ref), "W4A16 output")
+
+
+@pytest.mark.slow
+def test_decoder7b_w8a8_m256():
+    """7B-decoder projections at M = 256, W8A8 per-token / per-channel (no
+    fold, no rotation), fp16 out; sampled rows."""
+    wl = synth.CFG4
+    for proj in wl.projs[3:]:   # o 4096x4096, gate and up 11008x4096, down 4096x11008
+        say(f"decoder W8A8 {proj.name} {proj.n}x{proj.k}")
+        x = synth.activation(wl, proj, 256)
+        w = synth.weight(wl, proj)
+        _check_linear(x, w, None, 0, 8, "f16", rows=_sample_rows(256, 12))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("m", [6528, 52224])
+def test_backbone_sweep_layer_large_m(m):
+    """One layer of the 18-layer backbone sweep at M = 6528 and 52224: q (W4A4
+    2048x2048), o (W8A8 2048x2048) and the fused gate|up GeGLU GEMM (W4A4
+    32768x2048 interleaved) -> int8 h -> down (W8A8 2048x16384); b = 128,
+    bf16; sampled rows, stage by stage."""
+    wl = synth.CFG5
+    projs = {p.name: p for p in wl.projs}
+    rows = _sample_rows(m, 8)
+    rd = torch.as_tensor(rows, device=DEV)
+    for name in ("q", "o"):
+        p = projs[name]
+        say(f"sweep M={m} {name}")
+        x = synth.activation(wl, p, m, tag="/L0")
+        w = synth.weight(wl, p, tag="/L0")
+        s = oracle.calibrate_fold(synth.to_f64(x), synth.to_f64(w)).astype(np.float32)
+        _check_linear(x, w, torch.from_numpy(s), 128, 4 if p.scheme == "w4a4" else 8, "bf16", rows=rows)
+    gu, dn = projs["gate_up"], projs["down"]
+    f = dn.k
+    say(f"sweep M={m} gate|up GeGLU")
+    x = synth.activation(wl, gu, m, tag="/L0")
+    w_gu = synth.weight(wl, gu, tag="/L0")
+    w_int = q.interleave_gate_up(w_gu[:f], w_gu[f:])
+    xd, wd = x.to(DEV), w_int.to(DEV)
+    s1, inv1 = q.qlin_calibrate_fold(xd, wd)
+    wq1, ws1 = q.qlin_quantize_weights(wd, fold_s=s1, had_block=128, bits=4)
+    xq1, xs1 = q.qlin_rotate_quant_act(xd, fold_inv_s=inv1, had_block=128, bits=4)
+    h = q.qlin_gemm_w4a4_geglu(xq1, xs1, wq1, ws1, gu.k, h_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _, _, h_ref = oracle.gemm_geglu(codes_np(xq1[rd], 4), xs1[rd].cpu().numpy(), codes_np(wq1, 4),
+                                    ws1.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(h[rd]), h_ref), "h")
+    say(f"sweep M={m} down")
+    w_dn = synth.weight(wl, dn, tag="/L0")
+    wdd = w_dn.to(DEV)
+    s2, inv2 = q.qlin_calibrate_fold(h, wdd)
+    wq2, ws2 = q.qlin_quantize_weights(wdd, fold_s=s2, had_block=128, bits=8)
+    hq, hs = q.qlin_rotate_quant_act(h, fold_inv_s=inv2, had_block=128, bits=8)
+    y = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, f, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    hf = f64(h[rd])
+    qh, sh, rh = oracle.rotate_quant_act(hf, s2.cpu().numpy(), 128, 8)
+    hq_r = codes_np(hq[rd], 8)
+    assert_ok(oracle.compare_codes(hq_r, qh, rh), "h codes")
+    assert_ok(oracle.compare_scales(hs[rd].cpu().numpy(), sh), "h scales")
+    _, _, y_ref = oracle.gemm(hq_r, hs[rd].cpu().numpy(), codes_np(wq2, 8), ws2.cpu().numpy(), "bf16")
+    assert_ok(oracle.compare_outputs(f64(y[rd]), y_ref), "down output")
