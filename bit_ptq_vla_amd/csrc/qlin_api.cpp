@@ -75,6 +75,9 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // 256 lanes x 16 chunks x 8 values.
 constexpr int64_t kMaxRowK = 32768;
 
+// GEMM k bound (exclusive): 2^17.
+constexpr int64_t kMaxGemmK = 131072;
+
 qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                         int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream,
                         bool int4, bool a8) {
@@ -86,7 +89,9 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
     const int64_t kstep = int4 ? 128 : 64;
     if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return QLIN_ERR_SHAPE;
-    if (k > 131072) return QLIN_ERR_SHAPE;  // keeps |acc| (256*acc for int4, 16*acc W4A8) below 2^31
+    // k < 2^17: the accumulator, 256 * acc for W4A4 and 16 * acc for W4A8,
+    // stays below 2^31 in magnitude for any codes (|code| <= 8 int4, 128 int8)
+    if (k >= kMaxGemmK) return QLIN_ERR_SHAPE;
     if (m > 0x7FFFFFFF || n > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))
         return QLIN_ERR_ALIGN;
@@ -223,7 +228,7 @@ qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const voi
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !h || !w_scale || (!x_scale && m > 0)) return QLIN_ERR_NULL;
     if (h_dtype != QLIN_F16 && h_dtype != QLIN_BF16 && h_dtype != QLIN_F32) return QLIN_ERR_DTYPE;
-    if (m < 0 || n2 < 64 || (n2 % 64) != 0 || k < 128 || (k % 128) != 0 || k > 131072) return QLIN_ERR_SHAPE;
+    if (m < 0 || n2 < 64 || (n2 % 64) != 0 || k < 128 || (k % 128) != 0 || k >= kMaxGemmK) return QLIN_ERR_SHAPE;
     if (m > 0x7FFFFFFF || n2 > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(h) || !aligned16(x_scale) || !aligned16(w_scale))
         return QLIN_ERR_ALIGN;

@@ -148,8 +148,8 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
  *   y_dtype  F16, BF16, F32, or I32 (raw accumulators; the scales may then be NULL).
  *   y        out [m][n] contiguous.
  * Preconditions: m >= 0, n >= 1; k a multiple of 64 (w8a8) or of 128 (w4a4),
- * at least one such step; k <= 131072, which keeps every int32 accumulator
- * exact.
+ * at least one such step; k < 131072 (2^17), which keeps every int32
+ * accumulator exact for any codes, -8 and -128 included.
  */
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq,
                            const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
@@ -165,7 +165,7 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
  *   xq:      int8 [m][k] (qlin_rotate_quant_act with bits 8);
  *   wq:      uint8 [n][k/2] packed int4 (qlin_quantize_weights with bits 4);
  *   acc, y, scales, dtypes, stream and errors exactly as qlin_gemm_w4a4.
- * Preconditions: k a multiple of 128, at most 131072; otherwise those of
+ * Preconditions: k a multiple of 128, below 131072; otherwise those of
  * qlin_gemm_w4a4.  May take a split-K workspace from the stream-ordered
  * allocator, as the other GEMMs.
  */
@@ -187,7 +187,7 @@ qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
  *   h[m][c]  = round_{h_dtype}(gelu(g[m][c]) * u[m][c]), c = 0 .. f-1, h
  *            contiguous [m][f]; gelu is the erf form, evaluated in fp32 to
  *            within about one fp32 rounding; h_dtype F16, BF16 or F32.
- * Preconditions: m >= 0; n2 a multiple of 64; k a multiple of 128, at most
+ * Preconditions: m >= 0; n2 a multiple of 64; k a multiple of 128, below
  * 131072.  Errors: NULL pointers (QLIN_ERR_NULL), other dtypes
  * (QLIN_ERR_DTYPE), shapes (QLIN_ERR_SHAPE), pointers not 16-byte aligned
  * (QLIN_ERR_ALIGN), h overlapping an input (QLIN_ERR_ALIAS); m == 0 returns

@@ -111,7 +111,7 @@ def test_quantize_weights_rejects(lib, kw, status):
     (dict(sx=None), q.QLIN_ERR_NULL), (dict(sw=None), q.QLIN_ERR_NULL),
     (dict(ydt=9), q.QLIN_ERR_DTYPE),
     (dict(k=96), q.QLIN_ERR_SHAPE), (dict(k=32), q.QLIN_ERR_SHAPE), (dict(n=0), q.QLIN_ERR_SHAPE),
-    (dict(m=-2), q.QLIN_ERR_SHAPE), (dict(k=131072 + 64), q.QLIN_ERR_SHAPE),
+    (dict(m=-2), q.QLIN_ERR_SHAPE), (dict(k=131072 + 64), q.QLIN_ERR_SHAPE), (dict(k=131072), q.QLIN_ERR_SHAPE),
     (dict(xq=BAD), q.QLIN_ERR_ALIGN), (dict(y=BAD), q.QLIN_ERR_ALIGN), (dict(sw=BAD), q.QLIN_ERR_ALIGN),
     (dict(y=P + 64), q.QLIN_ERR_ALIAS),
 ])
@@ -142,7 +142,7 @@ def test_gemm_raw_i32_needs_no_scales_and_empty_ok(lib):
     (dict(sx=None), q.QLIN_ERR_NULL), (dict(sw=None), q.QLIN_ERR_NULL),
     (dict(hdt=3), q.QLIN_ERR_DTYPE), (dict(hdt=9), q.QLIN_ERR_DTYPE),
     (dict(n2=96), q.QLIN_ERR_SHAPE), (dict(n2=32), q.QLIN_ERR_SHAPE), (dict(k=192), q.QLIN_ERR_SHAPE),
-    (dict(k=64), q.QLIN_ERR_SHAPE), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=131072 + 128), q.QLIN_ERR_SHAPE),
+    (dict(k=64), q.QLIN_ERR_SHAPE), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=131072 + 128), q.QLIN_ERR_SHAPE), (dict(k=131072), q.QLIN_ERR_SHAPE),
     (dict(xq=BAD), q.QLIN_ERR_ALIGN), (dict(h=BAD), q.QLIN_ERR_ALIGN),
     (dict(h=P + 64), q.QLIN_ERR_ALIAS),
 ])

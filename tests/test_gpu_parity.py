@@ -268,6 +268,26 @@ def test_interleave_binding_matches_oracle():
     assert np.array_equal(got, oracle.interleave_gate_up(g.numpy(), u.numpy()))
 
 
+@pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
+def test_gemm_extreme_codes_at_max_k(scheme):
+    """Every code at the most negative value (-8 int4, -128 int8) and the
+    largest k the entry points take (131072 - 128): the largest accumulator
+    magnitudes the kernels can meet, bit-exact."""
+    abits, wbits, fn = SCHEMES[scheme]
+    fn = getattr(q, fn)
+    m, n, k = 3, 96, 131072 - 128
+    def extreme(rows, bits):
+        if bits == 8:
+            return torch.full((rows, k), -128, dtype=torch.int8)
+        return torch.full((rows, k // 2), 0x88, dtype=torch.uint8)   # two -8 nibbles
+    a, b = extreme(m, abits), extreme(n, wbits)
+    b[1] = 0x77 if wbits == 4 else 127                                # a row of +7 / +127
+    acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
+    torch.cuda.synchronize()
+    ref = oracle.int_gemm(codes_np(a, abits), codes_np(b, wbits))
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
+
+
 def test_gemm_deterministic():
     say("gemm determinism")
     a = synth.random_codes(SEED, "Ad", 129, 16384, 8).to(DEV)
