@@ -20,8 +20,11 @@ region is bracketed by HIP events created without a system-scope fence.  value =
 the step (2*M*N*K summed) / step time, in TOPS.  Also reported: the
 batch-1 W4A16 GEMV of a 7B-decoder layer (hidden 4096, MLP 11008) in GB/s
 with distinct weight copies rotated to defeat the 256 MB Infinity Cache, the
-W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape, the
-dominant kernel's roofline fraction, and the CPU oracle on a row sample.
+W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape, one layer
+of the 18-layer backbone sweep at M = 6528 and 52224 (the compute-bound
+regime), the action expert's projections over 10 denoising steps (W4A4 and
+W4A16), the dominant kernel's roofline fraction, and the CPU oracle on a row
+sample.
 
 Prints ONE JSON line.
 """
@@ -59,6 +62,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="GeGLU in the int8 quantizer, not the GEMM epilogue")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sweep-layer and action-expert legs")
     return ap.parse_args()
 
 
@@ -218,6 +222,90 @@ def w4a8_leg(block, steps):
             "note": "back-to-back launches of the GEMM alone (bf16 out)"}
 
 
+def _time_us(fn, reps):
+    """Mean time of fn() over reps calls, between fence-free HIP events."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = HipEvent(stream), HipEvent(stream)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) * 1e3 / reps
+
+
+def sweep_leg(dev, ms=(6528, 52224), reps=3):
+    """One layer of the mixed-precision backbone sweep at batched-observation
+    sizes (the compute-bound regime): q/k/v W4A4, o W8A8, fused gate|up GeGLU
+    W4A4, down W8A8, with every activation quantization; integer GEMM ops of
+    the layer / layer time."""
+    import torch
+
+    from bit_ptq_vla_amd.workload import SweepLayer
+
+    out = {}
+    for m in ms:
+        layer = SweepLayer(dev, m)
+        us = _time_us(layer.step, reps)
+        tops = layer.ops / (us * 1e-6) / 1e12
+        out[f"m{m}"] = {"us_per_layer": round(us, 1), "TOPS": round(tops, 1),
+                        "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "layer_gop": round(layer.ops / 1e9, 1)}
+        del layer
+        torch.cuda.empty_cache()
+    return out
+
+
+def _graph_us(fn, reps):
+    """Mean replay time of a HIP graph that captured fn() (no host launch
+    gaps), or None when fn cannot be captured."""
+    import torch
+
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # noqa: BLE001  (capture support, not a result)
+        log(f"bench: graph capture unavailable ({type(e).__name__}); eager timing used")
+        return None
+    return _time_us(g.replay, reps)
+
+
+def action_expert_leg(dev, reps=5):
+    """The action expert's projections at M = 50 over 10 denoising steps, W4A4
+    (b = 64, with activation quantization) and W4A16 g128 on the same weights;
+    weights stay resident in L2 / Infinity Cache across steps (warm).  The 10
+    steps are replayed from a captured HIP graph: at these sizes eager Python
+    launches (about 10 us each) would hide the kernels."""
+    from bit_ptq_vla_amd.workload import ActionExpert
+
+    ae = ActionExpert(dev)
+    res = {"m": 50, "steps": ae.steps}
+    for name, fn in (("w4a4", ae.run_w4a4), ("w4a16", ae.run_w4a16)):
+        us = _graph_us(fn, reps)
+        mode = "graph replay"
+        if us is None:
+            us, mode = _time_us(fn, reps), "eager launches (host-bound)"
+        us /= ae.steps
+        res[f"{name}_us_per_step"] = round(us, 2)
+        res[f"{name}_timing"] = mode
+        if name == "w4a4":
+            tops = ae.ops_per_step / (us * 1e-6) / 1e12
+            res["w4a4_TOPS"] = round(tops, 2)
+            res["w4a4_frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
+        else:
+            gbs = ae.w4a16_bytes / (us * 1e-6) / 1e9
+            res["w4a16_GB/s"] = round(gbs, 1)
+            res["w4a16_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+    res["note"] = "latency-bound (six projections of at most 4096 x 1024 per step); weights warm"
+    return res
+
+
 def cpu_baseline(block, rows):
     """The oracle as it stands on a row sample of the same step (single
     thread: NumPy's int64 matmul does not use BLAS; BLAS is pinned to one
@@ -300,6 +388,11 @@ def main():
     }
     log("bench: W4A8 GEMM leg")
     out["w4a8"] = w4a8_leg(block, args.steps)
+    if not args.no_sweep:
+        log("bench: backbone sweep layer leg (M = 6528, 52224)")
+        out["sweep_layer"] = sweep_leg(dev)
+        log("bench: action expert leg (M = 50, 10 steps)")
+        out["action_expert"] = action_expert_leg(dev)
     if not args.no_gemv:
         log("bench: batch-1 W4A16 GEMV leg")
         out["gemv"] = gemv_leg(dev)

@@ -79,3 +79,126 @@ class MlpBlock:
             q.qlin_rotate_quant_act(self.y1, k=self.dn.k, fold_inv_s=self.inv2, had_block=128, bits=8,
                                     pre=q.QLIN_PRE_GEGLU, out=(self.hq, self.hs))
         q.qlin_gemm_w8a8(self.hq, self.hs, self.wq2, self.ws2, self.dn.k, out=self.y2)
+
+
+class SweepLayer:
+    """One layer of the mixed-precision backbone sweep (hidden 2048, MLP 16384)
+    at M tokens: q, k, v W4A4 from one int4 quantization of the attention input,
+    o W8A8 from the attention output, the fused gate|up GeGLU GEMM (W4A4) from
+    the MLP input, then h -> int8 -> down W8A8; Hadamard block 128, bf16 out.
+    Inputs are synthetic (one tensor each for the attention input, the
+    attention output and the MLP input); weights are quantized once."""
+
+    def __init__(self, dev, m: int):
+        import torch
+
+        import bit_ptq_vla_amd as q
+        from bit_ptq_vla_amd import synth
+
+        self.q = q
+        self.m = m
+        wl = synth.CFG5
+        p = {pr.name: pr for pr in wl.projs}
+        self.p = p
+        f = p["down"].k
+        bf = torch.bfloat16
+
+        def act(name, tag):
+            return synth.activation(wl, p[name], m, tag=tag).to(dev)
+
+        def quant_w(name, x, bits, interleave=False):
+            w = synth.weight(wl, p[name], tag="/L0").to(dev)
+            if interleave:
+                w = q.interleave_gate_up(w[:f], w[f:])
+            s, inv = q.qlin_calibrate_fold(x, w)
+            wq, ws = q.qlin_quantize_weights(w, fold_s=s, had_block=128, bits=bits)
+            return s, inv, wq, ws
+
+        self.x_attn = act("q", "/sweep_attn")
+        self.x_o = act("o", "/sweep_o")
+        self.x_mlp = act("gate_up", "/sweep_mlp")
+        # q, k, v share the attention input and its fold (calibrated on q's weights)
+        s_qkv, self.inv_qkv, self.wq_q, self.ws_q = quant_w("q", self.x_attn, 4)
+        wk = synth.weight(wl, p["k"], tag="/L0").to(dev)
+        wv = synth.weight(wl, p["v"], tag="/L0").to(dev)
+        self.wq_k, self.ws_k = q.qlin_quantize_weights(wk, fold_s=s_qkv, had_block=128, bits=4)
+        self.wq_v, self.ws_v = q.qlin_quantize_weights(wv, fold_s=s_qkv, had_block=128, bits=4)
+        del wk, wv
+        _, self.inv_o, self.wq_o, self.ws_o = quant_w("o", self.x_o, 8)
+        _, self.inv_gu, self.wq_gu, self.ws_gu = quant_w("gate_up", self.x_mlp, 4, interleave=True)
+        self.xq4 = torch.empty((m, 1024), dtype=torch.uint8, device=dev)
+        self.xs4 = torch.empty(m, dtype=torch.float32, device=dev)
+        self.xq8 = torch.empty((m, 2048), dtype=torch.int8, device=dev)
+        self.xs8 = torch.empty(m, dtype=torch.float32, device=dev)
+        self.h = torch.empty((m, f), dtype=bf, device=dev)
+        self.hq = torch.empty((m, f), dtype=torch.int8, device=dev)
+        self.hs = torch.empty(m, dtype=torch.float32, device=dev)
+        self.y = {n: torch.empty((m, p[n].n), dtype=bf, device=dev) for n in ("q", "k", "v", "o", "down")}
+        q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))
+        q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, self.wq_gu, self.ws_gu, 2048, out=self.h)
+        wdn = synth.weight(wl, p["down"], tag="/L0").to(dev)
+        s2, self.inv_dn = q.qlin_calibrate_fold(self.h, wdn)
+        self.wq_dn, self.ws_dn = q.qlin_quantize_weights(wdn, fold_s=s2, had_block=128, bits=8)
+        del wdn
+        self.ops = 2 * m * sum(p[n].n * p[n].k for n in ("q", "k", "v", "o", "gate_up", "down"))
+
+    def step(self):
+        q = self.q
+        q.qlin_rotate_quant_act(self.x_attn, fold_inv_s=self.inv_qkv, had_block=128, bits=4,
+                                out=(self.xq4, self.xs4))
+        for n, wq, ws in (("q", self.wq_q, self.ws_q), ("k", self.wq_k, self.ws_k), ("v", self.wq_v, self.ws_v)):
+            q.qlin_gemm_w4a4(self.xq4, self.xs4, wq, ws, 2048, out=self.y[n])
+        q.qlin_rotate_quant_act(self.x_o, fold_inv_s=self.inv_o, had_block=128, bits=8, out=(self.xq8, self.xs8))
+        q.qlin_gemm_w8a8(self.xq8, self.xs8, self.wq_o, self.ws_o, 2048, out=self.y["o"])
+        q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))
+        q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, self.wq_gu, self.ws_gu, 2048, out=self.h)
+        q.qlin_rotate_quant_act(self.h, fold_inv_s=self.inv_dn, had_block=128, bits=8, out=(self.hq, self.hs))
+        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq_dn, self.ws_dn, 16384, out=self.y["down"])
+
+
+class ActionExpert:
+    """The action expert's six projections at M = 50 (width 1024, MLP 4096):
+    W4A4 with Hadamard block 64 (fold calibrated on the step-0 inputs) and
+    W4A16 g128 on the same weights; inputs drift with the denoising step."""
+
+    def __init__(self, dev, steps: int = 10):
+        import torch
+
+        import bit_ptq_vla_amd as q
+        from bit_ptq_vla_amd import synth
+
+        self.q = q
+        wl = synth.CFG3
+        self.projs = wl.projs
+        self.steps = steps
+        self.w4a4, self.w4a16 = [], []
+        for pr in wl.projs:
+            w = synth.weight(wl, pr).to(dev)
+            x0 = synth.activation(wl, pr, 50, tag="/t0", std=synth.cfg3_sigma(0)).to(dev)
+            s, inv = q.qlin_calibrate_fold(x0, w)
+            wq, ws = q.qlin_quantize_weights(w, fold_s=s, had_block=64, bits=4)
+            wq16, ws16 = q.qlin_quantize_weights(w, bits=4, group=128)
+            xs = [synth.activation(wl, pr, 50, tag=f"/t{t}", std=synth.cfg3_sigma(t)).to(dev)
+                  for t in range(steps)]
+            xq = torch.empty((50, pr.k // 2), dtype=torch.uint8, device=dev)
+            xsc = torch.empty(50, dtype=torch.float32, device=dev)
+            y = torch.empty((50, pr.n), dtype=torch.float16, device=dev)
+            self.w4a4.append((pr, xs, inv, wq, ws, xq, xsc, y))
+            self.w4a16.append((pr, xs, wq16, ws16, y))
+        self.ops_per_step = 2 * 50 * sum(pr.n * pr.k for pr in wl.projs)
+        self.w4a16_bytes = sum(pr.n * pr.k // 2 + pr.n * (pr.k // 128) * 2 + 2 * 50 * pr.k + 2 * 50 * pr.n
+                               for pr in wl.projs)
+
+    def run_w4a4(self):
+        q = self.q
+        for t in range(self.steps):
+            for pr, xs, inv, wq, ws, xq, xsc, y in self.w4a4:
+                q.qlin_rotate_quant_act(xs[t], fold_inv_s=inv, had_block=64, bits=4, out=(xq, xsc))
+                q.qlin_gemm_w4a4(xq, xsc, wq, ws, pr.k, out=y)
+
+    def run_w4a16(self):
+        q = self.q
+        for t in range(self.steps):
+            for pr, xs, wq16, ws16, y in self.w4a16:
+                q.qlin_gemv_w4a16(xs[t], wq16, ws16, out=y)
+
