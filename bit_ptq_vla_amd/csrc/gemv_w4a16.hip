@@ -1,8 +1,9 @@
-// Weight-only int4 projection for small batches (W4A16, group-128 fp16
-// scales), for gfx950.  The LoopQ abstract places this case at batch 1 in
-// the memory-bound action expert; the packed weights dominate the traffic, so
-// the kernel streams them from HBM once with 16-byte coalesced loads and has
-// every load of a wave in flight at once.
+// Weight-only int4 projection for one to three token rows (W4A16, group-128
+// fp16 scales), for gfx950; more rows go to the matrix-core kernel.  The
+// LoopQ abstract places this case at batch 1 in the memory-bound action
+// expert; the packed weights dominate the traffic, so the kernel streams them
+// from HBM once with 16-byte coalesced loads and has every load of a wave in
+// flight at once.
 //
 //   y[m][n] = fp16( sum_g s16[n][g] * sum_{k in g} x[m][k] * code[n][k] )
 //
@@ -248,14 +249,12 @@ hipError_t launch_g(const void* x, const void* wq, const void* ws, int64_t m, in
 template <int R, int CH>
 hipError_t launch_mt(const void* x, const void* wq, const void* ws, int64_t m, int64_t n, int64_t k,
                      void* y, hipStream_t st) {
-    // token rows per pass: as many as m needs, at most 8, with MT * k * 2 within the LDS budget
-    // (k > (CH / 2) * 2048 bounds MT from above, so larger MT are never built)
-    constexpr int kMaxMt = CH <= 2 ? 8 : CH <= 4 ? 4 : CH <= 8 ? 2 : 1;
+    // token rows per pass: as many as m (at most 3 here) needs, at most 4, with MT * k * 2
+    // within the LDS budget (k > (CH / 2) * 2048 bounds MT from above, so larger MT are
+    // never built)
+    constexpr int kMaxMt = CH <= 4 ? 4 : CH <= 8 ? 2 : 1;
     int mt = 1;
     while (mt < kMaxMt && mt < m && gemv_lds_bytes(2 * mt, R, k) <= kGemvLdsBytes) mt *= 2;
-    if constexpr (kMaxMt >= 8) {
-        if (mt == 8) return launch_g<R, CH, 8>(x, wq, ws, m, n, k, y, st);
-    }
     if constexpr (kMaxMt >= 4) {
         if (mt == 4) return launch_g<R, CH, 4>(x, wq, ws, m, n, k, y, st);
     }
@@ -281,6 +280,10 @@ hipError_t launch_ch(const void* x, const void* wq, const void* ws, int64_t m, i
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st) {
     (void)group;  // 128, checked by the caller
+    // from four token rows on, the matrix-core kernel (each weight decoded once
+    // for all rows) is faster than the vector dot products here (measured at
+    // n, k = 1024 and 4096)
+    if (m > 3) return launch_skinny_w4a16(x, wq, w_scale, m, n, k, y, st);
     const int64_t chunks = k / 32;
     const int64_t ch = (chunks + 63) / 64;   // chunk slots per lane
     if (ch <= 1) return launch_ch<1>(x, wq, w_scale, m, n, k, y, st);

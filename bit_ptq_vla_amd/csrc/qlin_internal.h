@@ -46,4 +46,8 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st);
 
+// The same projection on the matrix cores, for 8 < m; group 128.
+hipError_t launch_skinny_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
+                               int64_t n, int64_t k, void* y, hipStream_t st);
+
 }  // namespace qlin

@@ -307,7 +307,13 @@ GEMV_CASES = [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (3, 520, 1024
               # every chunk-slot count (k up to 32768), token-row pass size and rows-per-wave choice,
               # ragged n and m
               (1, 300, 128), (2, 77, 32768), (5, 130, 20480), (9, 333, 16384), (4, 250, 12288),
-              (8, 8200, 2048), (1, 9000, 5120), (64, 40, 1024), (50, 1030, 4096)]
+              (8, 8200, 2048), (1, 9000, 5120), (64, 40, 1024), (50, 1030, 4096),
+              # from four rows on the matrix-core kernel: one to four 16-row tiles, one group
+              # per k slice or several (odd counts, 1 to 32 per slice), idle slices (k = 128, 384),
+              # row tiles of 4..16 valid rows
+              (50, 1024, 1024), (33, 4096, 1024), (47, 520, 128), (12, 200, 384), (16, 1000, 1664),
+              (64, 100, 32768), (25, 96, 2560), (49, 17, 1152), (4, 1024, 4096), (7, 4096, 1024),
+              (3, 4096, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMV_CASES)
@@ -322,16 +328,19 @@ def test_gemv_w4a16_parity(m, n, k):
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
 
 
-def test_gemv_w4a16_subnormal_and_large_x():
-    # fp16 subnormal, zero and near-maximum activations (the kernel folds a
-    # per-chunk sum of x into its accumulation, which must see the same values)
-    say("gemv subnormal/large x")
-    m, n, k = 2, 520, 4096
+@pytest.mark.parametrize("m", [2, 20])
+def test_gemv_w4a16_subnormal_and_large_x(m):
+    # fp16 subnormal, zero and near-maximum activations (the vector kernel folds a
+    # per-chunk sum of x into its accumulation, which must see the same values;
+    # at 20 rows the matrix cores take them as operands)
+    say(f"gemv subnormal/large x m={m}")
+    n, k = 520, 4096
     x = synth.normal_tensor(SEED, "gx/sub", (m, k), dtype="f16")
     x[0, ::3] = torch.tensor(3.0e-6, dtype=torch.float16)     # subnormal
     x[0, 1::7] = 0
     x[1, ::5] = torch.tensor(-2.0e3, dtype=torch.float16)     # large
     x[1, 0], x[1, k - 1] = 6.0e4, -6.0e4                        # near the fp16 maximum
+    x[m - 1, 2::9] = torch.tensor(-6.1e-5, dtype=torch.float16)  # smallest normals
     w = synth.normal_tensor(SEED, "gw/sub", (n, k), std=0.015, dtype="f16")
     wq, ws = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
     y = q.qlin_gemv_w4a16(x.to(DEV), wq, ws)
@@ -339,6 +348,19 @@ def test_gemv_w4a16_subnormal_and_large_x():
     y32, y_ref = oracle.gemv_w4a16(synth.to_f64(x), codes_np(wq, 4), ws.cpu().numpy(), 128)
     for i in range(m):  # each row on its own scale
         assert_ok(oracle.compare_outputs(f64(y)[i:i + 1], y_ref[i:i + 1]), f"output row {i}")
+
+
+@pytest.mark.parametrize("m,n,k", [(50, 1024, 4096), (9, 300, 1024)])
+def test_gemv_w4a16_repeatable(m, n, k):
+    # the k slices' partial tiles are added in a fixed order: two calls agree bit for bit
+    say(f"gemv repeat {m}x{n}x{k}")
+    x = synth.normal_tensor(SEED, f"gx/{m}/{k}", (m, k), dtype="f16").to(DEV)
+    w = synth.normal_tensor(SEED, f"gw/{n}/{k}", (n, k), std=0.015, dtype="f16")
+    wq, ws = q.qlin_quantize_weights(w.to(DEV), bits=4, group=128)
+    y1 = q.qlin_gemv_w4a16(x, wq, ws)
+    y2 = q.qlin_gemv_w4a16(x, wq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 # ---------------------------------------------------------------- fold calibration
