@@ -41,8 +41,13 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// float -> fp16 bits, round half to even, of the fp32 value f as given: the
+// empty asm keeps the compiler from folding the multiply that produced f into
+// the conversion (v_fma_mix rounds the unrounded product once, which can
+// differ from rounding the fp32 product).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
-    _Float16 h = static_cast<_Float16>(f);  // v_cvt_f16_f32, round to nearest even
+    asm("" : "+v"(f));
+    _Float16 h = static_cast<_Float16>(f);  // v_cvt_f16_f32
     return __builtin_bit_cast(uint16_t, h);
 }
 

@@ -103,8 +103,10 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     if (m == 0) return QLIN_OK;
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
-    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8);
     hipStream_t s = as_stream(stream);
+    if (m <= qlin::kSkinnyIntMaxM)
+        return map_err(qlin::launch_skinny_int(xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, s));
+    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8);
     int32_t* ws = nullptr;
     if (plan.ws_bytes > 0) {
         if (hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.ws_bytes), s) != hipSuccess)

@@ -46,8 +46,15 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st);
 
-// The same projection on the matrix cores, for 8 < m; group 128.
+// The same projection on the matrix cores, for 3 < m <= 64; group 128.
 hipError_t launch_skinny_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                                int64_t n, int64_t k, void* y, hipStream_t st);
+
+// Integer projection (W4A4 / W8A8 / W4A8 as int4, a8 select) for m <= 64:
+// 16-column blocks, k split over eight waves; same results as launch_gemm.
+constexpr int64_t kSkinnyIntMaxM = 64;
+hipError_t launch_skinny_int(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
+                             int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y, int y_dtype,
+                             hipStream_t st);
 
 }  // namespace qlin

@@ -144,15 +144,22 @@ def test_quantize_weights_group128_parity(n, k, dtype):
 # ---------------------------------------------------------------- integer GEMM
 
 GEMM_SHAPES = [
+    # up to 64 rows: the 16-column kernel (one to four 16-row tiles, k over eight waves)
     (16, 512, 512),      # single linear
-    (300, 520, 1024),    # ragged M and N tiles
     (50, 1024, 4096),
-    (64, 256, 16384),    # split-K
-    (1, 96, 128),        # one token
-    (257, 256, 2048),
+    (64, 256, 16384),
+    (1, 96, 128),        # one token, fewer k pieces than waves
     (33, 64, 192),       # k % 128 == 64: w8a8 only (w4a4 needs k % 128 == 0)
-    (40, 100, 4096),     # split-K, n % 8 == 4: four outputs per reduce lane
-    (17, 99, 2048),      # split-K, odd n: one output per reduce lane
+    (40, 100, 4096),
+    (17, 99, 2048),      # odd n: ragged last column strip
+    (5, 1000, 1024),
+    (50, 4096, 1024),
+    # more rows: the large-tile GEMM
+    (300, 520, 1024),    # ragged M and N tiles
+    (257, 256, 2048),    # split-K
+    (80, 100, 4096),     # split-K, n % 8 == 4: four outputs per reduce lane
+    (70, 99, 2048),      # split-K, odd n: one output per reduce lane
+    (65, 256, 16384),    # split-K
 ]
 
 
@@ -224,7 +231,8 @@ def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
                                           ("w8a8", 64, 256, 16384), ("w4a4", 16, 512, 512),
                                           ("w8a8", 40, 100, 4096), ("w4a4", 17, 99, 2048),
                                           ("w4a8", 300, 520, 1024), ("w4a8", 64, 256, 16384),
-                                          ("w4a8", 17, 99, 2048)])
+                                          ("w4a8", 17, 99, 2048), ("w4a4", 50, 1024, 1024),
+                                          ("w8a8", 80, 100, 4096), ("w4a8", 9, 1000, 1024)])
 def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     say(f"gemm {out} {scheme} {m}x{n}x{k}")
     a, b, abits, wbits, fn = scheme_codes(scheme, "e", m, n, k)
@@ -268,14 +276,16 @@ def test_interleave_binding_matches_oracle():
     assert np.array_equal(got, oracle.interleave_gate_up(g.numpy(), u.numpy()))
 
 
+@pytest.mark.parametrize("m", [3, 65])
 @pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
-def test_gemm_extreme_codes_at_max_k(scheme):
+def test_gemm_extreme_codes_at_max_k(scheme, m):
     """Every code at the most negative value (-8 int4, -128 int8) and the
     largest k the entry points take (131072 - 128): the largest accumulator
-    magnitudes the kernels can meet, bit-exact."""
+    magnitudes the kernels can meet, bit-exact (3 rows: the 16-column kernel;
+    65: the large-tile GEMM)."""
     abits, wbits, fn = SCHEMES[scheme]
     fn = getattr(q, fn)
-    m, n, k = 3, 96, 131072 - 128
+    n, k = 96, 131072 - 128
     def extreme(rows, bits):
         if bits == 8:
             return torch.full((rows, k), -128, dtype=torch.int8)
@@ -286,6 +296,25 @@ def test_gemm_extreme_codes_at_max_k(scheme):
     torch.cuda.synchronize()
     ref = oracle.int_gemm(codes_np(a, abits), codes_np(b, wbits))
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
+def test_gemm_small_m_matches_large_tile_epilogue(scheme):
+    """Rows 0..63 computed alone (16-column kernel) equal the same rows of a
+    129-row call (large-tile GEMM) bit for bit: the two share the epilogue
+    arithmetic, float(acc) * s_x * (s_w * 2^-shift)."""
+    say(f"gemm small-m vs large-tile {scheme}")
+    m, n, k = 129, 520, 2048
+    a, b, abits, wbits, fn = scheme_codes(scheme, "cmp", m, n, k)
+    sx = synth.random_scales(SEED, f"sxc/{m}", m).to(DEV)
+    sw = synth.random_scales(SEED, f"swc/{n}", n).to(DEV)
+    a, b = a.to(DEV), b.to(DEV)
+    for dt in (torch.float16, torch.bfloat16, torch.float32):
+        big = fn(a, sx, b, sw, k, y_dtype=dt)
+        small = fn(a[:64].contiguous(), sx[:64].contiguous(), b, sw, k, y_dtype=dt)
+        torch.cuda.synchronize()
+        bits = torch.int32 if dt == torch.float32 else torch.int16
+        assert torch.equal(big[:64].contiguous().view(bits), small.view(bits)), str(dt)
 
 
 def test_gemm_deterministic():
