@@ -18,6 +18,10 @@ Blocchi"; LoopQ abstract for plain RTN weights and the W4A16 weight-only form):
                   from the bf16-rounded dequantized g, u (the fused form of the
                   backbone MLP's gated GeLU)
   W4A16 GEMV      f64 dot products against q * s16[group]
+  per-step table  (Omega-QVLA "Scalatura delle Attivazioni DiT per Passo")
+                  s_t[c] = max |rotated calibration activations| / qmax per
+                  step; static codes v / s_t[c]; s_t folded into that step's
+                  weights before their RTN
 
 Floating point is float64 throughout, integers are int64.  Every function is
 pinned by tests that do not re-use its own formula (closed forms, brute force,
@@ -38,6 +42,9 @@ from .qlin_ref import (  # noqa: F401
     geglu,
     rotate_quant_act,
     quantize_weights,
+    calibrate_step_scales,
+    rotate_quant_act_static,
+    quantize_weights_step,
     int_gemm,
     dequant_epilogue,
     gemm,

@@ -16,6 +16,11 @@ Sources (page title, section):
         batch 1; memory-bound action expert).
   [QV]  QuantVLA technical summary -- Methodology B/C (per-head and per-layer
         scalars folded into the dequantization scale, no extra runtime op).
+  [OS]  Omega-QVLA technical summary -- Metodologia 2, "Scalatura delle
+        Attivazioni DiT per Passo" (a precomputed scale table per denoising
+        step, per layer and per channel, derived from calibration
+        trajectories and looked up at inference in place of a single static
+        scale).
 
 Readings where the pages leave a step open are stated at each function.
 """
@@ -266,6 +271,64 @@ def quantize_weights(w, fold_s, had_block: int, bits: int, group: int = 0):
         w = w * np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
     w = rotate_blocks(w, had_block)
     return quantize_rows(w, bits)
+
+
+# --------------------------------------------------------------------------
+# Per-step static activation scales  [OS] Metodologia 2
+#
+# Reading (the page gives no formula): the table entry of a (step, layer)
+# pair is one scale per input channel of the projection, in the channel
+# space where activations are quantized (after the fold and the block
+# Hadamard), set RTN-style from the calibration tokens of that step:
+#     s_t[c] = float32( max_m |v_t[m, c]| / qmax ).
+# At inference the activation codes take it in place of the per-token
+# dynamic scale:  q[m, c] = clamp(rne(v[m, c] / s_t[c]), -qmax, qmax)
+# (code 0 where s_t[c] = 0).  A per-channel scale cannot be pulled out of the
+# integer dot product, so it is folded into that step's weights before their
+# per-output-channel RTN:  w_t = RTN_rows( rotate(w * s) * s_t ).  Then
+#     s_w_t[n] * sum_c q[m, c] qw_t[n, c]  ~  sum_c (v[m, c] / s_t[c]) (w_rot[n, c] s_t[c])
+# = x w^T, with the activation scale 1 in the GEMM's epilogue.  One weight
+# copy per step is the cost.
+# --------------------------------------------------------------------------
+
+
+def _rotated(x, fold_s, had_block: int, fold_op: str) -> np.ndarray:
+    v = np.asarray(x, dtype=np.float64)
+    if fold_s is not None:
+        f = np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
+        v = v / f if fold_op == "div" else v * f
+    return rotate_blocks(v, had_block)
+
+
+def calibrate_step_scales(x_cal, fold_s, had_block: int, bits: int) -> np.ndarray:
+    """Table row s_t[c] (float32 [K]) from the calibration tokens x_cal
+    [M][K] of one denoising step: the activation path up to the rotation
+    (x / s, block Hadamard), then float32(max_m |v[m, c]| / qmax)."""
+    v = _rotated(x_cal, fold_s, had_block, "div")
+    return (np.max(np.abs(v), axis=0) / qmax_of(bits)).astype(np.float32)
+
+
+def rotate_quant_act_static(x, fold_s, had_block: int, bits: int, step_scale):
+    """Activation codes at one step with its static per-channel scales:
+    v = rotate(x / s); r = v / float64(s_t[c]); q = clamp(rne(r), +-qmax);
+    channels with s_t[c] = 0 give code 0.  Returns (q int64 [M][K], r)."""
+    qmax = qmax_of(bits)
+    v = _rotated(x, fold_s, had_block, "div")
+    st = np.asarray(step_scale, dtype=np.float32).astype(np.float64)
+    r = np.zeros_like(v)
+    nz = st > 0
+    r[:, nz] = v[:, nz] / st[None, nz]
+    q = np.clip(np.rint(r), -qmax, qmax).astype(np.int64)
+    return q, r
+
+
+def quantize_weights_step(w, fold_s, had_block: int, bits: int, step_scale):
+    """One step's weights: rotate(w * s) with column c multiplied by s_t[c]
+    (float32 value, product in float64), then per-output-channel symmetric
+    RTN.  Returns (q int64 [N][K], scale float32 [N], r)."""
+    v = _rotated(w, fold_s, had_block, "mul")
+    v = v * np.asarray(step_scale, dtype=np.float32).astype(np.float64)[None, :]
+    return quantize_rows(v, bits)
 
 
 def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
