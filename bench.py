@@ -278,15 +278,18 @@ def _graph_us(fn, reps):
 
 def action_expert_leg(dev, reps=5):
     """The action expert's projections at M = 50 over 10 denoising steps, W4A4
-    (b = 64, with activation quantization) and W4A16 g128 on the same weights;
-    weights stay resident in L2 / Infinity Cache across steps (warm).  The 10
-    steps are replayed from a captured HIP graph: at these sizes eager Python
-    launches (about 10 us each) would hide the kernels."""
+    (b = 64, with activation quantization), W4A4 with per-step static
+    activation tables (one table and one weight copy per step), and W4A16
+    g128 on the same weights; weights stay resident in L2 / Infinity Cache
+    across steps (warm).  The 10 steps are replayed from a captured HIP graph:
+    at these sizes eager Python launches (about 10 us each) would hide the
+    kernels."""
     from bit_ptq_vla_amd.workload import ActionExpert
 
     ae = ActionExpert(dev)
+    ae.build_static()
     res = {"m": 50, "steps": ae.steps}
-    for name, fn in (("w4a4", ae.run_w4a4), ("w4a16", ae.run_w4a16)):
+    for name, fn in (("w4a4", ae.run_w4a4), ("w4a4_static", ae.run_w4a4_static), ("w4a16", ae.run_w4a16)):
         us = _graph_us(fn, reps)
         mode = "graph replay"
         if us is None:
@@ -294,10 +297,10 @@ def action_expert_leg(dev, reps=5):
         us /= ae.steps
         res[f"{name}_us_per_step"] = round(us, 2)
         res[f"{name}_timing"] = mode
-        if name == "w4a4":
+        if name.startswith("w4a4"):
             tops = ae.ops_per_step / (us * 1e-6) / 1e12
-            res["w4a4_TOPS"] = round(tops, 2)
-            res["w4a4_frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
+            res[f"{name}_TOPS"] = round(tops, 2)
+            res[f"{name}_frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
         else:
             gbs = ae.w4a16_bytes / (us * 1e-6) / 1e9
             res["w4a16_GB/s"] = round(gbs, 1)

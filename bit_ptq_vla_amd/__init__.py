@@ -50,6 +50,9 @@ SIGNATURES = {
     "qlin_gemm_w4a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
+    "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
+    "qlin_rotate_quant_act_static": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P],
+    "qlin_quantize_weights_step": [_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P],
 }
 
 _lib = None
@@ -179,6 +182,71 @@ def qlin_rotate_quant_act(x: torch.Tensor, k: Optional[int] = None, fold_inv_s: 
                                    _stream(x.device))
     _check(st, "qlin_rotate_quant_act")
     return xq, xs
+
+
+def _rows_arg(x: torch.Tensor, k: Optional[int]) -> int:
+    _dev_tensor(x, "x")
+    if k is None:
+        k = x.shape[1]
+    if x.dim() != 2 or x.stride(1) != 1 or k > x.shape[1]:
+        raise ValueError("x must be a row-major [m][>= k] tensor")
+    return k
+
+
+def qlin_calibrate_step_scales(x: torch.Tensor, k: Optional[int] = None,
+                               fold_inv_s: Optional[torch.Tensor] = None, had_block: int = 0,
+                               bits: int = 4, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One row of the per-step static scale table (float32 [k]) from the
+    calibration tokens x [m][ldx] of one denoising step."""
+    lib = load()
+    k = _rows_arg(x, k)
+    table = out if out is not None else torch.empty(k, dtype=torch.float32, device=x.device)
+    _need(table, k * 4, "table")
+    _need(fold_inv_s, k * 4, "fold_inv_s")
+    st = lib.qlin_calibrate_step_scales(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], x.shape[0], k, x.stride(0),
+                                        _ptr(fold_inv_s), had_block, bits, table.data_ptr(), _stream(x.device))
+    _check(st, "qlin_calibrate_step_scales")
+    return table
+
+
+def qlin_rotate_quant_act_static(x: torch.Tensor, table: torch.Tensor, k: Optional[int] = None,
+                                 fold_inv_s: Optional[torch.Tensor] = None, had_block: int = 0,
+                                 bits: int = 4, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Activation codes of x [m][ldx] with one step's static per-channel
+    scales (no per-row scale: the GEMM takes x_scale = 1)."""
+    lib = load()
+    k = _rows_arg(x, k)
+    m = x.shape[0]
+    xq = out if out is not None else torch.empty((m, k // 2) if bits == 4 else (m, k),
+                                                 dtype=torch.uint8 if bits == 4 else torch.int8,
+                                                 device=x.device)
+    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    _need(table, k * 4, "table")
+    _need(fold_inv_s, k * 4, "fold_inv_s")
+    st = lib.qlin_rotate_quant_act_static(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0),
+                                          _ptr(fold_inv_s), had_block, bits, table.data_ptr(), xq.data_ptr(),
+                                          _stream(x.device))
+    _check(st, "qlin_rotate_quant_act_static")
+    return xq
+
+
+def qlin_quantize_weights_step(w: torch.Tensor, table: torch.Tensor, fold_s: Optional[torch.Tensor] = None,
+                               had_block: int = 0, bits: int = 4) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One step's weights w [n][k] with that step's table folded in: codes
+    and float32 [n] scales."""
+    lib = load()
+    _dev_tensor(w, "w")
+    n, k = w.shape
+    _need(w, n * k * w.element_size(), "w")
+    _need(table, k * 4, "table")
+    _need(fold_s, k * 4, "fold_s")
+    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
+                     device=w.device)
+    ws = torch.empty(n, dtype=torch.float32, device=w.device)
+    st = lib.qlin_quantize_weights_step(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
+                                        bits, table.data_ptr(), wq.data_ptr(), ws.data_ptr(), _stream(w.device))
+    _check(st, "qlin_quantize_weights_step")
+    return wq, ws
 
 
 def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):

@@ -55,9 +55,20 @@ struct RowQuantParams {
     int nch;            // chunk passes actually used (<= NCH)
     int had_block;      // 0/1: none
     int bits;           // 4 or 8
-    void* q;            // codes out
-    float* scale;       // per-row scale out
+    void* q;            // codes out (column maxima as float bits in ROWQ_COLMAX)
+    float* scale;       // per-row scale out (unused in ROWQ_STATIC and ROWQ_COLMAX)
+    const float* post;  // per-channel table after the rotation (ROWQ_STATIC, ROWQ_POSTMUL)
 };
+
+// What the row kernel does after the fold and the rotation:
+//   ROWQ_DYNAMIC  per-row amax scale and codes (the per-token / RTN quantizer);
+//   ROWQ_STATIC   codes v / post[c] with a static per-channel scale table, no
+//                 per-row scale (Omega-QVLA per-step activation table);
+//   ROWQ_POSTMUL  v * post[c], then as ROWQ_DYNAMIC (weights of one step with
+//                 its table folded in);
+//   ROWQ_COLMAX   max over rows of |v| per column, as float bits (atomic max)
+//                 into q (the table's calibration).
+enum RowQuantMode { ROWQ_DYNAMIC = 0, ROWQ_STATIC = 1, ROWQ_POSTMUL = 2, ROWQ_COLMAX = 3 };
 
 // Cross-lane butterfly stages.  The true transform value t is carried as
 // w = sigma * t with a per-lane sign sigma.  At lane distance D the pair
@@ -254,8 +265,9 @@ __device__ __forceinline__ uint32_t pack8_i4(const uint32_t cb[8]) {
 // loaded once.  No load sits
 // behind a branch: rows past the end read the last row and columns past k
 // read column 0, and their values are replaced by zeros afterwards.
-template <int DT, int NCH, bool GEGLU, int TPB>
+template <int DT, int NCH, bool GEGLU, int TPB, int MODE = ROWQ_DYNAMIC>
 __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p) {
+    static_assert(MODE == ROWQ_DYNAMIC || !GEGLU, "table modes take plain rows");
     constexpr int NW = TPB / 64;
     __shared__ float red[2][NW];
     constexpr bool LUT = GEGLU && DT == BF16;
@@ -298,6 +310,17 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
         }
         mlt[c][0] = m0.x; mlt[c][1] = m0.y; mlt[c][2] = m0.z; mlt[c][3] = m0.w;
         mlt[c][4] = m1.x; mlt[c][5] = m1.y; mlt[c][6] = m1.z; mlt[c][7] = m1.w;
+    }
+    constexpr bool HAS_POST = (MODE == ROWQ_STATIC || MODE == ROWQ_POSTMUL);
+    float pst[HAS_POST ? NCH : 1][8];
+    if constexpr (HAS_POST) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const float4* pp = reinterpret_cast<const float4*>(p.post + col_ld[c]);
+            const float4 a0 = pp[0], a1 = pp[1];
+            pst[c][0] = a0.x; pst[c][1] = a0.y; pst[c][2] = a0.z; pst[c][3] = a0.w;
+            pst[c][4] = a1.x; pst[c][5] = a1.y; pst[c][6] = a1.z; pst[c][7] = a1.w;
+        }
     }
     // fp32 of 1/sqrt(b), correctly rounded (exact for b = 4^j)
     const float nrm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
@@ -356,9 +379,31 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
         if (b > 64) xlane_stage<8, NCH>(v, lane);
         if (b > 128) xlane_stage<16, NCH>(v, lane);
 
+        if constexpr (MODE == ROWQ_POSTMUL) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[c][e] *= pst[c][e];
+        }
+        if constexpr (MODE == ROWQ_COLMAX) {
+            // |v| * nrm is the rotated value's magnitude; float bits of
+            // non-negative values order like unsigned integers
+            if (row < p.m) {
+                uint32_t* cm = static_cast<uint32_t*>(p.q);
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    if (!col_ok[c]) continue;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        atomicMax(cm + col_ld[c] + e, __float_as_uint(fabsf(v[c][e]) * nrm));
+                }
+            }
+        }
+
         // row maximum: lanes, then the row's waves through LDS (two slots
         // alternate between iterations, so one barrier per group suffices)
         float amax = 0.f;
+        if constexpr (MODE == ROWQ_DYNAMIC || MODE == ROWQ_POSTMUL) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -372,8 +417,47 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
             amax = red[parity][first];
             for (int i = 1; i < wpr; ++i) amax = fmaxf(amax, red[parity][first + i]);
         }
+        }
 
-        if (row < p.m) {
+        if (MODE == ROWQ_STATIC && row < p.m) {
+            // codes rne(t / post[c]) with t = sigma * nrm * v: the fp32 product
+            // with sigma * nrm / post[c], redone on float64 quotients near a
+            // half-integer; a zero table entry gives code 0
+            constexpr float M = 12582912.f;
+            const double sqb = sqrt(static_cast<double>(b));
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (!col_ok[c]) continue;
+                const int64_t col = col_ld[c];
+                float qb[8], mulc[8];
+                float worst = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    mulc[e] = pst[c][e] > 0.f ? sigma * (nrm * (1.f / pst[c][e])) : 0.f;
+                    qb[e] = fmaf(v[c][e], mulc[e], M);
+                    worst = fmaxf(worst, fabsf(fmaf(v[c][e], mulc[e], M - qb[e])));
+                }
+                if (worst >= 0.5f - kTieWindow) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        qb[e] = (pst[c][e] > 0.f
+                                     ? quant_code(v[c][e], mulc[e], sigma * static_cast<double>(pst[c][e]) * sqb, qmax)
+                                     : 0.f) + M;
+                }
+                uint32_t cb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(qb[e], M - qmax, M + qmax));
+                if (p.bits == 8) {
+                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
+                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
+                } else {
+                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
+                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
+                }
+            }
+        }
+
+        if ((MODE == ROWQ_DYNAMIC || MODE == ROWQ_POSTMUL) && row < p.m) {
             const float scale = (amax * nrm) / qmax;
             const float mul = (scale > 0.f) ? sigma * (nrm * (1.f / scale)) : 0.f;
             const double div = sigma * static_cast<double>(scale) * sqrt(static_cast<double>(b));
@@ -777,9 +861,9 @@ int device_cus() {
 
 namespace {
 
-template <int DT, int NCH, bool GEGLU, int TPB>
+template <int DT, int NCH, bool GEGLU, int TPB, int MODE = ROWQ_DYNAMIC>
 hipError_t launch_rows_nch(const RowQuantParams& p, hipStream_t st) {
-    auto kern = rotate_quant_rows_kernel<DT, NCH, GEGLU, TPB>;
+    auto kern = rotate_quant_rows_kernel<DT, NCH, GEGLU, TPB, MODE>;
     // resident blocks per CU of this instantiation (queried once)
     static const int per_cu = [&] {
         int n = 0;
@@ -795,12 +879,12 @@ hipError_t launch_rows_nch(const RowQuantParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int DT, bool GEGLU, int TPB>
+template <int DT, bool GEGLU, int TPB, int MODE = ROWQ_DYNAMIC>
 hipError_t launch_rows_tpb(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
     switch (nch_tpl) {
-        case 1: return launch_rows_nch<DT, 1, GEGLU, TPB>(p, st);
-        case 2: return launch_rows_nch<DT, 2, GEGLU, TPB>(p, st);
-        case 4: return launch_rows_nch<DT, 4, GEGLU, TPB>(p, st);
+        case 1: return launch_rows_nch<DT, 1, GEGLU, TPB, MODE>(p, st);
+        case 2: return launch_rows_nch<DT, 2, GEGLU, TPB, MODE>(p, st);
+        case 4: return launch_rows_nch<DT, 4, GEGLU, TPB, MODE>(p, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -847,10 +931,27 @@ hipError_t launch_bf16_fast(const RowQuantParams& p, bool geglu, hipStream_t st)
     return geglu ? launch_fast_geglu<true>(p, st) : launch_fast_geglu<false>(p, st);
 }
 
-template <int DT, bool GEGLU>
+template <int DT, bool GEGLU, int MODE = ROWQ_DYNAMIC>
 hipError_t launch_rows_dt(const RowQuantParams& p, int nch_tpl, hipStream_t st) {
-    if (p.g > 256) return launch_rows_tpb<DT, GEGLU, 1024>(p, nch_tpl, st);
-    return launch_rows_tpb<DT, GEGLU, 256>(p, nch_tpl, st);
+    if (p.g > 256) return launch_rows_tpb<DT, GEGLU, 1024, MODE>(p, nch_tpl, st);
+    return launch_rows_tpb<DT, GEGLU, 256, MODE>(p, nch_tpl, st);
+}
+
+template <int MODE>
+hipError_t launch_rows_mode(const RowQuantParams& p, int dtype, int nch_tpl, hipStream_t st) {
+    switch (dtype) {
+        case F16: return launch_rows_dt<F16, false, MODE>(p, nch_tpl, st);
+        case BF16: return launch_rows_dt<BF16, false, MODE>(p, nch_tpl, st);
+        case F32: return launch_rows_dt<F32, false, MODE>(p, nch_tpl, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// table = column maximum bits / qmax, in place (fp32 division)
+__global__ void step_scale_finish_kernel(float* table, int64_t k, float qmax) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= k) return;
+    table[i] = __uint_as_float(reinterpret_cast<uint32_t*>(table)[i]) / qmax;
 }
 
 }  // namespace
@@ -900,7 +1001,7 @@ hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, i
     p.x = x; p.m = m; p.k = k; p.ldx = ldx; p.mult = mult;
     p.g = row_quant_lanes(k);
     p.nch = row_quant_chunks(k, p.g);
-    p.had_block = had_block; p.bits = bits; p.q = q; p.scale = scale;
+    p.had_block = had_block; p.bits = bits; p.q = q; p.scale = scale; p.post = nullptr;
     int tpl = 1;
     while (tpl < p.nch) tpl <<= 1;
     if (tpl > 4) return hipErrorInvalidValue;
@@ -922,6 +1023,42 @@ hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, i
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_rotate_quant_table(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                                     const float* mult, int had_block, int bits, const float* table,
+                                     bool weights, void* q, float* scale, hipStream_t st) {
+    RowQuantParams p;
+    p.x = x; p.m = m; p.k = k; p.ldx = ldx; p.mult = mult;
+    p.g = row_quant_lanes(k);
+    p.nch = row_quant_chunks(k, p.g);
+    p.had_block = had_block; p.bits = bits; p.q = q; p.scale = scale; p.post = table;
+    int tpl = 1;
+    while (tpl < p.nch) tpl <<= 1;
+    if (tpl > 4) return hipErrorInvalidValue;
+    if (weights) return launch_rows_mode<ROWQ_POSTMUL>(p, dtype, tpl, st);
+    return launch_rows_mode<ROWQ_STATIC>(p, dtype, tpl, st);
+}
+
+hipError_t launch_calibrate_step_scales(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                                        const float* mult, int had_block, int bits, float* table,
+                                        hipStream_t st) {
+    RowQuantParams p;
+    p.x = x; p.m = m; p.k = k; p.ldx = ldx; p.mult = mult;
+    p.g = row_quant_lanes(k);
+    p.nch = row_quant_chunks(k, p.g);
+    p.had_block = had_block; p.bits = bits; p.q = table; p.scale = nullptr; p.post = nullptr;
+    int tpl = 1;
+    while (tpl < p.nch) tpl <<= 1;
+    if (tpl > 4) return hipErrorInvalidValue;
+    const dim3 fg(static_cast<unsigned>((k + 255) / 256));
+    hipLaunchKernelGGL(fill_u32_kernel, fg, dim3(256), 0, st, reinterpret_cast<uint32_t*>(table), k, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_rows_mode<ROWQ_COLMAX>(p, dtype, tpl, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(step_scale_finish_kernel, fg, dim3(256), 0, st, table, k, bits == 8 ? 127.f : 7.f);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_groups_w4(const void* w, int dtype, int64_t n, int64_t k, void* q,

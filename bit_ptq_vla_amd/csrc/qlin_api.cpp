@@ -119,6 +119,21 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     return map_err(e);
 }
 
+// Shared checks of the per-step table entry points (rows of k values, no pre-op).
+qlin_status table_rows_check(const void* x, qlin_dtype dt, int64_t rows, int64_t k, int64_t ldx,
+                             const float* fold, int32_t had_block, int32_t bits, const void* table) {
+    if (!table) return QLIN_ERR_NULL;
+    if (rows > 0 && !x) return QLIN_ERR_NULL;
+    if (!is_float_in(dt)) return QLIN_ERR_DTYPE;
+    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 8 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < k) return QLIN_ERR_SHAPE;
+    if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
+    if (k > kMaxRowK) return QLIN_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(fold) || !aligned16(table)) return QLIN_ERR_ALIGN;
+    return QLIN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +223,58 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
     if (st != QLIN_OK) return st;
     return map_err(qlin::launch_rotate_quant(x, x_dtype, m, k, ldx, pre == QLIN_PRE_GEGLU, fold_inv_s,
                                              had_block, bits, xq, x_scale, as_stream(stream)));
+}
+
+qlin_status qlin_calibrate_step_scales(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                       const float* fold_inv_s, int32_t had_block, int32_t bits,
+                                       float* table, void* stream) {
+    qlin_status st = table_rows_check(x, x_dtype, m, k, ldx, fold_inv_s, had_block, bits, table);
+    if (st != QLIN_OK) return st;
+    if (m < 1) return QLIN_ERR_SHAPE;
+    const Span outs[1] = {{table, k * 4}};
+    const Span ins[2] = {{x, ((m - 1) * ldx + k) * dtype_size(x_dtype)}, {fold_inv_s, fold_inv_s ? k * 4 : 0}};
+    if (any_overlap(outs, 1, ins, 2)) return QLIN_ERR_ALIAS;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_calibrate_step_scales(x, x_dtype, m, k, ldx, fold_inv_s, had_block, bits,
+                                                      table, as_stream(stream)));
+}
+
+qlin_status qlin_rotate_quant_act_static(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                         const float* fold_inv_s, int32_t had_block, int32_t bits,
+                                         const float* table, void* xq, void* stream) {
+    qlin_status st = table_rows_check(x, x_dtype, m, k, ldx, fold_inv_s, had_block, bits, table);
+    if (st != QLIN_OK) return st;
+    if (m > 0 && !xq) return QLIN_ERR_NULL;
+    if (!aligned16(xq)) return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
+    const Span outs[1] = {{xq, code_bytes}};
+    const Span ins[3] = {{x, m > 0 ? ((m - 1) * ldx + k) * dtype_size(x_dtype) : 0},
+                         {fold_inv_s, fold_inv_s ? k * 4 : 0}, {table, k * 4}};
+    if (any_overlap(outs, 1, ins, 3)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_rotate_quant_table(x, x_dtype, m, k, ldx, fold_inv_s, had_block, bits, table,
+                                                   false, xq, nullptr, as_stream(stream)));
+}
+
+qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                       const float* fold_s, int32_t had_block, int32_t bits,
+                                       const float* table, void* wq, float* w_scale, void* stream) {
+    qlin_status st = table_rows_check(w, w_dtype, n, k, k, fold_s, had_block, bits, table);
+    if (st != QLIN_OK) return st;
+    if (!wq || !w_scale) return QLIN_ERR_NULL;
+    if (n < 1) return QLIN_ERR_SHAPE;
+    if (!aligned16(wq) || !aligned16(w_scale)) return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
+    const Span outs[2] = {{wq, code_bytes}, {w_scale, n * 4}};
+    const Span ins[3] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}, {table, k * 4}};
+    if (any_overlap(outs, 2, ins, 3)) return QLIN_ERR_ALIAS;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_rotate_quant_table(w, w_dtype, n, k, k, fold_s, had_block, bits, table, true,
+                                                   wq, w_scale, as_stream(stream)));
 }
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

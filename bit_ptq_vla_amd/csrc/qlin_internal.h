@@ -19,6 +19,18 @@ hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, i
 hipError_t launch_quant_groups_w4(const void* w, int dtype, int64_t n, int64_t k, void* q,
                                   void* scale, hipStream_t st);
 
+// Per-step static activation table: codes v / table[c] (weights == false, no
+// per-row scale), or one step's weights v * table[c] then per-row RTN
+// (weights == true, scale out).  Plain rows only (no GeGLU pre-op).
+hipError_t launch_rotate_quant_table(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                                     const float* mult, int had_block, int bits, const float* table,
+                                     bool weights, void* q, float* scale, hipStream_t st);
+
+// table[c] = max over the m rows of |rotate(x * mult)[., c]| / qmax.
+hipError_t launch_calibrate_step_scales(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,
+                                        const float* mult, int had_block, int bits, float* table,
+                                        hipStream_t st);
+
 hipError_t launch_calibrate_fold(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
                                  bool geglu, const void* w, int w_dtype, int64_t n, float* s,
                                  float* inv_s, hipStream_t st);

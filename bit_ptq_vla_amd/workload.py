@@ -159,7 +159,9 @@ class SweepLayer:
 class ActionExpert:
     """The action expert's six projections at M = 50 (width 1024, MLP 4096):
     W4A4 with Hadamard block 64 (fold calibrated on the step-0 inputs) and
-    W4A16 g128 on the same weights; inputs drift with the denoising step."""
+    W4A16 g128 on the same weights; inputs drift with the denoising step.
+    build_static() adds the per-step static-table variant (W4A4, one table
+    and one weight copy per step and projection)."""
 
     def __init__(self, dev, steps: int = 10):
         import torch
@@ -171,11 +173,12 @@ class ActionExpert:
         wl = synth.CFG3
         self.projs = wl.projs
         self.steps = steps
-        self.w4a4, self.w4a16 = [], []
+        self.w4a4, self.w4a16, self.fold_s = [], [], []
         for pr in wl.projs:
             w = synth.weight(wl, pr).to(dev)
             x0 = synth.activation(wl, pr, 50, tag="/t0", std=synth.cfg3_sigma(0)).to(dev)
             s, inv = q.qlin_calibrate_fold(x0, w)
+            self.fold_s.append(s)
             wq, ws = q.qlin_quantize_weights(w, fold_s=s, had_block=64, bits=4)
             wq16, ws16 = q.qlin_quantize_weights(w, bits=4, group=128)
             xs = [synth.activation(wl, pr, 50, tag=f"/t{t}", std=synth.cfg3_sigma(t)).to(dev)
@@ -188,6 +191,37 @@ class ActionExpert:
         self.ops_per_step = 2 * 50 * sum(pr.n * pr.k for pr in wl.projs)
         self.w4a16_bytes = sum(pr.n * pr.k // 2 + pr.n * (pr.k // 128) * 2 + 2 * 50 * pr.k + 2 * 50 * pr.n
                                for pr in wl.projs)
+
+    def build_static(self):
+        """Per-step static activation tables (one per step and projection,
+        calibrated on separate calibration tokens of that step) and the
+        per-step weights with each table folded in."""
+        import torch
+
+        q = self.q
+        from bit_ptq_vla_amd import synth
+
+        wl = synth.CFG3
+        dev = self.w4a4[0][3].device
+        self.ones = torch.ones(50, dtype=torch.float32, device=dev)
+        self.static = []
+        for (pr, xs, inv, wq, ws, xq, xsc, y), s in zip(self.w4a4, self.fold_s):
+            w = synth.weight(wl, pr).to(dev)
+            per_step = []
+            for t in range(self.steps):
+                xc = synth.activation(wl, pr, 50, tag=f"/cal{t}", std=synth.cfg3_sigma(t)).to(dev)
+                table = q.qlin_calibrate_step_scales(xc, fold_inv_s=inv, had_block=64, bits=4)
+                wq_t, ws_t = q.qlin_quantize_weights_step(w, table, fold_s=s, had_block=64, bits=4)
+                per_step.append((table, wq_t, ws_t))
+            self.static.append((pr, xs, inv, per_step, xq, y))
+
+    def run_w4a4_static(self):
+        q = self.q
+        for t in range(self.steps):
+            for pr, xs, inv, per_step, xq, y in self.static:
+                table, wq_t, ws_t = per_step[t]
+                q.qlin_rotate_quant_act_static(xs[t], table, fold_inv_s=inv, had_block=64, bits=4, out=xq)
+                q.qlin_gemm_w4a4(xq, self.ones, wq_t, ws_t, pr.k, out=y)
 
     def run_w4a4(self):
         q = self.q

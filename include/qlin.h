@@ -136,6 +136,48 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
                                   void* stream);
 
 /*
+ * Per-step static activation scales (Omega-QVLA technical summary,
+ * Metodologia 2, "Scalatura delle Attivazioni DiT per Passo": a scale table
+ * per denoising step, layer and channel, computed beforehand from
+ * calibration trajectories and looked up at inference in place of one static
+ * scale).  Reading taken: the table holds one scale per input channel of the
+ * projection, in the rotated space where activations are quantized; since a
+ * per-channel scale cannot leave the integer dot product, each step gets its
+ * own weights with the table folded in, and the GEMM then takes x_scale = 1.
+ * v below is the activation stage of qlin_rotate_quant_act without its
+ * quantizer: v = (x[m] * fold_inv_s) @ blockdiag(H_b / sqrt(b)) (no pre-op).
+ *
+ * qlin_calibrate_step_scales -- one table row from a step's calibration tokens:
+ *   table[c] = fp32( max_m |v[m][c]| / qmax ),  qmax = 7 (bits 4) or 127 (bits 8).
+ *   x [m][ldx] (k inputs first in each row), m >= 1; table: out float[k].
+ *
+ * qlin_rotate_quant_act_static -- activation codes of one step:
+ *   xq[m][c] = clamp(rne(v[m][c] / table[c]), +-qmax); a table entry that is
+ *   not a positive finite number gives code 0.  xq as in qlin_rotate_quant_act;
+ *   there is no per-row scale (the GEMM takes x_scale[m] = 1).
+ *
+ * qlin_quantize_weights_step -- one step's weights: per output row n,
+ *   v = (w[n] * fold_s) @ blockdiag(H_b / sqrt(b)), times table[c] (finite);
+ *   w_scale[n] = fp32(max_c |v| / qmax); wq = clamp(rne(v / w_scale[n]), +-qmax)
+ *   (layout and zero rows as qlin_quantize_weights with group 0).
+ *
+ * Arguments as qlin_rotate_quant_act / qlin_quantize_weights; table is
+ * float[k], 16-byte aligned, read (or written) on the device.  Preconditions:
+ * k >= 8, k % 8 == 0, ldx % 8 == 0, ldx >= k; had_block 0/1 or a power of two
+ * <= 256 dividing k; bits 4 or 8.  Errors as those entry points (NULL
+ * table: QLIN_ERR_NULL).
+ */
+qlin_status qlin_calibrate_step_scales(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                       int64_t ldx, const float* fold_inv_s, int32_t had_block,
+                                       int32_t bits, float* table, void* stream);
+qlin_status qlin_rotate_quant_act_static(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                         int64_t ldx, const float* fold_inv_s, int32_t had_block,
+                                         int32_t bits, const float* table, void* xq, void* stream);
+qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                       const float* fold_s, int32_t had_block, int32_t bits,
+                                       const float* table, void* wq, float* w_scale, void* stream);
+
+/*
  * qlin_gemm_w4a4 / qlin_gemm_w8a8 -- integer GEMM with int32 accumulation
  * and a fused dequantizing epilogue (FoldQuantVLA abstract: native integer
  * execution of the projections).

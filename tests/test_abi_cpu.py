@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("qlin_rotate_quant_act", "qlin_quantize_weights", "qlin_gemm_w4a4", "qlin_gemm_w8a8", "qlin_gemm_w4a8",
               "qlin_gemm_w4a4_geglu", "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version",
-              "qlin_status_string"):
+              "qlin_status_string", "qlin_calibrate_step_scales", "qlin_rotate_quant_act_static",
+              "qlin_quantize_weights_step"):
         assert n in names
 
 
@@ -184,6 +185,56 @@ def test_calibrate_fold_rejects(lib, kw, status):
     a.update(kw)
     assert lib.qlin_calibrate_fold(a["x"], a["xdt"], a["m"], a["k"], a["ldx"], a["pre"], a["w"], a["wdt"],
                                    a["n"], a["s"], a["inv"], None) == status
+
+
+# ---- per-step table entry points
+
+# qlin_calibrate_step_scales(x, dt, m, k, ldx, inv_s, b, bits, table, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), q.QLIN_ERR_NULL), (dict(t=None), q.QLIN_ERR_NULL), (dict(dt=3), q.QLIN_ERR_DTYPE),
+    (dict(bits=5), q.QLIN_ERR_UNSUPPORTED), (dict(b=96), q.QLIN_ERR_UNSUPPORTED),
+    (dict(m=0), q.QLIN_ERR_SHAPE), (dict(k=500, ldx=504), q.QLIN_ERR_SHAPE), (dict(ldx=256), q.QLIN_ERR_SHAPE),
+    (dict(k=65536, ldx=65536, b=0), q.QLIN_ERR_SHAPE), (dict(t=BAD), q.QLIN_ERR_ALIGN),
+    (dict(inv=BAD), q.QLIN_ERR_ALIGN), (dict(t=P + 64), q.QLIN_ERR_ALIAS),
+])
+def test_calibrate_step_scales_rejects(lib, kw, status):
+    a = dict(x=P, dt=0, m=8, k=512, ldx=512, inv=P4, b=64, bits=4, t=P3)
+    a.update(kw)
+    assert lib.qlin_calibrate_step_scales(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["inv"], a["b"], a["bits"],
+                                          a["t"], None) == status
+
+
+# qlin_rotate_quant_act_static(x, dt, m, k, ldx, inv_s, b, bits, table, xq, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), q.QLIN_ERR_NULL), (dict(t=None), q.QLIN_ERR_NULL), (dict(xq=None), q.QLIN_ERR_NULL),
+    (dict(dt=3), q.QLIN_ERR_DTYPE), (dict(bits=2), q.QLIN_ERR_UNSUPPORTED), (dict(b=3), q.QLIN_ERR_UNSUPPORTED),
+    (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=520, ldx=520), q.QLIN_ERR_SHAPE), (dict(ldx=513), q.QLIN_ERR_SHAPE),
+    (dict(xq=BAD), q.QLIN_ERR_ALIGN), (dict(t=BAD), q.QLIN_ERR_ALIGN),
+    (dict(xq=P + 128), q.QLIN_ERR_ALIAS), (dict(xq=P3), q.QLIN_ERR_ALIAS),
+])
+def test_rotate_quant_act_static_rejects(lib, kw, status):
+    a = dict(x=P, dt=1, m=4, k=512, ldx=512, inv=None, b=64, bits=4, t=P3, xq=P2)
+    a.update(kw)
+    assert lib.qlin_rotate_quant_act_static(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["inv"], a["b"], a["bits"],
+                                            a["t"], a["xq"], None) == status
+
+
+def test_rotate_quant_act_static_empty_is_ok(lib):
+    assert lib.qlin_rotate_quant_act_static(None, 0, 0, 512, 512, None, 64, 4, P3, None, None) == q.QLIN_OK
+
+
+# qlin_quantize_weights_step(w, dt, n, k, fold_s, b, bits, table, wq, ws, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), q.QLIN_ERR_NULL), (dict(t=None), q.QLIN_ERR_NULL), (dict(wq=None), q.QLIN_ERR_NULL),
+    (dict(ws=None), q.QLIN_ERR_NULL), (dict(dt=4), q.QLIN_ERR_DTYPE), (dict(bits=16), q.QLIN_ERR_UNSUPPORTED),
+    (dict(n=0), q.QLIN_ERR_SHAPE), (dict(k=544), q.QLIN_ERR_SHAPE), (dict(ws=BAD), q.QLIN_ERR_ALIGN),
+    (dict(s=BAD), q.QLIN_ERR_ALIGN), (dict(wq=P + 1024), q.QLIN_ERR_ALIAS), (dict(ws=P3 + 16), q.QLIN_ERR_ALIAS),
+])
+def test_quantize_weights_step_rejects(lib, kw, status):
+    a = dict(w=P, dt=0, n=8, k=512, s=None, b=64, bits=4, t=P3, wq=P2, ws=P4)
+    a.update(kw)
+    assert lib.qlin_quantize_weights_step(a["w"], a["dt"], a["n"], a["k"], a["s"], a["b"], a["bits"], a["t"],
+                                          a["wq"], a["ws"], None) == status
 
 
 def test_binding_raises_qlin_error(lib):
