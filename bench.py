@@ -22,9 +22,9 @@ batch-1 W4A16 GEMV of a 7B-decoder layer (hidden 4096, MLP 11008) in GB/s
 with distinct weight copies rotated to defeat the 256 MB Infinity Cache, the
 W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape, one layer
 of the 18-layer backbone sweep at M = 6528 and 52224 (the compute-bound
-regime), the action expert's projections over 10 denoising steps (W4A4 and
-W4A16), the dominant kernel's roofline fraction, and the CPU oracle on a row
-sample.
+regime), the action expert's projections over 10 denoising steps (W4A4 with
+per-token scales, W4A4 with per-step static tables, W4A16), the dominant
+kernel's roofline fraction, and the CPU oracle on a row sample.
 
 Prints ONE JSON line.
 """
