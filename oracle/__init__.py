@@ -18,6 +18,10 @@ Blocchi"; LoopQ abstract for plain RTN weights and the W4A16 weight-only form):
                   from the bf16-rounded dequantized g, u (the fused form of the
                   backbone MLP's gated GeLU)
   W4A16 GEMV      f64 dot products against q * s16[group]
+  composite rot.  (Omega-QVLA "Rotazione SVD" / "Implementazione a Blocchi")
+                  zigzag permutation of the input channels by weight norms,
+                  per block R_j = U_j H_b / sqrt(b) with U_j the eigenvectors
+                  of the block's weight Gram matrix
   per-step table  (Omega-QVLA "Scalatura delle Attivazioni DiT per Passo")
                   s_t[c] = max |rotated calibration activations| / qmax per
                   step; static codes v / s_t[c]; s_t folded into that step's
@@ -45,6 +49,11 @@ from .qlin_ref import (  # noqa: F401
     calibrate_step_scales,
     rotate_quant_act_static,
     quantize_weights_step,
+    zigzag_permutation,
+    composite_rotations,
+    rotate_composite,
+    rotate_quant_act_composite,
+    quantize_weights_composite,
     int_gemm,
     dequant_epilogue,
     gemm,

@@ -16,6 +16,9 @@ Sources (page title, section):
         batch 1; memory-bound action expert).
   [QV]  QuantVLA technical summary -- Methodology B/C (per-head and per-layer
         scalars folded into the dequantization scale, no extra runtime op).
+  [OR]  Omega-QVLA technical summary -- Metodologia 1, "Rotazione SVD",
+        "Rotazione Hadamard" (R = R_SVD * H) and "Implementazione a Blocchi"
+        (block form, zigzag permutation of the channels by weight norms).
   [OS]  Omega-QVLA technical summary -- Metodologia 2, "Scalatura delle
         Attivazioni DiT per Passo" (a precomputed scale table per denoising
         step, per layer and per channel, derived from calibration
@@ -329,6 +332,100 @@ def quantize_weights_step(w, fold_s, had_block: int, bits: int, step_scale):
     v = _rotated(w, fold_s, had_block, "mul")
     v = v * np.asarray(step_scale, dtype=np.float32).astype(np.float64)[None, :]
     return quantize_rows(v, bits)
+
+
+# --------------------------------------------------------------------------
+# SVD-Hadamard composite rotation with the zigzag permutation  [OR]
+#
+# Readings (the page is garbled on sides and conventions):
+#  * The page writes y = x W with W of shape C_in x C_out, so the U of its
+#    W = U S V^T is C_in x C_in and acts on the input channels.  In the
+#    [n][k] (out x in) storage used here that U is the eigenvector matrix of
+#    W^T W; in the block form, of the block's Gram matrix
+#    G_j = W[:, B_j]^T W[:, B_j] (b x b), eigenvectors ordered by descending
+#    eigenvalue, each with its largest-magnitude entry positive (the first
+#    such entry on ties).
+#  * The composite rotation of block j is R_j = U_j (H_b / sqrt(b)): x is
+#    multiplied by U_j, then by the normalised Hadamard matrix.
+#  * The zigzag permutation: input channels sorted by descending L2 norm of
+#    their weight column (lower index first on ties) are dealt to the k / b
+#    blocks in snake order -- rank r, round t = r // nb, i = r % nb goes to
+#    block i on even rounds and nb - 1 - i on odd rounds, at slot t.
+#  * The permutation is applied first (a gather of input channels), on both
+#    sides: x[:, perm] R and W[:, perm] R, so x W^T is unchanged.
+# --------------------------------------------------------------------------
+
+
+def zigzag_permutation(w, had_block: int) -> np.ndarray:
+    """perm[c'] = the input channel placed at position c' (int64 [K])."""
+    w = np.asarray(w, dtype=np.float64)
+    k = w.shape[1]
+    b = had_block
+    if b < 1 or k % b:
+        raise ValueError("k must be a multiple of the block")
+    nb = k // b
+    norms = np.sqrt(np.sum(w * w, axis=0))
+    order = np.lexsort((np.arange(k), -norms))   # descending norm, then index
+    perm = np.empty(k, dtype=np.int64)
+    for r, c in enumerate(order):
+        t, i = divmod(r, nb)
+        j = i if t % 2 == 0 else nb - 1 - i
+        perm[j * b + t] = c
+    return perm
+
+
+def _sign_fixed(u: np.ndarray) -> np.ndarray:
+    u = u.copy()
+    for c in range(u.shape[1]):
+        i = int(np.argmax(np.abs(u[:, c])))
+        if u[i, c] < 0:
+            u[:, c] = -u[:, c]
+    return u
+
+
+def composite_rotations(w, perm, had_block: int) -> np.ndarray:
+    """R [k/b][b][b] float64: R_j = U_j (H_b / sqrt(b)) from the Gram matrix
+    of block j of the permuted weight columns."""
+    w = np.asarray(w, dtype=np.float64)[:, np.asarray(perm)]
+    b = had_block
+    nb = w.shape[1] // b
+    hb = sylvester_hadamard(b).astype(np.float64) / math.sqrt(b)
+    out = np.empty((nb, b, b), dtype=np.float64)
+    for j in range(nb):
+        blk = w[:, j * b:(j + 1) * b]
+        evals, evecs = np.linalg.eigh(blk.T @ blk)
+        order = np.argsort(-evals, kind="stable")
+        out[j] = _sign_fixed(evecs[:, order]) @ hb
+    return out
+
+
+def rotate_composite(v, perm, rot) -> np.ndarray:
+    """v[:, perm], then block j of the permuted channels times rot[j]
+    (rot as given, float32 values taken exactly)."""
+    v = np.asarray(v, dtype=np.float64)[:, np.asarray(perm)]
+    rot = np.asarray(rot).astype(np.float64)
+    nb, b, _ = rot.shape
+    out = np.empty_like(v)
+    for j in range(nb):
+        out[:, j * b:(j + 1) * b] = v[:, j * b:(j + 1) * b] @ rot[j]
+    return out
+
+
+def rotate_quant_act_composite(x, fold_s, perm, rot, bits: int):
+    """x / s (optional fold, on the original channels) -> gather -> per-block
+    composite rotation -> per-token dynamic quantization."""
+    v = np.asarray(x, dtype=np.float64)
+    if fold_s is not None:
+        v = v / np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
+    return quantize_rows(rotate_composite(v, perm, rot), bits)
+
+
+def quantize_weights_composite(w, fold_s, perm, rot, bits: int):
+    """w * s -> gather -> per-block composite rotation -> per-row RTN."""
+    v = np.asarray(w, dtype=np.float64)
+    if fold_s is not None:
+        v = v * np.asarray(fold_s, dtype=np.float32).astype(np.float64)[None, :]
+    return quantize_rows(rotate_composite(v, perm, rot), bits)
 
 
 def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
