@@ -24,7 +24,9 @@ W4A8 GEMM (int8 activations x int4 weights) at the gate|up shape, one layer
 of the 18-layer backbone sweep at M = 6528 and 52224 (the compute-bound
 regime), the action expert's projections over 10 denoising steps (W4A4 with
 per-token scales, W4A4 with per-step static tables, W4A16), the dominant
-kernel's roofline fraction, and the CPU oracle on a row sample.
+kernel's roofline fraction, the activation stage with the SVD-Hadamard
+composite rotation against the block Hadamard, and the CPU oracle on a row
+sample.
 
 Prints ONE JSON line.
 """
@@ -309,6 +311,45 @@ def action_expert_leg(dev, reps=5):
     return res
 
 
+def composite_leg(dev, reps=5):
+    """Activation quantization with the SVD-Hadamard composite rotation and the
+    zigzag permutation against the fast block Hadamard, at the action
+    expert's input (50 x 1024, b = 64, fp16) and the backbone MLP's input
+    (816 x 2048, b = 128, bf16; rotations from the 2048 x 2048 q projection of
+    the backbone sweep); 20 calls per captured graph, us per call."""
+    import torch
+
+    import bit_ptq_vla_amd as q
+    from bit_ptq_vla_amd import synth
+
+    res = {}
+    for name, wl, proj, m, b in (("m50_k1024_b64", synth.CFG3, synth.CFG3.projs[0], 50, 64),
+                                 ("m816_k2048_b128", synth.CFG5, synth.CFG5.projs[0], 816, 128)):
+        w = synth.weight(wl, proj).to(dev)
+        x = synth.activation(wl, proj, m).to(dev)
+        perm, rot = q.qlin_calibrate_composite(w, b)
+        xq = torch.empty((m, proj.k // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty(m, dtype=torch.float32, device=dev)
+        work = torch.empty(m * proj.k, dtype=torch.float32, device=dev)
+
+        def had():
+            for _ in range(20):
+                q.qlin_rotate_quant_act(x, had_block=b, bits=4, out=(xq, xs))
+
+        def comp():
+            for _ in range(20):
+                q.qlin_rotate_quant_act_composite(x, perm, rot, bits=4, out=(xq, xs), work=work)
+
+        r = {}
+        for tag, fn in (("hadamard_us", had), ("composite_us", comp)):
+            fn()
+            torch.cuda.synchronize()
+            us = _graph_us(fn, reps)
+            r[tag] = round((us if us is not None else _time_us(fn, reps)) / 20, 2)
+        res[name] = r
+    return res
+
+
 def cpu_baseline(block, rows):
     """The oracle as it stands on a row sample of the same step (single
     thread: NumPy's int64 matmul does not use BLAS; BLAS is pinned to one
@@ -396,6 +437,7 @@ def main():
         out["sweep_layer"] = sweep_leg(dev)
         log("bench: action expert leg (M = 50, 10 steps)")
         out["action_expert"] = action_expert_leg(dev)
+        out["composite_rotation"] = composite_leg(dev)
     if not args.no_gemv:
         log("bench: batch-1 W4A16 GEMV leg")
         out["gemv"] = gemv_leg(dev)

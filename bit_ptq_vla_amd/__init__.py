@@ -53,6 +53,9 @@ SIGNATURES = {
     "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
     "qlin_rotate_quant_act_static": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P],
     "qlin_quantize_weights_step": [_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P],
+    "qlin_calibrate_composite": [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P],
+    "qlin_rotate_quant_act_composite": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _P, _P, _P],
+    "qlin_quantize_weights_composite": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _P, _P],
 }
 
 _lib = None
@@ -246,6 +249,77 @@ def qlin_quantize_weights_step(w: torch.Tensor, table: torch.Tensor, fold_s: Opt
     st = lib.qlin_quantize_weights_step(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
                                         bits, table.data_ptr(), wq.data_ptr(), ws.data_ptr(), _stream(w.device))
     _check(st, "qlin_quantize_weights_step")
+    return wq, ws
+
+
+def qlin_calibrate_composite(w: torch.Tensor, had_block: int, fold_s: Optional[torch.Tensor] = None
+                             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Zigzag channel permutation (int32 [k]) and per-block composite
+    rotations (float32 [k/b][b][b]) from the weights w [n][k] (times fold_s)."""
+    lib = load()
+    _dev_tensor(w, "w")
+    n, k = w.shape
+    _need(w, n * k * w.element_size(), "w")
+    _need(fold_s, k * 4, "fold_s")
+    perm = torch.empty(k, dtype=torch.int32, device=w.device)
+    rot = torch.empty((k // had_block, had_block, had_block), dtype=torch.float32, device=w.device)
+    st = lib.qlin_calibrate_composite(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
+                                      perm.data_ptr(), rot.data_ptr(), _stream(w.device))
+    _check(st, "qlin_calibrate_composite")
+    return perm, rot
+
+
+def qlin_rotate_quant_act_composite(x: torch.Tensor, perm: torch.Tensor, rot: torch.Tensor,
+                                    fold_inv_s: Optional[torch.Tensor] = None, bits: int = 4,
+                                    k: Optional[int] = None,
+                                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                                    work: Optional[torch.Tensor] = None
+                                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Activation codes and per-token scales with the composite rotation
+    (work: float32 scratch of m * k elements; allocated here when None)."""
+    lib = load()
+    k = _rows_arg(x, k)
+    m, b = x.shape[0], rot.shape[-1]
+    if out is None:
+        xq = torch.empty((m, k // 2) if bits == 4 else (m, k), dtype=torch.uint8 if bits == 4 else torch.int8,
+                         device=x.device)
+        xs = torch.empty(m, dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    _need(xs, m * 4, "x_scale")
+    _need(perm, k * 4, "perm")
+    _need(rot, k * b * 4, "rot")
+    _need(fold_inv_s, k * 4, "fold_inv_s")
+    if work is None:
+        work = torch.empty(max(m, 1) * k, dtype=torch.float32, device=x.device)
+    _need(work, m * k * 4, "work")
+    st = lib.qlin_rotate_quant_act_composite(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0),
+                                             _ptr(fold_inv_s), perm.data_ptr(), rot.data_ptr(), b, bits,
+                                             xq.data_ptr(), xs.data_ptr(), work.data_ptr(), _stream(x.device))
+    _check(st, "qlin_rotate_quant_act_composite")
+    return xq, xs
+
+
+def qlin_quantize_weights_composite(w: torch.Tensor, perm: torch.Tensor, rot: torch.Tensor,
+                                    fold_s: Optional[torch.Tensor] = None, bits: int = 4
+                                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Weight codes and per-row scales with the composite rotation."""
+    lib = load()
+    _dev_tensor(w, "w")
+    n, k = w.shape
+    b = rot.shape[-1]
+    _need(w, n * k * w.element_size(), "w")
+    _need(perm, k * 4, "perm")
+    _need(rot, k * b * 4, "rot")
+    _need(fold_s, k * 4, "fold_s")
+    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
+                     device=w.device)
+    ws = torch.empty(n, dtype=torch.float32, device=w.device)
+    st = lib.qlin_quantize_weights_composite(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s),
+                                             perm.data_ptr(), rot.data_ptr(), b, bits, wq.data_ptr(),
+                                             ws.data_ptr(), _stream(w.device))
+    _check(st, "qlin_quantize_weights_composite")
     return wq, ws
 
 

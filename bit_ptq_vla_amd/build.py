@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlin.so")
 SOURCES = ["act_quant.hip", "gemm_i8.hip", "gemv_w4a16.hip", "skinny_w4a16.hip",
-           "skinny_int.hip", "qlin_api.cpp"]
+           "skinny_int.hip", "composite.hip",
+           "qlin_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,427 @@
+// SVD-Hadamard composite rotation with the zigzag channel permutation
+// (Omega-QVLA technical summary, Metodologia 1: "Rotazione SVD", "Rotazione
+// Hadamard", "Implementazione a Blocchi"), for gfx950.
+//
+// Online (activations) and offline (weights) quantization with the composite
+// rotation in place of the fast Hadamard transform: per row,
+//   v[c'] = x[perm[c']] * mult[perm[c']]            (gather, optional fold)
+//   v[B_j] = v[B_j] @ R_j                           (b x b rotation per block)
+//   per-row symmetric quantization of v (scale = max |v| / qmax, RNE codes).
+// The rotation is a dense product: dot products of b terms, fp32 operands
+// with exact fp64 products and an fp64 sum, rounded to fp32 once.  One kernel
+// applies block j's rotation (staged in LDS once) to a tile of rows and
+// writes the rotated rows (fp32) to a workspace; the row quantizer of the
+// Hadamard path then quantizes them as they stand (no fold, no rotation).
+//
+// Offline calibration of perm and R from the weights:
+//   * column norms of w * fold, fp64;
+//   * zigzag: channels ranked by descending norm (lower index first on ties)
+//     are dealt to the k / b blocks in snake order;
+//   * per block, the Gram matrix G_j = W[:, B_j]^T W[:, B_j] (fp64) and its
+//     eigenvectors by cyclic Jacobi rotations (round-robin pairs, b / 2
+//     rotations per round applied together), ordered by descending
+//     eigenvalue, each with its largest-magnitude entry positive; then
+//     R_j = U_j H_b / sqrt(b).
+// The page writes y = x W with W of shape C_in x C_out, so the U of its SVD
+// acts on the input channels: in the [n][k] storage here that is the
+// eigenvector matrix of W^T W, restricted to each block.
+
+#include "device_common.h"
+#include "qlin_internal.h"
+
+namespace qlin {
+
+namespace {
+
+template <int DT>
+__device__ __forceinline__ float load1(const void* row, int64_t i);
+template <>
+__device__ __forceinline__ float load1<F16>(const void* row, int64_t i) {
+    return static_cast<float>(static_cast<const _Float16*>(row)[i]);
+}
+template <>
+__device__ __forceinline__ float load1<BF16>(const void* row, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(row)[i]);
+}
+template <>
+__device__ __forceinline__ float load1<F32>(const void* row, int64_t i) {
+    return static_cast<const float*>(row)[i];
+}
+
+struct CompParams {
+    const void* x;
+    int64_t m, k, ldx;
+    const float* mult;   // fold multiplier on the original channels, or nullptr
+    const int32_t* perm; // [k]
+    const float* rot;    // [k/b][b][b]
+    int b;
+    float* v;            // out: rotated rows [m][k] fp32
+};
+
+// Block (j, row tile): the b x b rotation of block j (staged in LDS once)
+// applied to RT = 8 * 256 / b rows.  Thread t owns column c = t % b of rows
+// t / b + u * (256 / b), u < 8: one R[i][c] serves its 8 independent sums.
+template <int DT>
+__global__ __launch_bounds__(256) void composite_rotate_kernel(CompParams p) {
+    extern __shared__ float lds[];
+    constexpr int NU = 8;
+    const int b = p.b, k = static_cast<int>(p.k);
+    const int rt = NU * 256 / b;
+    float* rs = lds;                                          // [b][b]
+    double* xs = reinterpret_cast<double*>(lds + b * b);      // [rt][b], fp64 (b * b is even)
+    const int tid = threadIdx.x;
+    const int j = blockIdx.x;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * rt;
+    // rotation of block j: b * b / 4 float4, at most 16 per thread, four
+    // loads in flight before their stores
+    const float4* rj = reinterpret_cast<const float4*>(p.rot + static_cast<int64_t>(j) * b * b);
+    const int nq = b * b / 4;
+    for (int q0 = tid; q0 < nq; q0 += 4 * 256) {
+        float4 t4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) t4[t] = rj[q0 + 256 * t < nq ? q0 + 256 * t : nq - 1];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (q0 + 256 * t < nq) reinterpret_cast<float4*>(rs)[q0 + 256 * t] = t4[t];
+    }
+    // gathered, folded x: rt * b = 2048 elements, eight per thread
+    {
+        int src[NU];
+        int64_t rowv[NU];
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+            const int e = tid + 256 * t;
+            const int r = e / b, i = e - r * b;
+            rowv[t] = row0 + r;
+            int sidx = p.perm[j * b + i];
+            src[t] = sidx < 0 ? 0 : (sidx >= k ? k - 1 : sidx);   // (a valid permutation never clamps)
+        }
+        float v[NU], f[NU];
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+            const bool ok = rowv[t] < p.m;
+            const int64_t rr = ok ? rowv[t] : 0;
+            v[t] = load1<DT>(static_cast<const char*>(p.x) + rr * p.ldx * (DT == F32 ? 4 : 2), src[t]);
+            f[t] = p.mult ? p.mult[src[t]] : 1.f;
+            if (!ok) v[t] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < NU; ++t) xs[tid + 256 * t] = static_cast<double>(v[t] * f[t]);
+    }
+    __syncthreads();
+    const int c = tid % b, rb = tid / b, rstep = 256 / b;
+    double acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = 0.0;
+    for (int i = 0; i < b; i += 2) {
+        const double r0 = static_cast<double>(rs[i * b + c]);
+        const double r1 = static_cast<double>(rs[(i + 1) * b + c]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            // (two consecutive x values of a row in one 16-byte LDS read; the
+            // wave reads the same address, a broadcast)
+            const double2 xv = *reinterpret_cast<const double2*>(xs + (rb + u * rstep) * b + i);
+            acc[u] = __builtin_fma(xv.x, r0, acc[u]);
+            acc[u] = __builtin_fma(xv.y, r1, acc[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int64_t row = row0 + rb + u * rstep;
+        if (row < p.m) p.v[row * p.k + static_cast<int64_t>(j) * b + c] = static_cast<float>(acc[u]);
+    }
+}
+
+// ---- calibration ------------------------------------------------------------
+
+// Partial sums of squares of w * fold per column over a chunk of 256 rows:
+// part[chunk][c] (fp64, summed afterwards in chunk order).
+template <int DT>
+__global__ __launch_bounds__(256) void colnorm_part_kernel(const void* w, int64_t n, int64_t k,
+                                                           const float* fold, double* part) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (c >= k) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 256;
+    const int64_t r1 = r0 + 256 < n ? r0 + 256 : n;
+    const double f = fold ? static_cast<double>(fold[c]) : 1.0;
+    double s = 0.0;
+    for (int64_t r = r0; r < r1; ++r) {
+        const double v = static_cast<double>(load1<DT>(static_cast<const char*>(w) + r * k * (DT == F32 ? 4 : 2), c)) * f;
+        s = __builtin_fma(v, v, s);
+    }
+    part[static_cast<int64_t>(blockIdx.y) * k + c] = s;
+}
+
+__global__ __launch_bounds__(256) void colnorm_sum_kernel(const double* part, int64_t chunks, int64_t k,
+                                                          double* norm2) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (c >= k) return;
+    double s = 0.0;
+    for (int64_t i = 0; i < chunks; ++i) s += part[i * k + c];
+    norm2[c] = s;
+}
+
+// rank of channel c: channels with a larger norm, or an equal one and a
+// lower index, come first; then the snake deal to its position.
+__global__ __launch_bounds__(256) void zigzag_kernel(const double* norm2, int64_t k, int b, int32_t* perm) {
+    __shared__ double tile[2048];
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const double mine = c < k ? norm2[c] : 0.0;
+    int64_t rank = 0;
+    for (int64_t t0 = 0; t0 < k; t0 += 2048) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < 2048; i += 256) tile[i] = t0 + i < k ? norm2[t0 + i] : 0.0;
+        __syncthreads();
+        const int64_t lim = k - t0 < 2048 ? k - t0 : 2048;
+        for (int64_t i = 0; i < lim; ++i) {
+            const double o = tile[i];
+            rank += (o > mine || (o == mine && t0 + i < c)) ? 1 : 0;
+        }
+    }
+    if (c >= k) return;
+    const int64_t nb = k / b;
+    const int64_t t = rank / nb, i = rank - t * nb;
+    const int64_t j = (t & 1) ? nb - 1 - i : i;
+    perm[j * b + t] = static_cast<int32_t>(c);
+}
+
+// Gram matrix of block j of the permuted columns of w * fold:
+// G[j][a][c] = sum_n v[n][perm[jb + a]] v[n][perm[jb + c]] (fp64).  Block
+// (j, tile): a 16 x 16 tile of G_j, rows of w in chunks of 64 through LDS.
+template <int DT>
+__global__ __launch_bounds__(256) void gram_kernel(const void* w, int64_t n, int64_t k, const float* fold,
+                                                   const int32_t* perm, int b, double* gram) {
+    __shared__ double va[64][17], vc[64][17];
+    const int j = blockIdx.x;
+    const int tiles = b / 16;
+    const int ta = blockIdx.y / tiles, tc = blockIdx.y - ta * tiles;
+    const int ia = threadIdx.x >> 4, ic = threadIdx.x & 15;
+    const int ca = perm[j * b + ta * 16 + (threadIdx.x & 15)];
+    const int cc = perm[j * b + tc * 16 + (threadIdx.x & 15)];
+    const double fa = fold ? static_cast<double>(fold[ca]) : 1.0;
+    const double fc = fold ? static_cast<double>(fold[cc]) : 1.0;
+    double acc = 0.0;
+    for (int64_t r0 = 0; r0 < n; r0 += 64) {
+        __syncthreads();
+        // 64 rows x 16 columns of each tile: thread t loads rows t/16, t/16 + 16, ...
+        for (int rr = threadIdx.x >> 4; rr < 64; rr += 16) {
+            const int64_t r = r0 + rr;
+            double a = 0.0, c = 0.0;
+            if (r < n) {
+                const char* wr = static_cast<const char*>(w) + r * k * (DT == F32 ? 4 : 2);
+                a = static_cast<double>(load1<DT>(wr, ca)) * fa;
+                c = static_cast<double>(load1<DT>(wr, cc)) * fc;
+            }
+            va[rr][threadIdx.x & 15] = a;
+            vc[rr][threadIdx.x & 15] = c;
+        }
+        __syncthreads();
+        for (int rr = 0; rr < 64; ++rr) acc = __builtin_fma(va[rr][ia], vc[rr][ic], acc);
+    }
+    gram[(static_cast<int64_t>(j) * b + ta * 16 + ia) * b + tc * 16 + ic] = acc;
+}
+
+// Cyclic Jacobi eigen-decomposition of one block's Gram matrix (T = double
+// for b <= 64, float for b = 128 so that A and V fit LDS), then the sorted,
+// sign-fixed eigenvectors times H_b / sqrt(b) into rot[j] (fp32).
+// Round-robin pairing (circle method): in round r the b positions
+// [0, (r + t) % (b - 1) + 1 for t = 0 .. b - 2] are paired first with last;
+// the b / 2 rotations of a round touch disjoint rows and columns, so their
+// row updates run together, then their column updates.  Sweeps stop when
+// every off-diagonal entry is below 1e-14 (fp32: 2e-6) of the largest
+// diagonal entry, or after 15 sweeps.
+template <typename T>
+__global__ __launch_bounds__(256) void jacobi_rot_kernel(const double* gram, int b, float* rot) {
+    extern __shared__ unsigned char smem[];
+    T* A = reinterpret_cast<T*>(smem);                 // [b][b]
+    T* V = A + b * b;                                  // [b][b]
+    __shared__ int pp[128], qq[128], order[256];
+    __shared__ T cs[128], sn[128];
+    __shared__ int converged;
+    const int j = blockIdx.x, tid = threadIdx.x;
+    const int half = b / 2;
+    const double* g = gram + static_cast<int64_t>(j) * b * b;
+    for (int i = tid; i < b * b; i += 256) {
+        A[i] = static_cast<T>(g[i]);
+        V[i] = (i / b == i % b) ? T(1) : T(0);
+    }
+    // converged when every off-diagonal entry is below tol times the largest
+    // diagonal entry (the rounding floor of the rotations is about eps times
+    // the matrix norm), or after 15 sweeps
+    const T tol = sizeof(T) == 8 ? T(1e-14) : T(2e-6);
+    __shared__ T dmax;
+    __syncthreads();
+    if (tid == 0) {
+        T d = T(0);
+        for (int i = 0; i < b; ++i) d = fmax(d, fabs(A[i * b + i]));
+        dmax = d;
+    }
+    for (int sweep = 0; sweep < 15; ++sweep) {
+        __syncthreads();
+        if (tid == 0) converged = 1;
+        __syncthreads();
+        const T lim = tol * dmax;
+        for (int i = tid; i < b * b; i += 256) {
+            const int r = i / b, c = i - r * b;
+            if (r < c && fabs(A[i]) > lim) converged = 0;
+        }
+        __syncthreads();
+        if (converged) break;
+        for (int round = 0; round < b - 1; ++round) {
+            if (tid < half) {
+                const int li = tid, lj = b - 1 - tid;
+                const int p = li == 0 ? 0 : (round + li - 1) % (b - 1) + 1;
+                const int q = (round + lj - 1) % (b - 1) + 1;
+                const T apq = A[p * b + q];
+                T c = T(1), s = T(0);
+                if (apq != T(0)) {
+                    const T tau = (A[q * b + q] - A[p * b + p]) / (T(2) * apq);
+                    const T t = (tau >= T(0) ? T(1) : T(-1)) / (fabs(tau) + sqrt(T(1) + tau * tau));
+                    c = T(1) / sqrt(T(1) + t * t);
+                    s = t * c;
+                }
+                pp[tid] = p; qq[tid] = q; cs[tid] = c; sn[tid] = s;
+            }
+            __syncthreads();
+            // rows: A <- J^T A
+            for (int i = tid; i < half * b; i += 256) {
+                const int pr = i / b, col = i - pr * b;
+                const int p = pp[pr], q = qq[pr];
+                const T c = cs[pr], s = sn[pr];
+                const T ap = A[p * b + col], aq = A[q * b + col];
+                A[p * b + col] = c * ap - s * aq;
+                A[q * b + col] = s * ap + c * aq;
+            }
+            __syncthreads();
+            // columns: A <- A J, V <- V J
+            for (int i = tid; i < half * b; i += 256) {
+                const int pr = i / b, row = i - pr * b;
+                const int p = pp[pr], q = qq[pr];
+                const T c = cs[pr], s = sn[pr];
+                const T ap = A[row * b + p], aq = A[row * b + q];
+                A[row * b + p] = c * ap - s * aq;
+                A[row * b + q] = s * ap + c * aq;
+                const T vp = V[row * b + p], vq = V[row * b + q];
+                V[row * b + p] = c * vp - s * vq;
+                V[row * b + q] = s * vp + c * vq;
+            }
+            __syncthreads();
+        }
+    }
+    __syncthreads();
+    // descending eigenvalues (lower index first on ties): position of column i
+    if (tid < b) {
+        const T d = A[tid * b + tid];
+        int rank = 0;
+        for (int l = 0; l < b; ++l) {
+            const T e = A[l * b + l];
+            rank += (e > d || (e == d && l < tid)) ? 1 : 0;
+        }
+        order[rank] = tid;
+    }
+    __syncthreads();
+    // U[:, r] = +-V[:, order[r]] with its largest-magnitude entry positive,
+    // then R = U H / sqrt(b), H[l][c] = (-1)^popcount(l & c)
+    __shared__ T sgn[256];
+    if (tid < b) {
+        const int col = order[tid];
+        int best = 0;
+        T bv = T(-1);
+        for (int r = 0; r < b; ++r) {
+            const T a = fabs(V[r * b + col]);
+            if (a > bv) { bv = a; best = r; }
+        }
+        sgn[tid] = V[best * b + col] < T(0) ? T(-1) : T(1);
+    }
+    __syncthreads();
+    const double nrm = 1.0 / sqrt(static_cast<double>(b));
+    float* out = rot + static_cast<int64_t>(j) * b * b;
+    for (int i = tid; i < b * b; i += 256) {
+        const int a = i / b, c = i - a * b;
+        double acc = 0.0;
+        for (int l = 0; l < b; ++l) {
+            const double u = static_cast<double>(V[a * b + order[l]]) * static_cast<double>(sgn[l]);
+            acc += (__builtin_popcount(l & c) & 1) ? -u : u;
+        }
+        out[i] = static_cast<float>(acc * nrm);
+    }
+}
+
+template <int DT>
+hipError_t launch_rot_dt(const CompParams& p, hipStream_t st) {
+    const int rt = 8 * 256 / p.b;
+    const size_t lds = static_cast<size_t>(p.b) * p.b * 4 + static_cast<size_t>(rt) * p.b * 8;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(composite_rotate_kernel<DT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    dim3 grid(static_cast<unsigned>(p.k / p.b), static_cast<unsigned>((p.m + rt - 1) / rt));
+    hipLaunchKernelGGL(composite_rotate_kernel<DT>, grid, dim3(256), lds, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_composite_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx, const float* mult,
+                                  const int32_t* perm, const float* rot, int b, int bits, void* q, float* scale,
+                                  float* v, hipStream_t st) {
+    CompParams p;
+    p.x = x; p.m = m; p.k = k; p.ldx = ldx; p.mult = mult; p.perm = perm; p.rot = rot; p.b = b; p.v = v;
+    hipError_t e = hipErrorInvalidValue;
+    switch (dtype) {
+        case F16: e = launch_rot_dt<F16>(p, st); break;
+        case BF16: e = launch_rot_dt<BF16>(p, st); break;
+        case F32: e = launch_rot_dt<F32>(p, st); break;
+    }
+    if (e != hipSuccess) return e;
+    // the rotated rows are then quantized per row as they stand (no fold, no rotation)
+    return launch_rotate_quant(v, F32, m, k, k, false, nullptr, 0, bits, q, scale, st);
+}
+
+hipError_t launch_calibrate_composite(const void* w, int dtype, int64_t n, int64_t k, const float* fold, int b,
+                                      int32_t* perm, float* rot, void* work, hipStream_t st) {
+    // work: chunks * k doubles (column partials), then k doubles (norms),
+    // then k * b doubles (Gram matrices)
+    const int64_t chunks = (n + 255) / 256;
+    double* part = static_cast<double*>(work);
+    double* norm2 = part + chunks * k;
+    double* gram = norm2 + k;
+    const dim3 cg(static_cast<unsigned>((k + 255) / 256), static_cast<unsigned>(chunks));
+    const dim3 kg(static_cast<unsigned>((k + 255) / 256));
+    const dim3 gg(static_cast<unsigned>(k / b), static_cast<unsigned>((b / 16) * (b / 16)));
+    switch (dtype) {
+        case F16: hipLaunchKernelGGL(colnorm_part_kernel<F16>, cg, dim3(256), 0, st, w, n, k, fold, part); break;
+        case BF16: hipLaunchKernelGGL(colnorm_part_kernel<BF16>, cg, dim3(256), 0, st, w, n, k, fold, part); break;
+        case F32: hipLaunchKernelGGL(colnorm_part_kernel<F32>, cg, dim3(256), 0, st, w, n, k, fold, part); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(colnorm_sum_kernel, kg, dim3(256), 0, st, part, chunks, k, norm2);
+    hipLaunchKernelGGL(zigzag_kernel, kg, dim3(256), 0, st, norm2, k, b, perm);
+    switch (dtype) {
+        case F16: hipLaunchKernelGGL(gram_kernel<F16>, gg, dim3(256), 0, st, w, n, k, fold, perm, b, gram); break;
+        case BF16: hipLaunchKernelGGL(gram_kernel<BF16>, gg, dim3(256), 0, st, w, n, k, fold, perm, b, gram); break;
+        case F32: hipLaunchKernelGGL(gram_kernel<F32>, gg, dim3(256), 0, st, w, n, k, fold, perm, b, gram); break;
+    }
+    if (b <= 64) {
+        const size_t lds = static_cast<size_t>(2) * b * b * 8;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_rot_kernel<double>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(jacobi_rot_kernel<double>, dim3(static_cast<unsigned>(k / b)), dim3(256), lds, st,
+                           gram, b, rot);
+    } else {
+        const size_t lds = static_cast<size_t>(2) * b * b * 4;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(jacobi_rot_kernel<float>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(jacobi_rot_kernel<float>, dim3(static_cast<unsigned>(k / b)), dim3(256), lds, st,
+                           gram, b, rot);
+    }
+    return hipGetLastError();
+}
+
+int64_t composite_calib_work_bytes(int64_t n, int64_t k, int b) {
+    const int64_t chunks = (n + 255) / 256;
+    return (chunks * k + k + k * b) * 8;
+}
+
+}  // namespace qlin

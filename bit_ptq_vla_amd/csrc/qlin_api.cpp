@@ -134,6 +134,31 @@ qlin_status table_rows_check(const void* x, qlin_dtype dt, int64_t rows, int64_t
     return QLIN_OK;
 }
 
+// Shared checks of the composite-rotation entry points.
+qlin_status composite_check(const void* x, qlin_dtype dt, int64_t rows, int64_t k, int64_t ldx, int32_t b) {
+    if (rows > 0 && !x) return QLIN_ERR_NULL;
+    if (!is_float_in(dt)) return QLIN_ERR_DTYPE;
+    if (b != 16 && b != 32 && b != 64 && b != 128) return QLIN_ERR_UNSUPPORTED;
+    if (rows < 0 || k < b || (k % b) != 0 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < k) return QLIN_ERR_SHAPE;
+    if (k > kMaxRowK) return QLIN_ERR_SHAPE;
+    return QLIN_OK;
+}
+
+// The rotated rows (fp32 [rows][k]) go through a stream-ordered workspace.
+qlin_status composite_run(const void* x, qlin_dtype dt, int64_t rows, int64_t k, int64_t ldx, const float* mult,
+                          const int32_t* perm, const float* rot, int32_t b, int32_t bits, void* q, float* scale,
+                          float* work, void* stream) {
+    hipStream_t s = as_stream(stream);
+    if (work) return map_err(qlin::launch_composite_quant(x, dt, rows, k, ldx, mult, perm, rot, b, bits, q, scale,
+                                                          work, s));
+    float* v = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void**>(&v), static_cast<size_t>(rows * k * 4), s) != hipSuccess)
+        return QLIN_ERR_DEVICE;
+    hipError_t e = qlin::launch_composite_quant(x, dt, rows, k, ldx, mult, perm, rot, b, bits, q, scale, v, s);
+    if (hipFreeAsync(v, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
+    return map_err(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,6 +300,73 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
     if (st != QLIN_OK) return st;
     return map_err(qlin::launch_rotate_quant_table(w, w_dtype, n, k, k, fold_s, had_block, bits, table, true,
                                                    wq, w_scale, as_stream(stream)));
+}
+
+qlin_status qlin_calibrate_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                     const float* fold_s, int32_t had_block, int32_t* perm, float* rot,
+                                     void* stream) {
+    qlin_status st = composite_check(w, w_dtype, n, k, k, had_block);
+    if (st != QLIN_OK) return st;
+    if (!w || !perm || !rot) return QLIN_ERR_NULL;
+    if (n < 1) return QLIN_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot)) return QLIN_ERR_ALIGN;
+    const Span outs[2] = {{perm, k * 4}, {rot, k * had_block * 4}};
+    const Span ins[2] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}};
+    if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    hipStream_t s = as_stream(stream);
+    void* work = nullptr;
+    const int64_t bytes = qlin::composite_calib_work_bytes(n, k, had_block);
+    if (hipMallocAsync(&work, static_cast<size_t>(bytes), s) != hipSuccess) return QLIN_ERR_DEVICE;
+    hipError_t e = qlin::launch_calibrate_composite(w, w_dtype, n, k, fold_s, had_block, perm, rot, work, s);
+    if (hipFreeAsync(work, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
+    return map_err(e);
+}
+
+qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                            int64_t ldx, const float* fold_inv_s, const int32_t* perm,
+                                            const float* rot, int32_t had_block, int32_t bits, void* xq,
+                                            float* x_scale, float* work, void* stream) {
+    qlin_status st = composite_check(x, x_dtype, m, k, ldx, had_block);
+    if (st != QLIN_OK) return st;
+    if (!perm || !rot) return QLIN_ERR_NULL;
+    if (m > 0 && (!xq || !x_scale)) return QLIN_ERR_NULL;
+    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(fold_inv_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(xq) ||
+        !aligned16(x_scale) || !aligned16(work))
+        return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
+    const Span outs[3] = {{xq, code_bytes}, {x_scale, m * 4}, {work, work ? m * k * 4 : 0}};
+    const Span ins[4] = {{x, m > 0 ? ((m - 1) * ldx + k) * dtype_size(x_dtype) : 0},
+                         {fold_inv_s, fold_inv_s ? k * 4 : 0}, {perm, k * 4}, {rot, k * had_block * 4}};
+    if (any_overlap(outs, 3, ins, 4)) return QLIN_ERR_ALIAS;
+    if (m == 0) return QLIN_OK;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    return composite_run(x, x_dtype, m, k, ldx, fold_inv_s, perm, rot, had_block, bits, xq, x_scale, work, stream);
+}
+
+qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                            const float* fold_s, const int32_t* perm, const float* rot,
+                                            int32_t had_block, int32_t bits, void* wq, float* w_scale,
+                                            void* stream) {
+    qlin_status st = composite_check(w, w_dtype, n, k, k, had_block);
+    if (st != QLIN_OK) return st;
+    if (!w || !perm || !rot || !wq || !w_scale) return QLIN_ERR_NULL;
+    if (n < 1) return QLIN_ERR_SHAPE;
+    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(wq) ||
+        !aligned16(w_scale))
+        return QLIN_ERR_ALIGN;
+    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
+    const Span outs[2] = {{wq, code_bytes}, {w_scale, n * 4}};
+    const Span ins[4] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}, {perm, k * 4},
+                         {rot, k * had_block * 4}};
+    if (any_overlap(outs, 2, ins, 4)) return QLIN_ERR_ALIAS;
+    st = check_device();
+    if (st != QLIN_OK) return st;
+    return composite_run(w, w_dtype, n, k, k, fold_s, perm, rot, had_block, bits, wq, w_scale, nullptr, stream);
 }
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

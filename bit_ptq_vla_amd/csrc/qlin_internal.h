@@ -31,6 +31,18 @@ hipError_t launch_calibrate_step_scales(const void* x, int dtype, int64_t m, int
                                         const float* mult, int had_block, int bits, float* table,
                                         hipStream_t st);
 
+// SVD-Hadamard composite rotation (b in 16..128): rows gathered by perm,
+// folded, rotated per block by rot[k/b][b][b] into v (fp32 [m][k], caller's
+// workspace), then per-row quantized.
+hipError_t launch_composite_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx, const float* mult,
+                                  const int32_t* perm, const float* rot, int b, int bits, void* q, float* scale,
+                                  float* v, hipStream_t st);
+// Calibration of perm and rot from weights [n][k] (times fold); `work` holds
+// composite_calib_work_bytes(n, k, b) bytes.
+int64_t composite_calib_work_bytes(int64_t n, int64_t k, int b);
+hipError_t launch_calibrate_composite(const void* w, int dtype, int64_t n, int64_t k, const float* fold, int b,
+                                      int32_t* perm, float* rot, void* work, hipStream_t st);
+
 hipError_t launch_calibrate_fold(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
                                  bool geglu, const void* w, int w_dtype, int64_t n, float* s,
                                  float* inv_s, hipStream_t st);

@@ -178,6 +178,54 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
                                        const float* table, void* wq, float* w_scale, void* stream);
 
 /*
+ * SVD-Hadamard composite rotation with the zigzag permutation (Omega-QVLA
+ * technical summary, Metodologia 1: "Rotazione SVD", "Rotazione Hadamard",
+ * "Implementazione a Blocchi").  In place of the fast Hadamard block of
+ * qlin_rotate_quant_act / qlin_quantize_weights, each row is gathered by a
+ * channel permutation and multiplied, block by block of b channels, by a
+ * dense b x b rotation R_j:
+ *   v[c'] = x[perm[c']] * fold[perm[c']];   v[B_j] = v[B_j] @ R_j
+ * then quantized per row (x_scale / w_scale = fp32(max |v| / qmax), codes
+ * clamp(rne(v / scale), +-qmax), layouts as the Hadamard entry points; codes
+ * are in the permuted channel order on both sides, so the GEMM is unchanged).
+ * The dot products take fp32 operands with an fp64 sum, rounded to fp32;
+ * the rotated rows pass through fp32 [rows][k] scratch: `work` when given
+ * (device, 16-byte aligned, rows * k floats, contents overwritten), else a
+ * stream-ordered temporary.
+ *
+ * qlin_calibrate_composite -- perm and R from the weights w [n][k] (times
+ *   fold_s): channels ranked by descending L2 norm of their column (lower
+ *   index first on ties) are dealt to the k / b blocks in snake order (rank
+ *   r, round t = r / (k/b), i = r % (k/b): block i on even rounds, k/b-1-i on
+ *   odd ones, slot t).  Per block j, U_j = eigenvectors of the Gram matrix
+ *   W[:, B_j]^T W[:, B_j] (the page's R_SVD = U of W = U S V^T with W stored
+ *   C_in x C_out) by descending eigenvalue, each with its largest-magnitude
+ *   entry positive; R_j = U_j H_b / sqrt(b) (Sylvester H).  Eigenvectors of
+ *   repeated eigenvalues are any orthonormal basis of their space.
+ *   perm: out int32[k]; rot: out float[k/b][b][b].  Takes a temporary of
+ *   about 8 (k b + k n / 256 + k) bytes from the stream-ordered allocator.
+ * qlin_rotate_quant_act_composite -- activations x [m][ldx] with fold_inv_s
+ *   (1/s or NULL), perm and rot as written by the calibration; xq, x_scale out.
+ * qlin_quantize_weights_composite -- weights w [n][k] with fold_s (s or
+ *   NULL); wq, w_scale out.
+ * Preconditions: had_block b in {16, 32, 64, 128} dividing k; k % 8 == 0;
+ * k <= 32768; bits 4 or 8;
+ * perm a permutation of 0 .. k-1 (other values are clamped into range).
+ * Errors as the Hadamard entry points.
+ */
+qlin_status qlin_calibrate_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                     const float* fold_s, int32_t had_block, int32_t* perm, float* rot,
+                                     void* stream);
+qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
+                                            int64_t ldx, const float* fold_inv_s, const int32_t* perm,
+                                            const float* rot, int32_t had_block, int32_t bits, void* xq,
+                                            float* x_scale, float* work, void* stream);
+qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
+                                            const float* fold_s, const int32_t* perm, const float* rot,
+                                            int32_t had_block, int32_t bits, void* wq, float* w_scale,
+                                            void* stream);
+
+/*
  * qlin_gemm_w4a4 / qlin_gemm_w8a8 -- integer GEMM with int32 accumulation
  * and a fused dequantizing epilogue (FoldQuantVLA abstract: native integer
  * execution of the projections).

@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     for n in ("qlin_rotate_quant_act", "qlin_quantize_weights", "qlin_gemm_w4a4", "qlin_gemm_w8a8", "qlin_gemm_w4a8",
               "qlin_gemm_w4a4_geglu", "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version",
               "qlin_status_string", "qlin_calibrate_step_scales", "qlin_rotate_quant_act_static",
-              "qlin_quantize_weights_step"):
+              "qlin_quantize_weights_step", "qlin_calibrate_composite", "qlin_rotate_quant_act_composite",
+              "qlin_quantize_weights_composite"):
         assert n in names
 
 
@@ -235,6 +236,59 @@ def test_quantize_weights_step_rejects(lib, kw, status):
     a.update(kw)
     assert lib.qlin_quantize_weights_step(a["w"], a["dt"], a["n"], a["k"], a["s"], a["b"], a["bits"], a["t"],
                                           a["wq"], a["ws"], None) == status
+
+
+# ---- composite rotation entry points
+
+# qlin_calibrate_composite(w, dt, n, k, fold_s, b, perm, rot, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), q.QLIN_ERR_NULL), (dict(perm=None), q.QLIN_ERR_NULL), (dict(rot=None), q.QLIN_ERR_NULL),
+    (dict(dt=3), q.QLIN_ERR_DTYPE), (dict(b=8), q.QLIN_ERR_UNSUPPORTED), (dict(b=256), q.QLIN_ERR_UNSUPPORTED),
+    (dict(b=48), q.QLIN_ERR_UNSUPPORTED), (dict(n=0), q.QLIN_ERR_SHAPE), (dict(k=520), q.QLIN_ERR_SHAPE),
+    (dict(k=65536), q.QLIN_ERR_SHAPE), (dict(rot=BAD), q.QLIN_ERR_ALIGN), (dict(s=BAD), q.QLIN_ERR_ALIGN),
+    (dict(perm=P + 64), q.QLIN_ERR_ALIAS), (dict(rot=P3 + 512), q.QLIN_ERR_ALIAS),
+])
+def test_calibrate_composite_rejects(lib, kw, status):
+    a = dict(w=P, dt=0, n=16, k=512, s=None, b=64, perm=P3, rot=P4)
+    a.update(kw)
+    assert lib.qlin_calibrate_composite(a["w"], a["dt"], a["n"], a["k"], a["s"], a["b"], a["perm"], a["rot"],
+                                        None) == status
+
+
+# qlin_rotate_quant_act_composite(x, dt, m, k, ldx, inv_s, perm, rot, b, bits, xq, xs, work, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(work=BAD), q.QLIN_ERR_ALIGN), (dict(work=P2 + 512), q.QLIN_ERR_ALIAS), (dict(work=P + 1024), q.QLIN_ERR_ALIAS),
+    (dict(x=None), q.QLIN_ERR_NULL), (dict(perm=None), q.QLIN_ERR_NULL), (dict(xq=None), q.QLIN_ERR_NULL),
+    (dict(xs=None), q.QLIN_ERR_NULL), (dict(dt=5), q.QLIN_ERR_DTYPE), (dict(b=4), q.QLIN_ERR_UNSUPPORTED),
+    (dict(bits=2), q.QLIN_ERR_UNSUPPORTED), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(ldx=256), q.QLIN_ERR_SHAPE),
+    (dict(k=65536, ldx=65536, b=128), q.QLIN_ERR_SHAPE), (dict(xq=BAD), q.QLIN_ERR_ALIGN),
+    (dict(perm=BAD), q.QLIN_ERR_ALIGN), (dict(xq=P + 32), q.QLIN_ERR_ALIAS), (dict(xs=P4 + 16), q.QLIN_ERR_ALIAS),
+])
+def test_rotate_quant_act_composite_rejects(lib, kw, status):
+    a = dict(x=P, dt=1, m=4, k=512, ldx=512, inv=None, perm=P3, rot=P4, b=64, bits=4, xq=P2, xs=0x70000000,
+             work=None)
+    a.update(kw)
+    assert lib.qlin_rotate_quant_act_composite(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["inv"], a["perm"],
+                                               a["rot"], a["b"], a["bits"], a["xq"], a["xs"], a["work"],
+                                               None) == status
+
+
+def test_rotate_quant_act_composite_empty_is_ok(lib):
+    assert lib.qlin_rotate_quant_act_composite(None, 0, 0, 512, 512, None, P3, P4, 64, 4, None, None, None,
+                                               None) == q.QLIN_OK
+
+
+# qlin_quantize_weights_composite(w, dt, n, k, fold_s, perm, rot, b, bits, wq, ws, stream)
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), q.QLIN_ERR_NULL), (dict(rot=None), q.QLIN_ERR_NULL), (dict(ws=None), q.QLIN_ERR_NULL),
+    (dict(b=512), q.QLIN_ERR_UNSUPPORTED), (dict(bits=3), q.QLIN_ERR_UNSUPPORTED), (dict(n=0), q.QLIN_ERR_SHAPE),
+    (dict(k=96), q.QLIN_ERR_SHAPE), (dict(wq=BAD), q.QLIN_ERR_ALIGN), (dict(wq=P + 128), q.QLIN_ERR_ALIAS),
+])
+def test_quantize_weights_composite_rejects(lib, kw, status):
+    a = dict(w=P, dt=0, n=8, k=512, s=None, perm=P3, rot=P4, b=64, bits=4, wq=P2, ws=0x70000000)
+    a.update(kw)
+    assert lib.qlin_quantize_weights_composite(a["w"], a["dt"], a["n"], a["k"], a["s"], a["perm"], a["rot"],
+                                               a["b"], a["bits"], a["wq"], a["ws"], None) == status
 
 
 def test_binding_raises_qlin_error(lib):

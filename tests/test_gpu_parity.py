@@ -193,6 +193,114 @@ def test_quantize_weights_step_parity(n, k, b, bits, dtype, fold):
     assert_ok(oracle.compare_scales(ws.cpu().numpy(), s_ref), "scales")
 
 
+# ---------------------------------------------------------------- composite rotation
+
+COMPOSITE_CASES = [
+    # m, k, b, bits, dtype, fold
+    (50, 1024, 64, 4, "f16", True),      # action-expert width
+    (37, 2048, 128, 4, "bf16", True),    # backbone hidden
+    (5, 16384, 128, 8, "bf16", True),    # down input width: one row per block
+    (300, 512, 32, 8, "f32", False),     # several row groups per block
+    (9, 256, 16, 4, "f16", False),
+]
+
+
+def _composite_weights(n, k, dtype, tag):
+    w = synth.normal_tensor(SEED, f"cw/{tag}/{n}/{k}", (n, k), std=0.02, dtype=dtype)
+    # channel norms spread over two decades, so the zigzag deal matters
+    spread = torch.from_numpy((10.0 ** np.random.default_rng(k).uniform(-1, 1, size=k)).astype(np.float32))
+    return (w.float() * spread[None, :]).to(w.dtype)
+
+
+@pytest.mark.parametrize("m,k,b,bits,dtype,fold", COMPOSITE_CASES)
+def test_composite_quant_parity(m, k, b, bits, dtype, fold):
+    """Activations and weights with the oracle's permutation and rotations
+    (fp32) as inputs: codes and scales against the oracle."""
+    say(f"composite quant m={m} k={k} b={b} bits={bits} {dtype}")
+    x = synth.normal_tensor(SEED, f"cx/{m}/{k}", (m, k), dtype=dtype, outliers=max(1, k // 100), outlier_scale=25.0)
+    x[m // 2] = 0
+    w = _composite_weights(64, k, dtype, "q")
+    s = synth.random_scales(SEED, f"cfold/{k}", k) * 100.0 if fold else None
+    sg = s.numpy() if fold else None
+    wf = synth.to_f64(w) * (sg.astype(np.float64)[None, :] if fold else 1.0)
+    perm = oracle.zigzag_permutation(wf, b)
+    rot = oracle.composite_rotations(wf, perm, b).astype(np.float32)
+    pd, rd = torch.from_numpy(perm.astype(np.int32)).to(DEV), torch.from_numpy(rot).to(DEV)
+    inv = (1.0 / s).to(DEV) if fold else None
+    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), pd, rd, fold_inv_s=inv, bits=bits)
+    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), pd, rd, fold_s=s.to(DEV) if fold else None, bits=bits)
+    torch.cuda.synchronize()
+    qx_ref, sx_ref, rx = oracle.rotate_quant_act_composite(synth.to_f64(x), sg, perm, rot, bits)
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), sx_ref), "act scales")
+    assert_ok(oracle.compare_codes(codes_np(xq, bits), qx_ref, rx), "act codes")
+    assert xs[m // 2].item() == 0.0
+    qw_ref, sw_ref, rw = oracle.quantize_weights_composite(synth.to_f64(w), sg, perm, rot, bits)
+    assert_ok(oracle.compare_scales(ws.cpu().numpy(), sw_ref), "weight scales")
+    assert_ok(oracle.compare_codes(codes_np(wq, bits), qw_ref, rw), "weight codes")
+
+
+@pytest.mark.parametrize("n,k,b,dtype,fold", [(96, 1024, 64, "f16", True), (256, 2048, 128, "bf16", True),
+                                               (40, 512, 16, "f32", False), (64, 256, 32, "f16", False)])
+def test_calibrate_composite_parity(n, k, b, dtype, fold):
+    """The zigzag permutation equals the oracle's; each rotation is
+    orthogonal, turns its block's weight columns into orthogonal columns
+    with the oracle's eigenvalues as energies, and matches the oracle's
+    rotation column for column where the eigenvalue is well separated."""
+    say(f"composite calibrate n={n} k={k} b={b} {dtype}")
+    w = _composite_weights(n, k, dtype, "c")
+    s = synth.random_scales(SEED, f"ccfold/{k}", k) * 100.0 if fold else None
+    perm, rot = q.qlin_calibrate_composite(w.to(DEV), b, fold_s=s.to(DEV) if fold else None)
+    torch.cuda.synchronize()
+    wf = synth.to_f64(w) * (s.numpy().astype(np.float64)[None, :] if fold else 1.0)
+    perm_ref = oracle.zigzag_permutation(wf, b)
+    assert np.array_equal(perm.cpu().numpy().astype(np.int64), perm_ref)
+    rot_ref = oracle.composite_rotations(wf, perm_ref, b)
+    h = oracle.sylvester_hadamard(b) / np.sqrt(b)
+    got = rot.cpu().numpy().astype(np.float64)
+    tol = 1e-5 if b <= 64 else 1e-4          # fp64 Jacobi up to b = 64, fp32 at 128
+    wp = wf[:, perm_ref]
+    for j in range(k // b):
+        r = got[j]
+        assert np.abs(r @ r.T - np.eye(b)).max() < tol, f"block {j} not orthogonal"
+        u = r @ h.T
+        blk = wp[:, j * b:(j + 1) * b]
+        z = blk @ u
+        ev = np.linalg.eigvalsh(blk.T @ blk)[::-1]
+        energies = (z * z).sum(axis=0)
+        assert np.abs(energies - ev).max() <= tol * ev[0] * 10, f"block {j} energies"
+        u_ref = rot_ref[j] @ h.T
+        gap = np.minimum(np.abs(np.diff(ev, prepend=np.inf)), np.abs(np.diff(ev, append=-np.inf)))
+        sep = gap > 1e-2 * ev[0]
+        assert np.abs(u[:, sep] - u_ref[:, sep]).max() < 1e-2, f"block {j} eigenvectors"
+
+
+def test_composite_linear_end_to_end():
+    """Calibrate on the GPU, quantize both sides with the GPU's permutation
+    and rotations, W4A4 GEMM: each stage against the oracle on the same
+    inputs, and the projection against x w^T."""
+    say("composite linear 50x1024x1024")
+    wl = synth.CFG3
+    pr = wl.projs[0]
+    w = synth.weight(wl, pr)
+    x = synth.activation(wl, pr, 50, tag="/t0", std=synth.cfg3_sigma(0))
+    perm, rot = q.qlin_calibrate_composite(w.to(DEV), 64)
+    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), perm, rot, bits=4)
+    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), perm, rot, bits=4)
+    y = q.qlin_gemm_w4a4(xq, xs, wq, ws, pr.k, y_dtype=torch.float16)
+    torch.cuda.synchronize()
+    pg, rg = perm.cpu().numpy().astype(np.int64), rot.cpu().numpy()
+    qx_ref, sx_ref, rx = oracle.rotate_quant_act_composite(synth.to_f64(x), None, pg, rg, 4)
+    assert_ok(oracle.compare_codes(codes_np(xq, 4), qx_ref, rx), "act codes")
+    assert_ok(oracle.compare_scales(xs.cpu().numpy(), sx_ref), "act scales")
+    rws = _sample_rows(pr.n, 32)
+    qw_ref, sw_ref, rw = oracle.quantize_weights_composite(synth.to_f64(w[rws]), None, pg, rg, 4)
+    assert_ok(oracle.compare_codes(codes_np(wq, 4)[rws], qw_ref, rw), "weight codes")
+    _, _, y_ref = oracle.gemm(codes_np(xq, 4), xs.cpu().numpy(), codes_np(wq, 4), ws.cpu().numpy(), "f16")
+    assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+    y_true = synth.to_f64(x) @ synth.to_f64(w).T
+    assert np.linalg.norm(f64(y) - y_true) / np.linalg.norm(y_true) < 0.3
+
+
 def test_rotate_quant_act_strided_rows():
     say("act strided ldx")
     x = synth.normal_tensor(SEED, "strided", (12, 1536), dtype="f16")
