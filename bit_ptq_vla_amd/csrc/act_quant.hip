@@ -357,7 +357,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
         for (int c = 0; c < NCH; ++c) {
             decode_chunk<DT, GEGLU>(raw[c], gtab, v[c]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[c][e] = col_ok[c] ? v[c][e] * mlt[c][e] : 0.f;
+            for (int e = 0; e < 8; ++e) v[c][e] = col_ok[c] ? mul_rn(v[c][e], mlt[c][e]) : 0.f;
 #pragma unroll
             for (int h = 1; h < 8; h <<= 1) {
                 if (h < b) {
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p
                 for (int e = 0; e < 8; ++e) x[e] *= gl[e];
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[c][e] = x[e] * mlt[c][e];
+            for (int e = 0; e < 8; ++e) v[c][e] = mul_rn(x[e], mlt[c][e]);
 #pragma unroll
             for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll

@@ -90,6 +90,15 @@ __device__ __forceinline__ void load8<F32>(const void* p, float f[8]) {
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
+// fp32 product rounded on its own, never fused into a following add.  The
+// fold multiply feeds the first Hadamard butterfly; left to the compiler, it
+// becomes fma(x0, m0, x1 * m1) in some kernels and not in others, and
+// kernels that must produce the same codes would then round differently.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 // ---- wave64 cross-lane helpers -------------------------------------------
 
 // Value held by lane (lane ^ mask).  For mask < 32 this is ds_swizzle in
@@ -104,12 +113,22 @@ __device__ __forceinline__ float lane_xor(float v) {
     }
 }
 
+// Value a DPP move brings in (no LDS round trip); 0 from a disabled lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_max(float v, int width) {
     // width is a power of two <= 64; reduce within aligned groups of `width`.
-    if (width >= 2) v = fmaxf(v, lane_xor<1>(v));
-    if (width >= 4) v = fmaxf(v, lane_xor<2>(v));
-    if (width >= 8) v = fmaxf(v, lane_xor<4>(v));
-    if (width >= 16) v = fmaxf(v, lane_xor<8>(v));
+    // Within a 16-lane row by DPP: the two quad swaps leave every quad
+    // holding its maximum, so the half-row mirror (lane i <- 7 - i) then
+    // meets the other quad and the row mirror (i <- 15 - i) the other half.
+    // Inputs are magnitudes (>= 0), for which a disabled lane's 0 is neutral.
+    if (width >= 2) v = fmaxf(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+    if (width >= 4) v = fmaxf(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+    if (width >= 8) v = fmaxf(v, dpp_mov<0x141>(v));   // row_half_mirror
+    if (width >= 16) v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
     if (width >= 32) v = fmaxf(v, lane_xor<16>(v));
     if (width >= 64) v = fmaxf(v, lane_xor<32>(v));
     return v;

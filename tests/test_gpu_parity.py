@@ -312,6 +312,23 @@ def test_rotate_quant_act_strided_rows():
     assert_ok(oracle.compare_codes(codes_np(xq, 4), q_ref, r_ref), "codes")
 
 
+@pytest.mark.parametrize("k,b,bits", [(1024, 64, 4), (4096, 128, 4), (2048, 64, 8)])
+def test_rotate_quant_act_bf16_path_rounds_like_f32(k, b, bits):
+    """bf16 rows take their own kernel at b = 64 / 128; fed the same values
+    as f32 (exact), the general kernel must give the same codes and scales
+    bit for bit: each fold product is rounded to fp32 before the first
+    butterfly in both (a product fused into that add would differ by an ulp
+    in some rows)."""
+    say(f"act bf16 vs f32 k={k} b={b} bits={bits}")
+    x = synth.normal_tensor(SEED, f"bf16f32/{k}", (37, k), dtype="bf16", outliers=k // 100, outlier_scale=20.0)
+    inv = (1.0 / (synth.random_scales(SEED, f"bf16f32/fold/{k}", k) * 100.0)).to(DEV)
+    xq1, xs1 = q.qlin_rotate_quant_act(x.to(DEV), fold_inv_s=inv, had_block=b, bits=bits)
+    xq2, xs2 = q.qlin_rotate_quant_act(x.float().to(DEV), fold_inv_s=inv, had_block=b, bits=bits)
+    torch.cuda.synchronize()
+    assert torch.equal(xs1.view(torch.int32), xs2.view(torch.int32))
+    assert torch.equal(xq1, xq2)
+
+
 # ---------------------------------------------------------------- weight stage
 
 WQ_CASES = [
