@@ -98,14 +98,6 @@ enum RowQuantMode { ROWQ_DYNAMIC = 0, ROWQ_STATIC = 1, ROWQ_POSTMUL = 2, ROWQ_CO
           "+v"(w[6]), "+v"(w[7])                                                       \
         : "v"(sgn))
 
-// Lane distance 4: banks 0 and 2 of a 16-lane row take lane + 4 (rotation
-// by 12), banks 1 and 3 take lane - 4 (rotation by 4), into a temporary,
-// then one multiply-add.
-#define QLIN_DPP4_ONE(I)                                                               \
-    "v_mov_b32_dpp %9, %" #I " row_ror:12 row_mask:0xf bank_mask:0x5\n\t"              \
-    "v_mov_b32_dpp %9, %" #I " row_ror:4 row_mask:0xf bank_mask:0xa\n\t"               \
-    "v_fmac_f32_e32 %" #I ", %9, %8\n\t"
-
 template <int D>
 __device__ __forceinline__ void xlane8(float (&w)[8], float sgn) {
     if constexpr (D == 1) {
@@ -114,16 +106,14 @@ __device__ __forceinline__ void xlane8(float (&w)[8], float sgn) {
         QLIN_DPP_FMAC8("quad_perm:[2,3,0,1]");
     } else if constexpr (D == 8) {
         QLIN_DPP_FMAC8("row_ror:8");
-    } else if constexpr (D == 4) {
-        float t;
-        asm("s_nop 1\n\t" QLIN_DPP4_ONE(0) QLIN_DPP4_ONE(1) QLIN_DPP4_ONE(2) QLIN_DPP4_ONE(3)
-                QLIN_DPP4_ONE(4) QLIN_DPP4_ONE(5) QLIN_DPP4_ONE(6) QLIN_DPP4_ONE(7)
-            : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]),
-              "+v"(w[7]), "+v"(sgn), "=&v"(t));
     } else {
-        // D = 16 crosses 16-lane rows: ds_swizzle
+        // D = 4 (no single DPP pattern: two moves would be needed) and D = 16
+        // (crosses 16-lane rows): ds_swizzle, one VALU instruction per value
+        float t[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = fmaf(lane_xor<D>(w[e]), sgn, w[e]);
+        for (int e = 0; e < 8; ++e) t[e] = lane_xor<D>(w[e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = fmaf(t[e], sgn, w[e]);
     }
 }
 
@@ -407,7 +397,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[c][e]));
+            for (int e = 0; e < 8; e += 2) amax = max3_abs(amax, v[c][e], v[c][e + 1]);
         amax = wave_max(amax, g < 64 ? g : 64);
         if (g > 64) {
             if (lane == 0) red[parity][wave] = amax;
@@ -512,42 +502,24 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
 // ---- bfloat16 fast path ---------------------------------------------------------
 // The same computation for bfloat16 rows whose k is a whole number of chunk
 // passes, with the Hadamard block (64 or 128), the code width and the GeGLU
-// pre-op fixed at compile time.  Per element it spends about 18 VALU
+// pre-op fixed at compile time.  Per element it spends about 16 VALU
 // instructions: the GeLU table index of two values at once with 16-bit
-// packed arithmetic, 3 in-lane and 3-4 cross-lane butterflies (the lane
-// distance 4 as a quad reversal plus a half-row mirror, two DPP operations),
-// max3 reductions, and no clamp (|v / scale| <= qmax by construction, so the
-// rounded code never leaves the grid).
+// packed arithmetic, 3 in-lane and 3-4 cross-lane butterflies (DPP, and the
+// lane distance 4 through ds_swizzle), max3 reductions, and no clamp
+// (|v / scale| <= qmax by construction, so the rounded code never leaves the
+// grid).
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-// Lane distance 4 via quad_perm [3,2,1,0] into a temporary and a fused
-// multiply-add reading the temporary through row_half_mirror (lane l then
-// sees the value of lane l ^ 4).
-__device__ __forceinline__ void xlane4_fast(float (&w)[8], float sgn) {
-    float t0, t1, t2, t3, t4, t5, t6, t7;
-    asm("s_nop 1\n\t"
-        "v_mov_b32_dpp %0, %8 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %1, %9 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %2, %10 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %3, %11 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %4, %12 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %5, %13 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %6, %14 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %7, %15 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf"
-        : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
-        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]));
-    asm("s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %8, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %11, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %12, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %13, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %14, %16 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %15, %16 row_half_mirror row_mask:0xf bank_mask:0xf"
-        : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
-        : "v"(t0), "v"(t1), "v"(t2), "v"(t3), "v"(t4), "v"(t5), "v"(t6), "v"(t7), "v"(sgn));
+// Lane distance 4 through the LDS crossbar (ds_swizzle, xor 4): one VALU
+// instruction per value where the DPP form takes two, and this kernel is
+// VALU-bound at the backbone's widths (the LDS unit is otherwise idle).
+__device__ __forceinline__ void xlane4_swz(float (&w)[8], float sgn) {
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = lane_xor<4>(w[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = fmaf(t[e], sgn, w[e]);
 }
 
 // gelu of 8 bfloat16 gate values (four dwords) from the LDS table; values
@@ -672,7 +644,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p
             for (int c = 0; c < NCH; ++c) {
                 xlane8<1>(v[c], s1);
                 xlane8<2>(v[c], s2);
-                xlane4_fast(v[c], s4);
+                xlane4_swz(v[c], s4);
                 if constexpr (HB == 128) xlane8<8>(v[c], (lane & 8) ? -1.f : 1.f);
             }
         }
@@ -681,7 +653,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) amax = fmaxf(amax, fmaxf(fabsf(v[c][e]), fabsf(v[c][e + 1])));
+            for (int e = 0; e < 8; e += 2) amax = max3_abs(amax, v[c][e], v[c][e + 1]);
         amax = wave_max(amax, g < 64 ? g : 64);
         if (g > 64) {
             if (lane == 0) red[parity][wave] = amax;
@@ -706,8 +678,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p
                 for (int e = 0; e < 8; ++e) qb[e] = fmaf(v[c][e], mul, M);
 #pragma unroll
                 for (int e = 0; e < 8; e += 2)
-                    worst = fmaxf(worst, fmaxf(fabsf(fmaf(v[c][e], mul, M - qb[e])),
-                                               fabsf(fmaf(v[c][e + 1], mul, M - qb[e + 1]))));
+                    worst = max3_abs(worst, fmaf(v[c][e], mul, M - qb[e]), fmaf(v[c][e + 1], mul, M - qb[e + 1]));
                 if (worst >= 0.5f - kTieWindow) {
                     const double div = sigma * static_cast<double>(scale) * (HB == 64 ? 8.0 : 11.313708498984761);
 #pragma unroll

@@ -99,6 +99,17 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
     return a * b;
 }
 
+// max(m, |a|, |b|) in one instruction.  Written as fmaxf, values that come
+// out of inline assembly (the DPP butterflies) are first quieted one by one
+// (v_max x, |x|, |x|) because the compiler cannot prove them canonical: an
+// extra instruction per value.  For finite and quiet-NaN inputs the result is
+// the fmaxf one (a quiet NaN operand is ignored).
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+    float r;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+}
+
 // ---- wave64 cross-lane helpers -------------------------------------------
 
 // Value held by lane (lane ^ mask).  For mask < 32 this is ds_swizzle in
