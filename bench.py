@@ -183,6 +183,23 @@ def gemv_leg(dev, reps=5):
     all_launches = [t for L in layers for t in L]
     layer_us = replay_us(all_launches, reps) / len(layers)
     layer_gbs = (layer_bytes + sum(2 * p.k + 2 * p.n for p, _, _ in layer)) / (layer_us * 1e-6) / 1e9
+    # the same layer with the projections that read one input merged along n
+    # (q|k|v and gate|up stacked, as inference engines store them): 4 launches
+    merged_layers = []
+    for L in layers:
+        by = {p.name: (p, wq, ws) for p, wq, ws in L}
+        merged = []
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            ps = [by[nm] for nm in names]
+            p0 = ps[0][0]
+            pm = type(p0)("|".join(names), sum(t[0].n for t in ps), p0.k, p0.scheme)
+            merged.append((pm, torch.cat([t[1] for t in ps]), torch.cat([t[2] for t in ps])))
+        merged_layers.append(merged)
+    for n in {p.n for p, _, _ in merged_layers[0]}:
+        ys.setdefault(n, torch.empty((1, n), dtype=torch.float16, device=dev))
+    merged_us = replay_us([t for L in merged_layers for t in L], reps) / len(merged_layers)
+    merged_gbs = (layer_bytes + sum(2 * p.k + 2 * p.n for p, _, _ in merged_layers[0])) / (merged_us * 1e-6) / 1e9
+    del merged_layers
     shapes = {}
     for (n, k) in sorted({(p.n, p.k) for p, _, _ in layer}):
         launches = [(p, wq, ws) for L in layers for (p, wq, ws) in L if (p.n, p.k) == (n, k)]
@@ -192,6 +209,8 @@ def gemv_leg(dev, reps=5):
     return {"workload": "decoder7b_layer_m1_w4a16_g128", "layer_MB": round(layer_bytes / 1e6, 2),
             "weight_copies": copies, "layer_us": round(layer_us, 2), "GB/s": round(layer_gbs, 1),
             "frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph replay, cold weights",
+            "merged_qkv_gate_up": {"launches": 4, "layer_us": round(merged_us, 2), "GB/s": round(merged_gbs, 1),
+                                   "frac_hbm": round(merged_gbs / HBM_PEAK_GBS, 4)},
             "shapes": shapes}
 
 

@@ -616,6 +616,25 @@ def test_gemv_w4a16_repeatable(m, n, k):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,k,ns", [(1, 4096, (4096, 4096, 4096)), (1, 4096, (11008, 11008)), (20, 1024, (520, 96))])
+def test_gemv_w4a16_merged_rows_equal_separate(m, k, ns):
+    """Weights of projections that read one input stacked along n (q|k|v,
+    gate|up): the merged call's outputs are the separate calls' outputs, bit
+    for bit (every output row is computed from its own weight row alone)."""
+    say(f"gemv merged m={m} k={k} n={ns}")
+    x = synth.normal_tensor(SEED, f"gmx/{m}/{k}", (m, k), dtype="f16").to(DEV)
+    parts = []
+    for i, n in enumerate(ns):
+        w = synth.normal_tensor(SEED, f"gmw/{i}/{n}/{k}", (n, k), std=0.015, dtype="f16")
+        parts.append(q.qlin_quantize_weights(w.to(DEV), bits=4, group=128))
+    wq = torch.cat([t[0] for t in parts])
+    ws = torch.cat([t[1] for t in parts])
+    y = q.qlin_gemv_w4a16(x, wq, ws)
+    ys = [q.qlin_gemv_w4a16(x, a, b) for a, b in parts]
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), torch.cat(ys, dim=1).view(torch.int16))
+
+
 # ---------------------------------------------------------------- fold calibration
 
 
