@@ -83,9 +83,11 @@ class MlpBlock:
 
 class SweepLayer:
     """One layer of the mixed-precision backbone sweep (hidden 2048, MLP 16384)
-    at M tokens: q, k, v W4A4 from one int4 quantization of the attention input,
-    o W8A8 from the attention output, the fused gate|up GeGLU GEMM (W4A4) from
-    the MLP input, then h -> int8 -> down W8A8; Hadamard block 128, bf16 out.
+    at M tokens: q, k, v W4A4 from one int4 quantization of the attention input
+    (their weights stacked along n, one 6144-column GEMM; q, k and v are column
+    slices of its output), o W8A8 from the attention output, the fused gate|up
+    GeGLU GEMM (W4A4) from the MLP input, then h -> int8 -> down W8A8; Hadamard
+    block 128, bf16 out.
     Inputs are synthetic (one tensor each for the attention input, the
     attention output and the MLP input); weights are quantized once."""
 
@@ -121,9 +123,13 @@ class SweepLayer:
         s_qkv, self.inv_qkv, self.wq_q, self.ws_q = quant_w("q", self.x_attn, 4)
         wk = synth.weight(wl, p["k"], tag="/L0").to(dev)
         wv = synth.weight(wl, p["v"], tag="/L0").to(dev)
-        self.wq_k, self.ws_k = q.qlin_quantize_weights(wk, fold_s=s_qkv, had_block=128, bits=4)
-        self.wq_v, self.ws_v = q.qlin_quantize_weights(wv, fold_s=s_qkv, had_block=128, bits=4)
+        wq_k, ws_k = q.qlin_quantize_weights(wk, fold_s=s_qkv, had_block=128, bits=4)
+        wq_v, ws_v = q.qlin_quantize_weights(wv, fold_s=s_qkv, had_block=128, bits=4)
         del wk, wv
+        # per-row quantization: the stacked codes are the separate ones
+        self.wq_qkv = torch.cat([self.wq_q, wq_k, wq_v])
+        self.ws_qkv = torch.cat([self.ws_q, ws_k, ws_v])
+        del self.wq_q, self.ws_q, wq_k, wq_v
         _, self.inv_o, self.wq_o, self.ws_o = quant_w("o", self.x_o, 8)
         _, self.inv_gu, self.wq_gu, self.ws_gu = quant_w("gate_up", self.x_mlp, 4, interleave=True)
         self.xq4 = torch.empty((m, 1024), dtype=torch.uint8, device=dev)
@@ -133,7 +139,8 @@ class SweepLayer:
         self.h = torch.empty((m, f), dtype=bf, device=dev)
         self.hq = torch.empty((m, f), dtype=torch.int8, device=dev)
         self.hs = torch.empty(m, dtype=torch.float32, device=dev)
-        self.y = {n: torch.empty((m, p[n].n), dtype=bf, device=dev) for n in ("q", "k", "v", "o", "down")}
+        self.y = {n: torch.empty((m, p[n].n), dtype=bf, device=dev) for n in ("o", "down")}
+        self.y["qkv"] = torch.empty((m, p["q"].n + p["k"].n + p["v"].n), dtype=bf, device=dev)
         q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))
         q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, self.wq_gu, self.ws_gu, 2048, out=self.h)
         wdn = synth.weight(wl, p["down"], tag="/L0").to(dev)
@@ -146,8 +153,7 @@ class SweepLayer:
         q = self.q
         q.qlin_rotate_quant_act(self.x_attn, fold_inv_s=self.inv_qkv, had_block=128, bits=4,
                                 out=(self.xq4, self.xs4))
-        for n, wq, ws in (("q", self.wq_q, self.ws_q), ("k", self.wq_k, self.ws_k), ("v", self.wq_v, self.ws_v)):
-            q.qlin_gemm_w4a4(self.xq4, self.xs4, wq, ws, 2048, out=self.y[n])
+        q.qlin_gemm_w4a4(self.xq4, self.xs4, self.wq_qkv, self.ws_qkv, 2048, out=self.y["qkv"])
         q.qlin_rotate_quant_act(self.x_o, fold_inv_s=self.inv_o, had_block=128, bits=8, out=(self.xq8, self.xs8))
         q.qlin_gemm_w8a8(self.xq8, self.xs8, self.wq_o, self.ws_o, 2048, out=self.y["o"])
         q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))

@@ -522,6 +522,24 @@ def test_gemm_extreme_codes_at_max_k(scheme, m):
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
 
 
+@pytest.mark.parametrize("m", [40, 700])
+def test_gemm_w4a4_stacked_weights_equal_separate(m):
+    """q, k, v weights stacked along n (one GEMM over their shared activation
+    codes): outputs equal the three separate GEMMs' outputs bit for bit, on the
+    small-M and the large-tile kernels."""
+    say(f"gemm stacked qkv m={m}")
+    k, ns = 2048, (2048, 512, 1024)
+    x = synth.normal_tensor(SEED, f"stk/x/{m}", (m, k), dtype="bf16", outliers=20, outlier_scale=20.0).to(DEV)
+    xq, xs = q.qlin_rotate_quant_act(x, had_block=128, bits=4)
+    parts = [q.qlin_quantize_weights(synth.normal_tensor(SEED, f"stk/w/{i}", (n, k), std=0.02, dtype="bf16").to(DEV),
+                                     had_block=128, bits=4) for i, n in enumerate(ns)]
+    y = q.qlin_gemm_w4a4(xq, xs, torch.cat([t[0] for t in parts]), torch.cat([t[1] for t in parts]), k,
+                         y_dtype=torch.bfloat16)
+    ys = [q.qlin_gemm_w4a4(xq, xs, a, b, k, y_dtype=torch.bfloat16) for a, b in parts]
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), torch.cat(ys, dim=1).view(torch.int16))
+
+
 @pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
 def test_gemm_small_m_matches_large_tile_epilogue(scheme):
     """Rows 0..63 computed alone (16-column kernel) equal the same rows of a
