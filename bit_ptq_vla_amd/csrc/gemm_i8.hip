@@ -845,6 +845,16 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
     if (tiles * 2 <= slots) {
         while (tiles * splits * 2 <= slots && stages / (splits * 2) >= 16) splits *= 2;
     }
+    // int8 x int8 with few tiles: the largest split that still gives every
+    // block a CU of its own (the deep ring below), when it fills at least 3/4
+    // of the CUs.  At 816 x 2048 x 16384 that is two splits on 224 CUs: the
+    // GEMM takes the time of four splits at two blocks per CU (38.1 us) and
+    // the reduction reads half the partials (4.8 us instead of 7.2 us).
+    if (!int4 && !a8) {
+        int deep_splits = 1;
+        while (tiles * deep_splits * 2 <= cus && stages / (deep_splits * 2) >= 16) deep_splits *= 2;
+        if (deep_splits >= 2 && tiles * deep_splits * 4 >= cus * 3 && tiles * splits > cus) splits = deep_splits;
+    }
     g.splits = splits;
     // A grid of at most one block per CU gets the whole LDS for a deeper ring:
     // with one wave per SIMD nothing else covers the DMA latency.
