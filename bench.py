@@ -301,16 +301,19 @@ def action_expert_leg(dev, reps=5):
     """The action expert's projections at M = 50 over 10 denoising steps, W4A4
     (b = 64, with activation quantization), W4A4 with per-step static
     activation tables (one table and one weight copy per step), and W4A16
-    g128 on the same weights; weights stay resident in L2 / Infinity Cache
-    across steps (warm).  The 10 steps are replayed from a captured HIP graph:
+    g128 on the same weights; then both schemes with q, k, v reading one
+    input as one stacked 3072-column projection (shared fold); weights stay
+    resident in L2 / Infinity Cache across steps (warm).  The 10 steps are replayed from a captured HIP graph:
     at these sizes eager Python launches (about 10 us each) would hide the
     kernels."""
     from bit_ptq_vla_amd.workload import ActionExpert
 
     ae = ActionExpert(dev)
     ae.build_static()
+    ae.build_merged()
     res = {"m": 50, "steps": ae.steps}
-    for name, fn in (("w4a4", ae.run_w4a4), ("w4a4_static", ae.run_w4a4_static), ("w4a16", ae.run_w4a16)):
+    for name, fn in (("w4a4", ae.run_w4a4), ("w4a4_static", ae.run_w4a4_static), ("w4a16", ae.run_w4a16),
+                     ("w4a4_merged_qkv", ae.run_w4a4_merged), ("w4a16_merged_qkv", ae.run_w4a16_merged)):
         us = _graph_us(fn, reps)
         mode = "graph replay"
         if us is None:
@@ -322,7 +325,7 @@ def action_expert_leg(dev, reps=5):
             tops = ae.ops_per_step / (us * 1e-6) / 1e12
             res[f"{name}_TOPS"] = round(tops, 2)
             res[f"{name}_frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
-        else:
+        elif name == "w4a16":
             gbs = ae.w4a16_bytes / (us * 1e-6) / 1e9
             res["w4a16_GB/s"] = round(gbs, 1)
             res["w4a16_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)

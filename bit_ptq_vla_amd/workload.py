@@ -221,6 +221,54 @@ class ActionExpert:
                 per_step.append((table, wq_t, ws_t))
             self.static.append((pr, xs, inv, per_step, xq, y))
 
+    def build_merged(self):
+        """q, k and v reading one input (the q projection's per-step tokens,
+        as in a transformer block) with their weights stacked along n: one
+        fold calibrated on the stacked weights, one activation quantization
+        and one 3072-column projection per step instead of three of each."""
+        import torch
+
+        q = self.q
+        from bit_ptq_vla_amd import synth
+
+        wl = synth.CFG3
+        names = [pr.name for pr in self.projs]
+        iq = [names.index(nm) for nm in ("q", "k", "v")]
+        self.rest = [i for i in range(len(self.projs)) if i not in iq]
+        dev = self.w4a4[0][3].device
+        w = torch.cat([synth.weight(wl, self.projs[i]).to(dev) for i in iq])
+        xs = self.w4a4[iq[0]][1]
+        s, inv = q.qlin_calibrate_fold(xs[0], w)
+        wq, ws = q.qlin_quantize_weights(w, fold_s=s, had_block=64, bits=4)
+        # group-128 rows quantize independently: the stacked codes are the separate ones
+        wq16 = torch.cat([self.w4a16[i][2] for i in iq])
+        ws16 = torch.cat([self.w4a16[i][3] for i in iq])
+        k = self.projs[iq[0]].k
+        self.merged = (xs, inv, wq, ws, wq16, ws16, k,
+                       torch.empty((50, k // 2), dtype=torch.uint8, device=dev),
+                       torch.empty(50, dtype=torch.float32, device=dev),
+                       torch.empty((50, w.shape[0]), dtype=torch.float16, device=dev))
+
+    def run_w4a4_merged(self):
+        q = self.q
+        xs, inv, wq, ws, _, _, k, xq, xsc, y = self.merged
+        for t in range(self.steps):
+            q.qlin_rotate_quant_act(xs[t], fold_inv_s=inv, had_block=64, bits=4, out=(xq, xsc))
+            q.qlin_gemm_w4a4(xq, xsc, wq, ws, k, out=y)
+            for i in self.rest:
+                pr, xs_i, inv_i, wq_i, ws_i, xq_i, xsc_i, y_i = self.w4a4[i]
+                q.qlin_rotate_quant_act(xs_i[t], fold_inv_s=inv_i, had_block=64, bits=4, out=(xq_i, xsc_i))
+                q.qlin_gemm_w4a4(xq_i, xsc_i, wq_i, ws_i, pr.k, out=y_i)
+
+    def run_w4a16_merged(self):
+        q = self.q
+        xs, _, _, _, wq16, ws16, _, _, _, y = self.merged
+        for t in range(self.steps):
+            q.qlin_gemv_w4a16(xs[t], wq16, ws16, out=y)
+            for i in self.rest:
+                pr, xs_i, wq_i, ws_i, y_i = self.w4a16[i]
+                q.qlin_gemv_w4a16(xs_i[t], wq_i, ws_i, out=y_i)
+
     def run_w4a4_static(self):
         q = self.q
         for t in range(self.steps):

@@ -860,6 +860,21 @@ def test_action_expert_denoising_steps():
             assert_ok(oracle.compare_outputs(f64(y16), y16_ref), "W4A16 output")
 
 
+def test_action_expert_merged_qkv():
+    """q, k, v of the action expert reading one input with their weights
+    stacked along n (3072 x 1024, one fold calibrated on the stacked weights):
+    the whole W4A4 linear against the oracle at steps 0 and 9."""
+    wl = synth.CFG3
+    pr = {p.name: p for p in wl.projs}
+    w = torch.cat([synth.weight(wl, pr[n]) for n in ("q", "k", "v")])
+    x0 = synth.activation(wl, pr["q"], 50, tag="/t0", std=synth.cfg3_sigma(0))
+    s = oracle.calibrate_fold(synth.to_f64(x0), synth.to_f64(w)).astype(np.float32)
+    for t in (0, 9):
+        say(f"action expert merged qkv step {t}")
+        x = synth.activation(wl, pr["q"], 50, tag=f"/t{t}", std=synth.cfg3_sigma(t))
+        _check_linear(x, w, torch.from_numpy(s), 64, 4, "f16")
+
+
 def test_action_expert_per_step_static_tables():
     """Action expert at steps 0, 4 and 9 with per-step static tables: each
     step's table calibrated (on the GPU) from that step's calibration tokens,
