@@ -58,77 +58,109 @@ struct CompParams {
     float* v;            // out: rotated rows [m][k] fp32
 };
 
-// Block (j, row tile): the b x b rotation of block j (staged in LDS once)
-// applied to RT = 8 * 256 / b rows.  Thread t owns column c = t % b of rows
-// t / b + u * (256 / b), u < 8: one R[i][c] serves its 8 independent sums.
-template <int DT>
+// Block (j, column slice, row tile): CW = min(B, 64) output columns of block
+// j's rotation, R[:, c0 .. c0 + CW) staged in LDS (fp32), applied to a tile of
+// RT rows whose gathered, folded values are staged in LDS as the fp32
+// products they are (row pitch B + 4 floats: rows of one wave fall in
+// different banks).  A thread owns 4 adjacent columns of RPT rows; per four
+// input channels it reads one float4 of R per channel (shared by the wave's
+// row groups) and one float4 of x per row, and runs each output's fp64 FMA
+// chain in channel order, so every output is the same fp64 sum as a plain
+// loop over the channels.  At B = 128 two blocks fit a CU (65 KB of LDS).
+template <int DT, int B, int RPT>
 __global__ __launch_bounds__(256) void composite_rotate_kernel(CompParams p) {
+    constexpr int CW = B < 64 ? B : 64;
+    constexpr int CG = CW / 4;            // column groups of 4
+    constexpr int RG = 256 / CG;          // row groups
+    constexpr int RT = RG * RPT;          // rows per block
+    constexpr int XP = B + 4;             // x tile pitch, floats
     extern __shared__ float lds[];
-    constexpr int NU = 8;
-    const int b = p.b, k = static_cast<int>(p.k);
-    const int rt = NU * 256 / b;
-    float* rs = lds;                                          // [b][b]
-    double* xs = reinterpret_cast<double*>(lds + b * b);      // [rt][b], fp64 (b * b is even)
+    float* rs = lds;                      // [B][CW]
+    float* xs = lds + B * CW;             // [RT][XP]
     const int tid = threadIdx.x;
-    const int j = blockIdx.x;
-    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * rt;
-    // rotation of block j: b * b / 4 float4, at most 16 per thread, four
-    // loads in flight before their stores
-    const float4* rj = reinterpret_cast<const float4*>(p.rot + static_cast<int64_t>(j) * b * b);
-    const int nq = b * b / 4;
-    for (int q0 = tid; q0 < nq; q0 += 4 * 256) {
-        float4 t4[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) t4[t] = rj[q0 + 256 * t < nq ? q0 + 256 * t : nq - 1];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (q0 + 256 * t < nq) reinterpret_cast<float4*>(rs)[q0 + 256 * t] = t4[t];
-    }
-    // gathered, folded x: rt * b = 2048 elements, eight per thread
+    const int j = blockIdx.x / (B / CW);
+    const int c0 = (blockIdx.x % (B / CW)) * CW;
+    const int k = static_cast<int>(p.k);
+    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * RT;
     {
-        int src[NU];
-        int64_t rowv[NU];
+        // R[:, c0 .. c0 + CW) of block j: B * CW / 4 float4
+        constexpr int NQ = B * CW / 4;
+        constexpr int PER = (NQ + 255) / 256;
+        const float* rj = p.rot + static_cast<int64_t>(j) * B * B + c0;
+        float4 t4[PER];
 #pragma unroll
-        for (int t = 0; t < NU; ++t) {
-            const int e = tid + 256 * t;
-            const int r = e / b, i = e - r * b;
-            rowv[t] = row0 + r;
-            int sidx = p.perm[j * b + i];
-            src[t] = sidx < 0 ? 0 : (sidx >= k ? k - 1 : sidx);   // (a valid permutation never clamps)
-        }
-        float v[NU], f[NU];
-#pragma unroll
-        for (int t = 0; t < NU; ++t) {
-            const bool ok = rowv[t] < p.m;
-            const int64_t rr = ok ? rowv[t] : 0;
-            v[t] = load1<DT>(static_cast<const char*>(p.x) + rr * p.ldx * (DT == F32 ? 4 : 2), src[t]);
-            f[t] = p.mult ? p.mult[src[t]] : 1.f;
-            if (!ok) v[t] = 0.f;
+        for (int t = 0; t < PER; ++t) {
+            const int q = tid + 256 * t < NQ ? tid + 256 * t : NQ - 1;
+            const int i = q / (CW / 4), cq = q - i * (CW / 4);
+            t4[t] = *reinterpret_cast<const float4*>(rj + i * B + 4 * cq);
         }
 #pragma unroll
-        for (int t = 0; t < NU; ++t) xs[tid + 256 * t] = static_cast<double>(v[t] * f[t]);
+        for (int t = 0; t < PER; ++t) {
+            const int q = tid + 256 * t;
+            if (q < NQ) {
+                const int i = q / (CW / 4), cq = q - i * (CW / 4);
+                *reinterpret_cast<float4*>(rs + i * CW + 4 * cq) = t4[t];
+            }
+        }
+    }
+    {
+        // gathered, folded x: a thread keeps one channel i = tid % B (256 is a
+        // multiple of B) for rows tid / B + (256 / B) t: its source channel and
+        // fold multiplier are loaded once, its RT * B / 256 row loads all
+        // issued before the first is used
+        constexpr int NR = RT * B / 256;      // rows per thread
+        constexpr int RS = 256 / B;           // row stride
+        const int i = tid % B, r0 = tid / B;
+        int sidx = p.perm[j * B + i];
+        sidx = sidx < 0 ? 0 : (sidx >= k ? k - 1 : sidx);   // (a valid permutation never clamps)
+        const float f = p.mult ? p.mult[sidx] : 1.f;
+        const char* xb = static_cast<const char*>(p.x);
+        const int64_t pitch = p.ldx * (DT == F32 ? 4 : 2);
+        float xv[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            const int64_t row = row0 + r0 + RS * t;
+            xv[t] = load1<DT>(xb + (row < p.m ? row : 0) * pitch, sidx);
+        }
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            const int64_t row = row0 + r0 + RS * t;
+            xs[(r0 + RS * t) * XP + i] = row < p.m ? xv[t] * f : 0.f;
+        }
     }
     __syncthreads();
-    const int c = tid % b, rb = tid / b, rstep = 256 / b;
-    double acc[NU];
+    const int cg = tid % CG, rg = tid / CG;
+    double acc[RPT][4];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) acc[u] = 0.0;
-    for (int i = 0; i < b; i += 2) {
-        const double r0 = static_cast<double>(rs[i * b + c]);
-        const double r1 = static_cast<double>(rs[(i + 1) * b + c]);
+    for (int u = 0; u < RPT; ++u)
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            // (two consecutive x values of a row in one 16-byte LDS read; the
-            // wave reads the same address, a broadcast)
-            const double2 xv = *reinterpret_cast<const double2*>(xs + (rb + u * rstep) * b + i);
-            acc[u] = __builtin_fma(xv.x, r0, acc[u]);
-            acc[u] = __builtin_fma(xv.y, r1, acc[u]);
+        for (int c = 0; c < 4; ++c) acc[u][c] = 0.0;
+#pragma unroll 2
+    for (int i = 0; i < B; i += 4) {
+        float4 r4[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) r4[ii] = *reinterpret_cast<const float4*>(rs + (i + ii) * CW + 4 * cg);
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const float4 x4 = *reinterpret_cast<const float4*>(xs + (rg + u * RG) * XP + i);
+            const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const double xd = static_cast<double>(xv[ii]);
+                acc[u][0] = __builtin_fma(xd, static_cast<double>(r4[ii].x), acc[u][0]);
+                acc[u][1] = __builtin_fma(xd, static_cast<double>(r4[ii].y), acc[u][1]);
+                acc[u][2] = __builtin_fma(xd, static_cast<double>(r4[ii].z), acc[u][2]);
+                acc[u][3] = __builtin_fma(xd, static_cast<double>(r4[ii].w), acc[u][3]);
+            }
         }
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int64_t row = row0 + rb + u * rstep;
-        if (row < p.m) p.v[row * p.k + static_cast<int64_t>(j) * b + c] = static_cast<float>(acc[u]);
+    for (int u = 0; u < RPT; ++u) {
+        const int64_t row = row0 + rg + u * RG;
+        if (row < p.m)
+            *reinterpret_cast<float4*>(p.v + row * p.k + static_cast<int64_t>(j) * B + c0 + 4 * cg) =
+                make_float4(static_cast<float>(acc[u][0]), static_cast<float>(acc[u][1]),
+                            static_cast<float>(acc[u][2]), static_cast<float>(acc[u][3]));
     }
 }
 
@@ -347,16 +379,39 @@ __global__ __launch_bounds__(256) void jacobi_rot_kernel(const double* gram, int
     }
 }
 
-template <int DT>
-hipError_t launch_rot_dt(const CompParams& p, hipStream_t st) {
-    const int rt = 8 * 256 / p.b;
-    const size_t lds = static_cast<size_t>(p.b) * p.b * 4 + static_cast<size_t>(rt) * p.b * 8;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(composite_rotate_kernel<DT>),
+template <int DT, int B, int RPT>
+hipError_t launch_rot_b(const CompParams& p, hipStream_t st) {
+    constexpr int CW = B < 64 ? B : 64;
+    constexpr int RT = (256 / (CW / 4)) * RPT;
+    const size_t lds = static_cast<size_t>(B) * CW * 4 + static_cast<size_t>(RT) * (B + 4) * 4;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(composite_rotate_kernel<DT, B, RPT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    dim3 grid(static_cast<unsigned>(p.k / p.b), static_cast<unsigned>((p.m + rt - 1) / rt));
-    hipLaunchKernelGGL(composite_rotate_kernel<DT>, grid, dim3(256), lds, st, p);
+    dim3 grid(static_cast<unsigned>(p.k / B * (B / CW)), static_cast<unsigned>((p.m + RT - 1) / RT));
+    hipLaunchKernelGGL((composite_rotate_kernel<DT, B, RPT>), grid, dim3(256), lds, st, p);
     return hipGetLastError();
+}
+
+// Four rows per thread when that still makes a grid of at least 256 blocks,
+// else one (the action expert's few dozen rows).
+template <int DT, int B>
+hipError_t launch_rot_rpt(const CompParams& p, hipStream_t st) {
+    constexpr int CW = B < 64 ? B : 64;
+    constexpr int RT4 = (256 / (CW / 4)) * 4;
+    const int64_t blocks4 = p.k / B * (B / CW) * ((p.m + RT4 - 1) / RT4);
+    if (blocks4 >= 256) return launch_rot_b<DT, B, 4>(p, st);
+    return launch_rot_b<DT, B, 1>(p, st);
+}
+
+template <int DT>
+hipError_t launch_rot_dt(const CompParams& p, hipStream_t st) {
+    switch (p.b) {
+        case 16: return launch_rot_rpt<DT, 16>(p, st);
+        case 32: return launch_rot_rpt<DT, 32>(p, st);
+        case 64: return launch_rot_rpt<DT, 64>(p, st);
+        case 128: return launch_rot_rpt<DT, 128>(p, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
