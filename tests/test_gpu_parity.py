@@ -202,6 +202,11 @@ COMPOSITE_CASES = [
     (5, 16384, 128, 8, "bf16", True),    # down input width: one row per block
     (300, 512, 32, 8, "f32", False),     # several row groups per block
     (9, 256, 16, 4, "f16", False),
+    # four rows per thread (grids of >= 256 blocks), ragged last row tile
+    (816, 2048, 128, 4, "bf16", True),   # the backbone MLP input
+    (700, 2048, 64, 4, "f16", True),
+    (600, 4096, 32, 8, "bf16", False),
+    (1100, 1024, 16, 4, "f32", True),
 ]
 
 
