@@ -140,6 +140,16 @@ __device__ __forceinline__ void dma16(v4i rsrc, int voff, uint32_t lds_addr) {
 }
 
 // ---- GeLU for the fused GeGLU epilogue -------------------------------------
+
+// max(g, 0) for the bfloat16 g in the low half of w, in one instruction.
+// fmaxf on the bit-cast value first quiets it (v_max x, x, x), since the
+// compiler cannot tell that a value produced by v_cvt_pk_bf16_f32 is never a
+// signalling NaN; for every other input the result is fmaxf's.
+__device__ __forceinline__ float relu_bf16_word(uint32_t w) {
+    float r;
+    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(__uint_as_float(w << 16)));
+    return r;
+}
 // T(x) = x * Phi(-x) = -gelu(-x) for the bfloat16 values 2^-12 <= x < 16
 // (16 exponents x 128 mantissas, 8 KB), evaluated in float64 through erfc
 // and rounded to fp32.  Then gelu(g) = -T(|g|) for g < 0 and g - T(g) for
@@ -246,7 +256,7 @@ __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN /
                 for (int r = 0; r < 16; ++r) {
                     const float t = *reinterpret_cast<const float*>(reinterpret_cast<const int8_t*>(tab) +
                                                                     (toff[r] & 0x1FFCu));
-                    gl[r] = fmaxf(__uint_as_float(pk[r] << 16), 0.f) - t;   // relu(g) - T(|g|)
+                    gl[r] = relu_bf16_word(pk[r]) - t;   // relu(g) - T(|g|)
                 }
                 if (any & 0x1E000u) {
 #pragma unroll
