@@ -145,16 +145,6 @@ __device__ __forceinline__ float wave_max(float v, int width) {
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    v += lane_xor<1>(v);
-    v += lane_xor<2>(v);
-    v += lane_xor<4>(v);
-    v += lane_xor<8>(v);
-    v += lane_xor<16>(v);
-    v += lane_xor<32>(v);
-    return v;
-}
-
 // Exact GeLU, t * (1 + erf(t / sqrt 2)) / 2, in fp32 (device-library erff).
 __device__ __forceinline__ float gelu_erf(float t) {
     return 0.5f * t * (1.0f + erff(t * 0.70710678118654752440f));
