@@ -389,6 +389,7 @@ GEMM_SHAPES = [
     (80, 100, 4096),     # split-K, n % 8 == 4: four outputs per reduce lane
     (70, 99, 2048),      # split-K, odd n: one output per reduce lane
     (65, 256, 16384),    # split-K
+    (1000, 1800, 4096),  # int8 x int8: two K splits, one block per CU (240 CUs); ragged M and N
 ]
 
 
