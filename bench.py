@@ -411,8 +411,8 @@ def cpu_baseline(block, rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(the projection path runs on a single GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
 
