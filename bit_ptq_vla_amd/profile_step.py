@@ -2,7 +2,7 @@
 
 Two parts:
 
-  run        a short driver to launch under ``rocprofv3 --pmc``: a plain
+  run        a short program to launch under ``rocprofv3 --pmc``: a plain
              device copy of known size (the calibration reference), then a few
              steps of the M = 816 backbone MLP block.
   summarize  reads the FETCH_SIZE and WRITE_SIZE collections of two such runs

@@ -1,5 +1,5 @@
 """Device-resident workloads of the projection path, shared by bench.py and
-the profiling driver.  Nothing here computes the method itself: every step
+the profiling program.  Nothing here computes the method itself: every step
 runs through the library's entry points.
 """
 
