@@ -28,9 +28,13 @@ QLIN_ERR_UNSUPPORTED = 5
 QLIN_ERR_DEVICE = 6
 QLIN_ERR_LAUNCH = 7
 QLIN_ERR_ALIAS = 8
+QLIN_ERR_CAPTURE = 9
+QLIN_ERR_WORKSPACE = 10
 
 QLIN_F16, QLIN_BF16, QLIN_F32, QLIN_I32 = 0, 1, 2, 3
 QLIN_PRE_NONE, QLIN_PRE_GEGLU = 0, 1
+QLIN_W4A4, QLIN_W8A8, QLIN_W4A8 = 0, 1, 2
+_SCHEME = {"qlin_gemm_w4a4": QLIN_W4A4, "qlin_gemm_w8a8": QLIN_W8A8, "qlin_gemm_w4a8": QLIN_W4A8}
 
 _TORCH_TO_QLIN = {torch.float16: QLIN_F16, torch.bfloat16: QLIN_BF16,
                   torch.float32: QLIN_F32, torch.int32: QLIN_I32}
@@ -48,14 +52,17 @@ SIGNATURES = {
     "qlin_gemm_w4a4": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w8a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w4a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemm_ws": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _I64, _P],
+    "qlin_gemm_workspace_bytes": [_I32, _I64, _I64, _I64],
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
     "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
     "qlin_rotate_quant_act_static": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P],
     "qlin_quantize_weights_step": [_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P],
-    "qlin_calibrate_composite": [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P],
+    "qlin_calibrate_composite_work_bytes": [_I64, _I64, _I32],
+    "qlin_calibrate_composite": [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _I64, _P],
     "qlin_rotate_quant_act_composite": [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _P, _P, _P],
-    "qlin_quantize_weights_composite": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _P, _P],
+    "qlin_quantize_weights_composite": [_P, _I32, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _P, _P, _P],
 }
 
 _lib = None
@@ -78,7 +85,8 @@ def load() -> ctypes.CDLL:
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "qlin_status_string" else ctypes.c_int32
+        fn.restype = (ctypes.c_char_p if name == "qlin_status_string"
+                      else ctypes.c_int64 if name.endswith("_bytes") else ctypes.c_int32)
     _lib = lib
     return lib
 
@@ -263,8 +271,13 @@ def qlin_calibrate_composite(w: torch.Tensor, had_block: int, fold_s: Optional[t
     _need(fold_s, k * 4, "fold_s")
     perm = torch.empty(k, dtype=torch.int32, device=w.device)
     rot = torch.empty((k // had_block, had_block, had_block), dtype=torch.float32, device=w.device)
+    nbytes = lib.qlin_calibrate_composite_work_bytes(n, k, had_block)
+    if nbytes < 0:
+        raise QlinError(QLIN_ERR_SHAPE, "qlin_calibrate_composite_work_bytes")
+    work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
     st = lib.qlin_calibrate_composite(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
-                                      perm.data_ptr(), rot.data_ptr(), _stream(w.device))
+                                      perm.data_ptr(), rot.data_ptr(), work.data_ptr(), work.numel(),
+                                      _stream(w.device))
     _check(st, "qlin_calibrate_composite")
     return perm, rot
 
@@ -302,9 +315,10 @@ def qlin_rotate_quant_act_composite(x: torch.Tensor, perm: torch.Tensor, rot: to
 
 
 def qlin_quantize_weights_composite(w: torch.Tensor, perm: torch.Tensor, rot: torch.Tensor,
-                                    fold_s: Optional[torch.Tensor] = None, bits: int = 4
-                                    ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Weight codes and per-row scales with the composite rotation."""
+                                    fold_s: Optional[torch.Tensor] = None, bits: int = 4,
+                                    work: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Weight codes and per-row scales with the composite rotation (work:
+    float32 scratch of n * k elements; allocated here when None)."""
     lib = load()
     _dev_tensor(w, "w")
     n, k = w.shape
@@ -316,14 +330,32 @@ def qlin_quantize_weights_composite(w: torch.Tensor, perm: torch.Tensor, rot: to
     wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
                      device=w.device)
     ws = torch.empty(n, dtype=torch.float32, device=w.device)
+    if work is None:
+        work = torch.empty(n * k, dtype=torch.float32, device=w.device)
+    _need(work, n * k * 4, "work")
     st = lib.qlin_quantize_weights_composite(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s),
                                              perm.data_ptr(), rot.data_ptr(), b, bits, wq.data_ptr(),
-                                             ws.data_ptr(), _stream(w.device))
+                                             ws.data_ptr(), work.data_ptr(), _stream(w.device))
     _check(st, "qlin_quantize_weights_composite")
     return wq, ws
 
 
-def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):
+def gemm_workspace_bytes(scheme: int, m: int, n: int, k: int) -> int:
+    """Bytes of split-K workspace a qlin_gemm_ws call of this shape takes (0: none)."""
+    nbytes = load().qlin_gemm_workspace_bytes(scheme, m, n, k)
+    if nbytes < 0:
+        raise QlinError(QLIN_ERR_SHAPE, "qlin_gemm_workspace_bytes")
+    return nbytes
+
+
+def gemm_workspace(scheme: int, m: int, n: int, k: int, device) -> Optional[torch.Tensor]:
+    """A device buffer for qlin_gemm_ws's split-K partials (None when the
+    shape takes no split)."""
+    nbytes = gemm_workspace_bytes(scheme, m, n, k)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out, workspace=None):
     lib = load()
     _dev_tensor(wq, "wq")
     m, n = xq.shape[0], wq.shape[0]
@@ -335,25 +367,36 @@ def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out):
     _need(w_scale, n * 4, "w_scale")
     y = out if out is not None else torch.empty((m, n), dtype=y_dtype, device=wq.device)
     _need(y, m * n * y.element_size(), "y")
-    st = getattr(lib, fn_name)(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
-                               y.data_ptr(), _TORCH_TO_QLIN[y.dtype], _stream(wq.device))
-    _check(st, fn_name)
+    if workspace is None:
+        st = getattr(lib, fn_name)(xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
+                                   y.data_ptr(), _TORCH_TO_QLIN[y.dtype], _stream(wq.device))
+        _check(st, fn_name)
+    else:
+        _need(workspace, 0, "workspace")
+        st = lib.qlin_gemm_ws(_SCHEME[fn_name], xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
+                              y.data_ptr(), _TORCH_TO_QLIN[y.dtype], workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream(wq.device))
+        _check(st, "qlin_gemm_ws")
     return y
 
 
-def qlin_gemm_w4a4(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
-    """y [m][n] from packed int4 codes xq [m][k/2], wq [n][k/2]."""
-    return _gemm("qlin_gemm_w4a4", xq, x_scale, wq, w_scale, k, y_dtype, out)
+def qlin_gemm_w4a4(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None,
+                   workspace=None) -> torch.Tensor:
+    """y [m][n] from packed int4 codes xq [m][k/2], wq [n][k/2] (workspace:
+    split-K scratch from gemm_workspace, through qlin_gemm_ws)."""
+    return _gemm("qlin_gemm_w4a4", xq, x_scale, wq, w_scale, k, y_dtype, out, workspace)
 
 
-def qlin_gemm_w8a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+def qlin_gemm_w8a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None,
+                   workspace=None) -> torch.Tensor:
     """y [m][n] from int8 codes xq [m][k], wq [n][k]."""
-    return _gemm("qlin_gemm_w8a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
+    return _gemm("qlin_gemm_w8a8", xq, x_scale, wq, w_scale, k, y_dtype, out, workspace)
 
 
-def qlin_gemm_w4a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+def qlin_gemm_w4a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None,
+                   workspace=None) -> torch.Tensor:
     """y [m][n] from int8 activation codes xq [m][k] and packed int4 weight codes wq [n][k/2]."""
-    return _gemm("qlin_gemm_w4a8", xq, x_scale, wq, w_scale, k, y_dtype, out)
+    return _gemm("qlin_gemm_w4a8", xq, x_scale, wq, w_scale, k, y_dtype, out, workspace)
 
 
 def qlin_gemm_w4a4_geglu(xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat16, out=None) -> torch.Tensor:

@@ -153,12 +153,13 @@ __global__ void gelu_table_init_kernel() {
 }
 
 // gelu of a bfloat16 value outside the table: tiny |g| by its Taylor start,
-// |g| >= 8 as g or 0.
+// |g| >= 256 as g (positive) or 0 (negative, -inf included); a NaN gate
+// stays NaN, as in the fused GeGLU epilogue.
 __device__ __forceinline__ float gelu_bf16_edge(uint32_t bits) {
     const float g = __uint_as_float(bits << 16);
     if (((bits & 0x7FFFu) >> 7) < static_cast<uint32_t>(GELU_EF0))
         return fmaf(g * g, 0.39894228040143267794f, 0.5f * g);
-    return g > 0.f ? g : 0.f;
+    return g > 0.f ? g : (g == g ? 0.f : g);
 }
 
 // Eight gelu values of gate bits w[0..3] (two bfloat16 per word).
@@ -943,22 +944,44 @@ int row_quant_lanes(int64_t k) {
 int row_quant_chunks(int64_t k, int g) { return static_cast<int>((k + 8LL * g - 1) / (8LL * g)); }
 
 namespace {
-std::mutex g_tab_mu;
-bool g_tab_ready[64] = {false};
+std::mutex g_once_mu;
+}  // namespace
 
-// Fills the bfloat16 GeLU table on the current device (once per device).
-hipError_t ensure_gelu_table(hipStream_t st) {
+hipError_t fill_once_per_device(OncePerDevice& once, hipStream_t caller, hipError_t (*fill)(hipStream_t)) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_tab_mu);
-    if (g_tab_ready[dev]) return hipSuccess;
-    hipLaunchKernelGGL(gelu_table_init_kernel, dim3((GELU_TAB + 255) / 256), dim3(256), 0, st);
-    e = hipGetLastError();
-    if (e == hipSuccess) g_tab_ready[dev] = true;
+    std::lock_guard<std::mutex> lock(g_once_mu);
+    if (once.ready[dev]) return hipSuccess;
+    if (caller != nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(caller, &cs);
+        if (e != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    }
+    hipStream_t own = nullptr;
+    e = hipStreamCreateWithFlags(&own, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    e = fill(own);
+    const hipError_t es = hipStreamSynchronize(own);
+    if (e == hipSuccess) e = es;
+    const hipError_t ed = hipStreamDestroy(own);
+    if (e == hipSuccess) e = ed;
+    if (e == hipSuccess) once.ready[dev] = true;
     return e;
 }
+
+namespace {
+OncePerDevice g_gelu_tab_once;
+
+hipError_t fill_gelu_table(hipStream_t st) {
+    hipLaunchKernelGGL(gelu_table_init_kernel, dim3((GELU_TAB + 255) / 256), dim3(256), 0, st);
+    return hipGetLastError();
+}
+
+// The bfloat16 GeLU table of this device, filled before first use.
+hipError_t ensure_gelu_table(hipStream_t st) { return fill_once_per_device(g_gelu_tab_once, st, fill_gelu_table); }
 }  // namespace
 
 hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,

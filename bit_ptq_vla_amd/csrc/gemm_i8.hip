@@ -34,7 +34,6 @@
 // Split-K writes int32 partial tiles; a second kernel sums them in a fixed
 // order (integer addition: bit-exact) and applies the epilogue.
 
-#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -815,27 +814,19 @@ hipError_t launch_geglu_out(const GemmParams& p, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-std::mutex g_gtab_mu;
-bool g_gtab_ready[64] = {false};
+OncePerDevice g_gtab_once;
 
-// Fills the fused epilogue's GeLU table on the current device (once per device,
-// on the caller's stream, ahead of the first GEMM that reads it).
-hipError_t ensure_gelu_neg_tab(hipStream_t st) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_gtab_mu);
-    if (g_gtab_ready[dev]) return hipSuccess;
+hipError_t fill_gelu_neg_tab(hipStream_t st) {
     hipLaunchKernelGGL(gelu_neg_tab_init_kernel, dim3((GTAB_N + 255) / 256), dim3(256), 0, st);
-    e = hipGetLastError();
-    if (e == hipSuccess) g_gtab_ready[dev] = true;
-    return e;
+    return hipGetLastError();
 }
+
+// The fused epilogue's GeLU table of this device, filled before first use.
+hipError_t ensure_gelu_neg_tab(hipStream_t st) { return fill_once_per_device(g_gtab_once, st, fill_gelu_neg_tab); }
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool allow_split) {
     // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes
     // per MFMA), two blocks per CU (one block's per-stage barrier and LDS
     // latency is covered by the other block's MFMAs).
@@ -852,7 +843,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
     int splits = 1;
     // split K only when the tile grid fills under half of the block slots,
     // keeping at least 16 stages (1 KiB of k per row) in every split
-    if (tiles * 2 <= slots) {
+    if (allow_split && tiles * 2 <= slots) {
         while (tiles * splits * 2 <= slots && stages / (splits * 2) >= 16) splits *= 2;
     }
     // int8 x int8 with few tiles: the largest split that still gives every
@@ -860,7 +851,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
     // of the CUs.  At 816 x 2048 x 16384 that is two splits on 224 CUs: the
     // GEMM takes the time of four splits at two blocks per CU (38.1 us) and
     // the reduction reads half the partials (4.8 us instead of 7.2 us).
-    if (!int4 && !a8) {
+    if (allow_split && !int4 && !a8) {
         int deep_splits = 1;
         while (tiles * deep_splits * 2 <= cus && stages / (deep_splits * 2) >= 16) deep_splits *= 2;
         if (deep_splits >= 2 && tiles * deep_splits * 4 >= cus * 3 && tiles * splits > cus) splits = deep_splits;
@@ -931,7 +922,7 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
     if (!int4) return hipErrorInvalidValue;   // the gate|up projections run at W4A4
     hipError_t e = ensure_gelu_neg_tab(st);
     if (e != hipSuccess) return e;
-    const GemmPlan plan = plan_gemm(m, n, k, int4, false);   // tile shape; the fused epilogue takes no split
+    const GemmPlan plan = plan_gemm(m, n, k, int4, false, false);   // tile shape; the fused epilogue takes no split
     GemmParams p;
     p.a = static_cast<const int8_t*>(xq);
     p.b = static_cast<const int8_t*>(wq);

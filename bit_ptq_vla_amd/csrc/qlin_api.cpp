@@ -67,7 +67,11 @@ qlin_status check_device() {
     return g_device_ok[dev] == 1 ? QLIN_OK : QLIN_ERR_DEVICE;
 }
 
-qlin_status map_err(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN_ERR_LAUNCH; }
+qlin_status map_err(hipError_t e) {
+    if (e == hipSuccess) return QLIN_OK;
+    if (e == hipErrorStreamCaptureUnsupported) return QLIN_ERR_CAPTURE;
+    return QLIN_ERR_LAUNCH;
+}
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -78,45 +82,62 @@ constexpr int64_t kMaxRowK = 32768;
 // GEMM k bound (exclusive): 2^17.
 constexpr int64_t kMaxGemmK = 131072;
 
+// Shape checks of the integer GEMM schemes (before any pointer check).
+bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, bool int4) {
+    // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
+    const int64_t kstep = int4 ? 128 : 64;
+    if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return false;
+    // k < 2^17: the accumulator, 256 * acc for W4A4 and 16 * acc for W4A8,
+    // stays below 2^31 in magnitude for any codes (|code| <= 8 int4, 128 int8)
+    if (k >= kMaxGemmK) return false;
+    return m <= 0x7FFFFFFF && n <= 0x7FFFFFFF;
+}
+
+// Split-K partial bytes of the plan a call with a workspace takes (0: no split).
+int64_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
+    if (m == 0 || m <= qlin::kSkinnyIntMaxM) return 0;   // the small-M kernel never splits
+    return qlin::plan_gemm(m, n, k, int4, a8, true).ws_bytes;
+}
+
 qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
-                        int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream,
-                        bool int4, bool a8) {
+                        int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* ws, int64_t ws_bytes,
+                        void* stream, bool int4, bool a8) {
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !y) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_F16 && y_dtype != QLIN_BF16 && y_dtype != QLIN_F32 && y_dtype != QLIN_I32)
         return QLIN_ERR_DTYPE;
-    // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
-    const int64_t kstep = int4 ? 128 : 64;
-    if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return QLIN_ERR_SHAPE;
-    // k < 2^17: the accumulator, 256 * acc for W4A4 and 16 * acc for W4A8,
-    // stays below 2^31 in magnitude for any codes (|code| <= 8 int4, 128 int8)
-    if (k >= kMaxGemmK) return QLIN_ERR_SHAPE;
-    if (m > 0x7FFFFFFF || n > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
-    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))
+    if (!gemm_shape_ok(m, n, k, int4)) return QLIN_ERR_SHAPE;
+    if (ws_bytes < 0) return QLIN_ERR_SHAPE;
+    if (!ws && ws_bytes > 0) return QLIN_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale) ||
+        !aligned16(ws))
         return QLIN_ERR_ALIGN;
+    const int64_t need = ws ? gemm_ws_need(m, n, k, int4, a8) : 0;
+    if (ws && ws_bytes < need) return QLIN_ERR_WORKSPACE;
     const int64_t kb = int4 ? k / 2 : k;
     const int64_t ka = (int4 && !a8) ? k / 2 : k;
-    const Span outs[1] = {{y, m * n * dtype_size(y_dtype)}};
+    const Span outs[2] = {{y, m * n * dtype_size(y_dtype)}, {ws, ws ? ws_bytes : 0}};
     const Span ins[4] = {{xq, m * ka}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
-    if (any_overlap(outs, 1, ins, 4)) return QLIN_ERR_ALIAS;
+    if (any_overlap(outs, 2, ins, 4)) return QLIN_ERR_ALIAS;
     if (m == 0) return QLIN_OK;
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
     if (m <= qlin::kSkinnyIntMaxM)
         return map_err(qlin::launch_skinny_int(xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, s));
-    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8);
-    int32_t* ws = nullptr;
-    if (plan.ws_bytes > 0) {
-        if (hipMallocAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.ws_bytes), s) != hipSuccess)
-            return QLIN_ERR_DEVICE;
+    const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8, ws != nullptr);
+    return map_err(qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype,
+                                     static_cast<int32_t*>(ws), s));
+}
+
+bool scheme_flags(qlin_scheme scheme, bool* int4, bool* a8) {
+    switch (scheme) {
+        case QLIN_W4A4: *int4 = true; *a8 = false; return true;
+        case QLIN_W8A8: *int4 = false; *a8 = false; return true;
+        case QLIN_W4A8: *int4 = true; *a8 = true; return true;
     }
-    hipError_t e = qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, ws, s);
-    if (ws) {
-        if (hipFreeAsync(ws, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
-    }
-    return map_err(e);
+    return false;
 }
 
 // Shared checks of the per-step table entry points (rows of k values, no pre-op).
@@ -144,19 +165,12 @@ qlin_status composite_check(const void* x, qlin_dtype dt, int64_t rows, int64_t 
     return QLIN_OK;
 }
 
-// The rotated rows (fp32 [rows][k]) go through a stream-ordered workspace.
+// The rotated rows (fp32 [rows][k]) go through the caller's workspace.
 qlin_status composite_run(const void* x, qlin_dtype dt, int64_t rows, int64_t k, int64_t ldx, const float* mult,
                           const int32_t* perm, const float* rot, int32_t b, int32_t bits, void* q, float* scale,
                           float* work, void* stream) {
-    hipStream_t s = as_stream(stream);
-    if (work) return map_err(qlin::launch_composite_quant(x, dt, rows, k, ldx, mult, perm, rot, b, bits, q, scale,
-                                                          work, s));
-    float* v = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void**>(&v), static_cast<size_t>(rows * k * 4), s) != hipSuccess)
-        return QLIN_ERR_DEVICE;
-    hipError_t e = qlin::launch_composite_quant(x, dt, rows, k, ldx, mult, perm, rot, b, bits, q, scale, v, s);
-    if (hipFreeAsync(v, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
-    return map_err(e);
+    return map_err(qlin::launch_composite_quant(x, dt, rows, k, ldx, mult, perm, rot, b, bits, q, scale, work,
+                                                as_stream(stream)));
 }
 
 }  // namespace
@@ -176,6 +190,8 @@ const char* qlin_status_string(qlin_status s) {
         case QLIN_ERR_DEVICE: return "no usable gfx950 device or HIP runtime error";
         case QLIN_ERR_LAUNCH: return "kernel launch failed";
         case QLIN_ERR_ALIAS: return "output overlaps an input";
+        case QLIN_ERR_CAPTURE: return "first use of a lookup table inside stream capture";
+        case QLIN_ERR_WORKSPACE: return "workspace smaller than the call needs";
     }
     return "unknown status";
 }
@@ -302,26 +318,30 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
                                                    wq, w_scale, as_stream(stream)));
 }
 
+int64_t qlin_calibrate_composite_work_bytes(int64_t n, int64_t k, int32_t had_block) {
+    if (n < 1 || k < 1 || (had_block != 16 && had_block != 32 && had_block != 64 && had_block != 128) ||
+        k % had_block != 0 || k > kMaxRowK)
+        return -1;
+    return qlin::composite_calib_work_bytes(n, k, had_block);
+}
+
 qlin_status qlin_calibrate_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
                                      const float* fold_s, int32_t had_block, int32_t* perm, float* rot,
-                                     void* stream) {
+                                     void* work, int64_t work_bytes, void* stream) {
     qlin_status st = composite_check(w, w_dtype, n, k, k, had_block);
     if (st != QLIN_OK) return st;
-    if (!w || !perm || !rot) return QLIN_ERR_NULL;
+    if (!w || !perm || !rot || !work) return QLIN_ERR_NULL;
     if (n < 1) return QLIN_ERR_SHAPE;
-    if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot)) return QLIN_ERR_ALIGN;
-    const Span outs[2] = {{perm, k * 4}, {rot, k * had_block * 4}};
+    if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(work))
+        return QLIN_ERR_ALIGN;
+    if (work_bytes < qlin::composite_calib_work_bytes(n, k, had_block)) return QLIN_ERR_WORKSPACE;
+    const Span outs[3] = {{perm, k * 4}, {rot, k * had_block * 4}, {work, work_bytes}};
     const Span ins[2] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}};
-    if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
+    if (any_overlap(outs, 3, ins, 2)) return QLIN_ERR_ALIAS;
     st = check_device();
     if (st != QLIN_OK) return st;
-    hipStream_t s = as_stream(stream);
-    void* work = nullptr;
-    const int64_t bytes = qlin::composite_calib_work_bytes(n, k, had_block);
-    if (hipMallocAsync(&work, static_cast<size_t>(bytes), s) != hipSuccess) return QLIN_ERR_DEVICE;
-    hipError_t e = qlin::launch_calibrate_composite(w, w_dtype, n, k, fold_s, had_block, perm, rot, work, s);
-    if (hipFreeAsync(work, s) != hipSuccess && e == hipSuccess) return QLIN_ERR_DEVICE;
-    return map_err(e);
+    return map_err(qlin::launch_calibrate_composite(w, w_dtype, n, k, fold_s, had_block, perm, rot, work,
+                                                    as_stream(stream)));
 }
 
 qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
@@ -331,13 +351,13 @@ qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, i
     qlin_status st = composite_check(x, x_dtype, m, k, ldx, had_block);
     if (st != QLIN_OK) return st;
     if (!perm || !rot) return QLIN_ERR_NULL;
-    if (m > 0 && (!xq || !x_scale)) return QLIN_ERR_NULL;
+    if (m > 0 && (!xq || !x_scale || !work)) return QLIN_ERR_NULL;
     if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(fold_inv_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(xq) ||
         !aligned16(x_scale) || !aligned16(work))
         return QLIN_ERR_ALIGN;
     const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
-    const Span outs[3] = {{xq, code_bytes}, {x_scale, m * 4}, {work, work ? m * k * 4 : 0}};
+    const Span outs[3] = {{xq, code_bytes}, {x_scale, m * 4}, {work, m * k * 4}};
     const Span ins[4] = {{x, m > 0 ? ((m - 1) * ldx + k) * dtype_size(x_dtype) : 0},
                          {fold_inv_s, fold_inv_s ? k * 4 : 0}, {perm, k * 4}, {rot, k * had_block * 4}};
     if (any_overlap(outs, 3, ins, 4)) return QLIN_ERR_ALIAS;
@@ -350,38 +370,54 @@ qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, i
 qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
                                             const float* fold_s, const int32_t* perm, const float* rot,
                                             int32_t had_block, int32_t bits, void* wq, float* w_scale,
-                                            void* stream) {
+                                            float* work, void* stream) {
     qlin_status st = composite_check(w, w_dtype, n, k, k, had_block);
     if (st != QLIN_OK) return st;
-    if (!w || !perm || !rot || !wq || !w_scale) return QLIN_ERR_NULL;
+    if (!w || !perm || !rot || !wq || !w_scale || !work) return QLIN_ERR_NULL;
     if (n < 1) return QLIN_ERR_SHAPE;
     if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
     if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(wq) ||
-        !aligned16(w_scale))
+        !aligned16(w_scale) || !aligned16(work))
         return QLIN_ERR_ALIGN;
     const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
-    const Span outs[2] = {{wq, code_bytes}, {w_scale, n * 4}};
+    const Span outs[3] = {{wq, code_bytes}, {w_scale, n * 4}, {work, n * k * 4}};
     const Span ins[4] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}, {perm, k * 4},
                          {rot, k * had_block * 4}};
-    if (any_overlap(outs, 2, ins, 4)) return QLIN_ERR_ALIAS;
+    if (any_overlap(outs, 3, ins, 4)) return QLIN_ERR_ALIAS;
     st = check_device();
     if (st != QLIN_OK) return st;
-    return composite_run(w, w_dtype, n, k, k, fold_s, perm, rot, had_block, bits, wq, w_scale, nullptr, stream);
+    return composite_run(w, w_dtype, n, k, k, fold_s, perm, rot, had_block, bits, wq, w_scale, work, stream);
 }
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, true, false);
 }
 
 qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, false, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, false, false);
 }
 
 qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, stream, true, true);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, true, true);
+}
+
+int64_t qlin_gemm_workspace_bytes(qlin_scheme scheme, int64_t m, int64_t n, int64_t k) {
+    bool int4 = false, a8 = false;
+    if (!scheme_flags(scheme, &int4, &a8)) return -1;
+    if (!gemm_shape_ok(m, n, k, int4)) return -1;
+    return gemm_ws_need(m, n, k, int4, a8);
+}
+
+qlin_status qlin_gemm_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                         const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+    bool int4 = false, a8 = false;
+    if (!scheme_flags(scheme, &int4, &a8)) return QLIN_ERR_UNSUPPORTED;
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, workspace, workspace_bytes, stream, int4,
+                       a8);
 }
 
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

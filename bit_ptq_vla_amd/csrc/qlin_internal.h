@@ -9,6 +9,18 @@ namespace qlin {
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cus();
 
+// Device-resident lookup tables filled once per device.  The first call on a
+// device runs `fill` on a private stream and waits for it, so every later call
+// on any stream or thread reads the finished table; a table is never in use
+// while it is written.  A first call made while `caller` is being captured
+// into a graph returns hipErrorStreamCaptureUnsupported (the fill cannot go
+// into the caller's graph, and the host wait is not allowed there); later
+// calls, captured or not, return hipSuccess at once.
+struct OncePerDevice {
+    bool ready[64] = {false};
+};
+hipError_t fill_once_per_device(OncePerDevice& once, hipStream_t caller, hipError_t (*fill)(hipStream_t));
+
 int row_quant_lanes(int64_t k);
 int row_quant_chunks(int64_t k, int g);
 
@@ -56,8 +68,9 @@ struct GemmPlan {
     bool deep;      // grid fits one block per CU: one block per CU with a deeper DMA ring
     int64_t ws_bytes;
 };
-// a8 (with int4): int8 activations against int4 weights (W4A8).
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8);
+// a8 (with int4): int8 activations against int4 weights (W4A8).  Split-K
+// only when allow_split (the caller supplies the partials' workspace).
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool allow_split);
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
                        const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st);

@@ -26,10 +26,15 @@
  *    elements and must keep each row 16-byte aligned.  Outputs must not
  *    overlap inputs.
  *  - m == 0 (no tokens) is a valid empty call: QLIN_OK, nothing launched.
- *  - Entry points are thread-safe.  qlin_gemm_* may take device memory for
- *    split-K partial sums from the stream-ordered allocator
- *    (hipMallocAsync/hipFreeAsync on `stream`); no other entry point
- *    allocates.
+ *  - Entry points are thread-safe.  No entry point allocates device memory:
+ *    scratch (split-K partial sums, rotated rows, calibration temporaries)
+ *    comes from a caller-owned workspace argument where an operation needs
+ *    one, with a *_bytes query of its size.
+ *  - Two lookup tables (the GeLU values of the GeGLU paths) are filled once
+ *    per device by the first call that needs them, on a private stream that
+ *    the library waits for; if that first call is made while `stream` is
+ *    being captured into a graph it returns QLIN_ERR_CAPTURE (make one such
+ *    call outside capture first).
  *  - Codes: int8 codes are int8_t[rows][k]; int4 codes are packed two per
  *    byte, uint8_t[rows][k/2], element 2j in the low nibble and 2j+1 in the
  *    high nibble, two's complement.  Both grids are symmetric: codes lie in
@@ -45,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QLIN_ABI_VERSION 1
+#define QLIN_ABI_VERSION 2
 
 typedef int32_t qlin_status;
 enum {
@@ -57,7 +62,9 @@ enum {
     QLIN_ERR_UNSUPPORTED = 5, /* bits / block / group / pre-op value not supported */
     QLIN_ERR_DEVICE = 6,      /* no usable gfx950 device / HIP runtime error      */
     QLIN_ERR_LAUNCH = 7,      /* kernel launch failed (hipGetLastError)           */
-    QLIN_ERR_ALIAS = 8        /* an output overlaps an input                      */
+    QLIN_ERR_ALIAS = 8,       /* an output overlaps an input                      */
+    QLIN_ERR_CAPTURE = 9,     /* first use of a lookup table inside stream capture */
+    QLIN_ERR_WORKSPACE = 10   /* workspace smaller than the call needs            */
 };
 
 typedef int32_t qlin_dtype;
@@ -65,6 +72,10 @@ enum { QLIN_F16 = 0, QLIN_BF16 = 1, QLIN_F32 = 2, QLIN_I32 = 3 };
 
 typedef int32_t qlin_preop;
 enum { QLIN_PRE_NONE = 0, QLIN_PRE_GEGLU = 1 };
+
+/* Integer GEMM schemes: activation codes x weight codes. */
+typedef int32_t qlin_scheme;
+enum { QLIN_W4A4 = 0, QLIN_W8A8 = 1, QLIN_W4A8 = 2 };
 
 /* Version of this ABI (QLIN_ABI_VERSION). */
 int32_t qlin_abi_version(void);
@@ -189,9 +200,8 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
  * clamp(rne(v / scale), +-qmax), layouts as the Hadamard entry points; codes
  * are in the permuted channel order on both sides, so the GEMM is unchanged).
  * The dot products take fp32 operands with an fp64 sum, rounded to fp32;
- * the rotated rows pass through fp32 [rows][k] scratch: `work` when given
- * (device, 16-byte aligned, rows * k floats, contents overwritten), else a
- * stream-ordered temporary.
+ * the rotated rows pass through the caller's fp32 scratch `work` (device,
+ * 16-byte aligned, rows * k floats, contents overwritten; required).
  *
  * qlin_calibrate_composite -- perm and R from the weights w [n][k] (times
  *   fold_s): channels ranked by descending L2 norm of their column (lower
@@ -202,20 +212,23 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
  *   C_in x C_out) by descending eigenvalue, each with its largest-magnitude
  *   entry positive; R_j = U_j H_b / sqrt(b) (Sylvester H).  Eigenvectors of
  *   repeated eigenvalues are any orthonormal basis of their space.
- *   perm: out int32[k]; rot: out float[k/b][b][b].  Takes a temporary of
- *   about 8 (k b + k n / 256 + k) bytes from the stream-ordered allocator.
+ *   perm: out int32[k]; rot: out float[k/b][b][b].  work: device scratch of
+ *   work_bytes >= qlin_calibrate_composite_work_bytes(n, k, b) bytes, 16-byte
+ *   aligned (about 8 (k b + k n / 256 + k) bytes; QLIN_ERR_WORKSPACE if
+ *   smaller).
  * qlin_rotate_quant_act_composite -- activations x [m][ldx] with fold_inv_s
  *   (1/s or NULL), perm and rot as written by the calibration; xq, x_scale out.
  * qlin_quantize_weights_composite -- weights w [n][k] with fold_s (s or
- *   NULL); wq, w_scale out.
+ *   NULL); wq, w_scale out; work as above (n * k floats).
  * Preconditions: had_block b in {16, 32, 64, 128} dividing k; k % 8 == 0;
  * k <= 32768; bits 4 or 8;
  * perm a permutation of 0 .. k-1 (other values are clamped into range).
  * Errors as the Hadamard entry points.
  */
+int64_t qlin_calibrate_composite_work_bytes(int64_t n, int64_t k, int32_t had_block);
 qlin_status qlin_calibrate_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
                                      const float* fold_s, int32_t had_block, int32_t* perm, float* rot,
-                                     void* stream);
+                                     void* work, int64_t work_bytes, void* stream);
 qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
                                             int64_t ldx, const float* fold_inv_s, const int32_t* perm,
                                             const float* rot, int32_t had_block, int32_t bits, void* xq,
@@ -223,7 +236,7 @@ qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, i
 qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
                                             const float* fold_s, const int32_t* perm, const float* rot,
                                             int32_t had_block, int32_t bits, void* wq, float* w_scale,
-                                            void* stream);
+                                            float* work, void* stream);
 
 /*
  * qlin_gemm_w4a4 / qlin_gemm_w8a8 -- integer GEMM with int32 accumulation
@@ -240,6 +253,9 @@ qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, i
  * Preconditions: m >= 0, n >= 1; k a multiple of 64 (w8a8) or of 128 (w4a4),
  * at least one such step; k < 131072 (2^17), which keeps every int32
  * accumulator exact for any codes, -8 and -128 included.
+ * These calls never split k (no scratch); a grid of few output tiles with a
+ * long k (the FFN-down projection at a few hundred tokens) runs faster
+ * through qlin_gemm_ws with a workspace.
  */
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq,
                            const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
@@ -256,12 +272,34 @@ qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq,
  *   wq:      uint8 [n][k/2] packed int4 (qlin_quantize_weights with bits 4);
  *   acc, y, scales, dtypes, stream and errors exactly as qlin_gemm_w4a4.
  * Preconditions: k a multiple of 128, below 131072; otherwise those of
- * qlin_gemm_w4a4.  May take a split-K workspace from the stream-ordered
- * allocator, as the other GEMMs.
+ * qlin_gemm_w4a4.
  */
 qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
                            const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
                            qlin_dtype y_dtype, void* stream);
+
+/*
+ * qlin_gemm_ws -- the integer GEMM of qlin_gemm_w4a4 / _w8a8 / _w4a8
+ * (scheme QLIN_W4A4, QLIN_W8A8 or QLIN_W4A8; same arguments, results and
+ * preconditions) with a caller-owned workspace for split-K partial sums.
+ * When the output tile grid leaves the chip under-filled and k is long, the
+ * call splits k over several blocks per tile: each split writes int32 partial
+ * accumulators to the workspace ([splits][m][n]) and a second kernel adds
+ * them in split order (exact integer sums, so the result is bit-identical to
+ * the unsplit GEMM) and applies the epilogue.
+ *   workspace        device memory, 16-byte aligned, contents overwritten; or
+ *                    NULL with workspace_bytes 0 (then no split, as
+ *                    qlin_gemm_w4a4 and co.).
+ *   workspace_bytes  its size; at least qlin_gemm_workspace_bytes(scheme, m, n, k)
+ *                    when workspace is not NULL, else QLIN_ERR_WORKSPACE.
+ * Two calls in flight on different streams need different workspaces.
+ * qlin_gemm_workspace_bytes returns the bytes the split plan of that shape
+ * needs (0 when it takes no split), or -1 for an invalid scheme or shape.
+ */
+int64_t qlin_gemm_workspace_bytes(qlin_scheme scheme, int64_t m, int64_t n, int64_t k);
+qlin_status qlin_gemm_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                         const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                         qlin_dtype y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * qlin_gemm_w4a4_geglu -- the backbone MLP's gate and up projections with the
@@ -281,8 +319,8 @@ qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
  * 131072.  Errors: NULL pointers (QLIN_ERR_NULL), other dtypes
  * (QLIN_ERR_DTYPE), shapes (QLIN_ERR_SHAPE), pointers not 16-byte aligned
  * (QLIN_ERR_ALIGN), h overlapping an input (QLIN_ERR_ALIAS); m == 0 returns
- * QLIN_OK without touching the device.  Never allocates; the first call on a
- * device also fills a static 8 KB table there (on the same stream).
+ * QLIN_OK without touching the device.  The first call on a device also
+ * fills a static 8 KB GeLU table there (see the conventions above).
  */
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq,
                                  const float* w_scale, int64_t m, int64_t n2, int64_t k, void* h,

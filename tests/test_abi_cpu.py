@@ -31,7 +31,7 @@ def lib():
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:qlin_status|int32_t|const char\*)\s+(qlin_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:qlin_status|int32_t|int64_t|const char\*)\s+(qlin_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
               "qlin_gemm_w4a4_geglu", "qlin_gemv_w4a16", "qlin_calibrate_fold", "qlin_abi_version",
               "qlin_status_string", "qlin_calibrate_step_scales", "qlin_rotate_quant_act_static",
               "qlin_quantize_weights_step", "qlin_calibrate_composite", "qlin_rotate_quant_act_composite",
-              "qlin_quantize_weights_composite"):
+              "qlin_quantize_weights_composite", "qlin_calibrate_composite_work_bytes", "qlin_gemm_ws",
+              "qlin_gemm_workspace_bytes"):
         assert n in names
 
 
@@ -51,8 +52,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qlin_abi_version() == 1
-    for s in range(0, 9):
+    assert lib.qlin_abi_version() == 2
+    for s in range(0, 11):
         assert lib.qlin_status_string(s).decode() not in ("", "unknown status")
     assert lib.qlin_status_string(99).decode() == "unknown status"
 
@@ -135,6 +136,46 @@ def test_gemm_k_step_per_scheme(lib, fn, k, status):
 def test_gemm_raw_i32_needs_no_scales_and_empty_ok(lib):
     # no scales with I32 output passes validation; m == 0 then returns before any HIP call
     assert lib.qlin_gemm_w8a8(None, None, P2, None, 0, 64, 512, 0x70000000, 3, None) == q.QLIN_OK
+
+
+# ---- qlin_gemm_ws(scheme, xq, sx, wq, sw, m, n, k, y, ydt, ws, ws_bytes, stream)
+
+DOWN = dict(m=816, n=2048, k=16384)   # the FFN-down shape at 816 tokens: 112 tiles, k split in two
+
+
+def test_gemm_workspace_bytes(lib):
+    # 2 splits x 816 x 2048 int32 partials (planned for 256 CUs: the default without a device)
+    if not torch.cuda.is_available():
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 816, 2048, 16384) == 2 * 816 * 2048 * 4
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 52224, 2048, 16384) == 0    # large grid: no split
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 50, 1024, 4096) == 0        # small-M kernel: no split
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 192) == -1       # int4 k step is 128
+    assert lib.qlin_gemm_workspace_bytes(3, 816, 2048, 16384) == -1               # no such scheme
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 0, 2048, 16384) == 0
+
+
+def gemm_ws(lib, scheme=q.QLIN_W8A8, xq=P, sx=P3, wq=P2, sw=P4, m=DOWN["m"], n=DOWN["n"], k=DOWN["k"],
+            y=0x70000000, ydt=1, ws=0x7C000000, wsb=64 << 20):
+    return lib.qlin_gemm_ws(scheme, xq, sx, wq, sw, m, n, k, y, ydt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scheme=3), q.QLIN_ERR_UNSUPPORTED), (dict(scheme=-1), q.QLIN_ERR_UNSUPPORTED),
+    (dict(ws=None), q.QLIN_ERR_NULL),                      # bytes > 0 with no buffer
+    (dict(wsb=-16), q.QLIN_ERR_SHAPE), (dict(ws=0x7C000008), q.QLIN_ERR_ALIGN),
+    (dict(wsb=1024), q.QLIN_ERR_WORKSPACE),                # smaller than the split plan needs
+    (dict(ws=0x70000000 + 4096), q.QLIN_ERR_ALIAS),         # workspace overlaps y
+    (dict(ws=P2 + 64), q.QLIN_ERR_ALIAS),                   # workspace overlaps the weights
+    (dict(k=100), q.QLIN_ERR_SHAPE), (dict(xq=None), q.QLIN_ERR_NULL), (dict(ydt=7), q.QLIN_ERR_DTYPE),
+])
+def test_gemm_ws_rejects(lib, kw, status):
+    assert gemm_ws(lib, **kw) == status
+
+
+def test_gemm_ws_empty_and_no_workspace_ok(lib):
+    assert gemm_ws(lib, m=0) == q.QLIN_OK
+    assert gemm_ws(lib, m=0, ws=None, wsb=0) == q.QLIN_OK
+    assert gemm_ws(lib, m=0, wsb=16) == q.QLIN_OK            # no split needed for an empty call
 
 
 # ---- qlin_gemm_w4a4_geglu(xq, sx, wq, sw, m, n2, k, h, hdt, stream)
@@ -240,23 +281,34 @@ def test_quantize_weights_step_rejects(lib, kw, status):
 
 # ---- composite rotation entry points
 
-# qlin_calibrate_composite(w, dt, n, k, fold_s, b, perm, rot, stream)
+# qlin_calibrate_composite(w, dt, n, k, fold_s, b, perm, rot, work, work_bytes, stream)
 @pytest.mark.parametrize("kw,status", [
     (dict(w=None), q.QLIN_ERR_NULL), (dict(perm=None), q.QLIN_ERR_NULL), (dict(rot=None), q.QLIN_ERR_NULL),
+    (dict(work=None), q.QLIN_ERR_NULL), (dict(work=BAD), q.QLIN_ERR_ALIGN), (dict(wb=64), q.QLIN_ERR_WORKSPACE),
+    (dict(work=P + 256), q.QLIN_ERR_ALIAS),
     (dict(dt=3), q.QLIN_ERR_DTYPE), (dict(b=8), q.QLIN_ERR_UNSUPPORTED), (dict(b=256), q.QLIN_ERR_UNSUPPORTED),
     (dict(b=48), q.QLIN_ERR_UNSUPPORTED), (dict(n=0), q.QLIN_ERR_SHAPE), (dict(k=520), q.QLIN_ERR_SHAPE),
     (dict(k=65536), q.QLIN_ERR_SHAPE), (dict(rot=BAD), q.QLIN_ERR_ALIGN), (dict(s=BAD), q.QLIN_ERR_ALIGN),
     (dict(perm=P + 64), q.QLIN_ERR_ALIAS), (dict(rot=P3 + 512), q.QLIN_ERR_ALIAS),
 ])
 def test_calibrate_composite_rejects(lib, kw, status):
-    a = dict(w=P, dt=0, n=16, k=512, s=None, b=64, perm=P3, rot=P4)
+    a = dict(w=P, dt=0, n=16, k=512, s=None, b=64, perm=P3, rot=P4, work=0x50000000, wb=1 << 20)
     a.update(kw)
     assert lib.qlin_calibrate_composite(a["w"], a["dt"], a["n"], a["k"], a["s"], a["b"], a["perm"], a["rot"],
-                                        None) == status
+                                        a["work"], a["wb"], None) == status
+
+
+def test_calibrate_composite_work_bytes(lib):
+    nb = lib.qlin_calibrate_composite_work_bytes(16, 512, 64)
+    assert 8 * 512 * 64 <= nb <= 1 << 20
+    assert lib.qlin_calibrate_composite_work_bytes(16, 512, 48) == -1
+    assert lib.qlin_calibrate_composite_work_bytes(0, 512, 64) == -1
+    assert lib.qlin_calibrate_composite_work_bytes(16, 520, 64) == -1
 
 
 # qlin_rotate_quant_act_composite(x, dt, m, k, ldx, inv_s, perm, rot, b, bits, xq, xs, work, stream)
 @pytest.mark.parametrize("kw,status", [
+    (dict(work=None), q.QLIN_ERR_NULL),
     (dict(work=BAD), q.QLIN_ERR_ALIGN), (dict(work=P2 + 512), q.QLIN_ERR_ALIAS), (dict(work=P + 1024), q.QLIN_ERR_ALIAS),
     (dict(x=None), q.QLIN_ERR_NULL), (dict(perm=None), q.QLIN_ERR_NULL), (dict(xq=None), q.QLIN_ERR_NULL),
     (dict(xs=None), q.QLIN_ERR_NULL), (dict(dt=5), q.QLIN_ERR_DTYPE), (dict(b=4), q.QLIN_ERR_UNSUPPORTED),
@@ -266,7 +318,7 @@ def test_calibrate_composite_rejects(lib, kw, status):
 ])
 def test_rotate_quant_act_composite_rejects(lib, kw, status):
     a = dict(x=P, dt=1, m=4, k=512, ldx=512, inv=None, perm=P3, rot=P4, b=64, bits=4, xq=P2, xs=0x70000000,
-             work=None)
+             work=0x50000000)
     a.update(kw)
     assert lib.qlin_rotate_quant_act_composite(a["x"], a["dt"], a["m"], a["k"], a["ldx"], a["inv"], a["perm"],
                                                a["rot"], a["b"], a["bits"], a["xq"], a["xs"], a["work"],
@@ -278,17 +330,18 @@ def test_rotate_quant_act_composite_empty_is_ok(lib):
                                                None) == q.QLIN_OK
 
 
-# qlin_quantize_weights_composite(w, dt, n, k, fold_s, perm, rot, b, bits, wq, ws, stream)
+# qlin_quantize_weights_composite(w, dt, n, k, fold_s, perm, rot, b, bits, wq, ws, work, stream)
 @pytest.mark.parametrize("kw,status", [
     (dict(w=None), q.QLIN_ERR_NULL), (dict(rot=None), q.QLIN_ERR_NULL), (dict(ws=None), q.QLIN_ERR_NULL),
+    (dict(work=None), q.QLIN_ERR_NULL), (dict(work=BAD), q.QLIN_ERR_ALIGN), (dict(work=0x70000000), q.QLIN_ERR_ALIAS),
     (dict(b=512), q.QLIN_ERR_UNSUPPORTED), (dict(bits=3), q.QLIN_ERR_UNSUPPORTED), (dict(n=0), q.QLIN_ERR_SHAPE),
     (dict(k=96), q.QLIN_ERR_SHAPE), (dict(wq=BAD), q.QLIN_ERR_ALIGN), (dict(wq=P + 128), q.QLIN_ERR_ALIAS),
 ])
 def test_quantize_weights_composite_rejects(lib, kw, status):
-    a = dict(w=P, dt=0, n=8, k=512, s=None, perm=P3, rot=P4, b=64, bits=4, wq=P2, ws=0x70000000)
+    a = dict(w=P, dt=0, n=8, k=512, s=None, perm=P3, rot=P4, b=64, bits=4, wq=P2, ws=0x70000000, work=0x50000000)
     a.update(kw)
     assert lib.qlin_quantize_weights_composite(a["w"], a["dt"], a["n"], a["k"], a["s"], a["perm"], a["rot"],
-                                               a["b"], a["bits"], a["wq"], a["ws"], None) == status
+                                               a["b"], a["bits"], a["wq"], a["ws"], a["work"], None) == status
 
 
 def test_binding_raises_qlin_error(lib):

@@ -404,14 +404,25 @@ def scheme_codes(scheme, tag, m, n, k):
     return a, b, abits, wbits, getattr(q, fn)
 
 
+def workspace_for(scheme, m, n, k):
+    """The split-K workspace of qlin_gemm_ws for this shape (None: no split)."""
+    return q.gemm_workspace({"w4a4": q.QLIN_W4A4, "w8a8": q.QLIN_W8A8, "w4a8": q.QLIN_W4A8}[scheme], m, n, k, DEV)
+
+
+@pytest.mark.parametrize("ws", [False, True], ids=["plain", "workspace"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 @pytest.mark.parametrize("scheme", ["w4a4", "w8a8", "w4a8"])
-def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k):
-    say(f"gemm i32 {scheme} {m}x{n}x{k}")
+def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k, ws):
+    """Plain entry points (never split k) and qlin_gemm_ws with its workspace
+    (split-K on the shapes marked so): raw int32 accumulators, bit-exact."""
+    say(f"gemm i32 {scheme} {m}x{n}x{k} ws={ws}")
     if scheme != "w8a8" and k % 128:
         pytest.skip("int4 weights take k in multiples of 128")
+    work = workspace_for(scheme, m, n, k) if ws else None
+    if ws and work is None:
+        pytest.skip("no split-K at this shape: the workspace call is the plain call")
     a, b, abits, wbits, fn = scheme_codes(scheme, "", m, n, k)
-    acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
+    acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32, workspace=work)
     torch.cuda.synchronize()
     ref = oracle.int_gemm(codes_np(a, abits), codes_np(b, wbits))
     got = acc.cpu().numpy().astype(np.int64)
@@ -468,10 +479,17 @@ def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     a, b, abits, wbits, fn = scheme_codes(scheme, "e", m, n, k)
     sx = synth.random_scales(SEED, f"sx/{m}", m)
     sw = synth.random_scales(SEED, f"sw/{n}", n)
-    y = fn(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, y_dtype=DT[out])
+    a, b, sx, sw = a.to(DEV), b.to(DEV), sx.to(DEV), sw.to(DEV)
+    y = fn(a, sx, b, sw, k, y_dtype=DT[out])
+    work = workspace_for(scheme, m, n, k)
+    y_ws = fn(a, sx, b, sw, k, y_dtype=DT[out], workspace=work) if work is not None else y
     torch.cuda.synchronize()
-    _, _, y_ref = oracle.gemm(codes_np(a, abits), sx.numpy(), codes_np(b, wbits), sw.numpy(), out)
+    _, _, y_ref = oracle.gemm(codes_np(a.cpu(), abits), sx.cpu().numpy(), codes_np(b.cpu(), wbits),
+                              sw.cpu().numpy(), out)
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
+    # the split-K reduction applies the same epilogue arithmetic: bit-identical outputs
+    bits = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(y.view(bits), y_ws.view(bits))
 
 
 GEGLU_SHAPES = [
@@ -571,8 +589,9 @@ def test_gemm_deterministic():
     b = synth.random_codes(SEED, "Bd", 256, 16384, 8).to(DEV)
     sx = synth.random_scales(SEED, "sxd", 129).to(DEV)
     sw = synth.random_scales(SEED, "swd", 256).to(DEV)
-    y1 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384)
-    y2 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384)
+    work = workspace_for("w8a8", 129, 256, 16384)
+    y1 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384, workspace=work)
+    y2 = q.qlin_gemm_w8a8(a, sx, b, sw, 16384, workspace=work)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
@@ -744,7 +763,8 @@ def test_backbone_mlp_block_stagewise_full_size():
     s2, inv2 = q.qlin_calibrate_fold(y1, wdd, pre=q.QLIN_PRE_GEGLU)
     wq2, ws2 = q.qlin_quantize_weights(wdd, fold_s=s2, had_block=128, bits=8)
     hq, hs = q.qlin_rotate_quant_act(y1, k=16384, fold_inv_s=inv2, had_block=128, bits=8, pre=q.QLIN_PRE_GEGLU)
-    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, 16384, y_dtype=torch.bfloat16)
+    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, 16384, y_dtype=torch.bfloat16,
+                          workspace=workspace_for("w8a8", m, dn.n, 16384))
     torch.cuda.synchronize()
     say("backbone MLP block: oracle checks")
     xf = synth.to_f64(x)
@@ -798,7 +818,7 @@ def test_backbone_mlp_block_fused_geglu_full_size():
     s2, inv2 = q.qlin_calibrate_fold(h, wdd)
     wq2, ws2 = q.qlin_quantize_weights(wdd, fold_s=s2, had_block=128, bits=8)
     hq, hs = q.qlin_rotate_quant_act(h, fold_inv_s=inv2, had_block=128, bits=8)
-    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, f, y_dtype=torch.bfloat16)
+    y2 = q.qlin_gemm_w8a8(hq, hs, wq2, ws2, f, y_dtype=torch.bfloat16, workspace=workspace_for("w8a8", m, dn.n, f))
     torch.cuda.synchronize()
     say("fused MLP block: oracle checks")
     rows = _sample_rows(m, 6)
