@@ -54,6 +54,7 @@ SIGNATURES = {
     "qlin_gemm_w4a8": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_ws": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P, _I64, _P],
     "qlin_gemm_workspace_bytes": [_I32, _I64, _I64, _I64],
+    "qlin_gemm_static_ws": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
     "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
@@ -377,6 +378,31 @@ def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out, workspac
                               y.data_ptr(), _TORCH_TO_QLIN[y.dtype], workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), _stream(wq.device))
         _check(st, "qlin_gemm_ws")
+    return y
+
+
+QLIN_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def qlin_gemm_static_ws(scheme: int, xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16,
+                        out=None) -> torch.Tensor:
+    """The integer GEMM of `scheme` with split-K partials in the library's
+    static device scratch (no workspace argument, nothing allocated by the
+    library; calls overlapping on one GPU race)."""
+    lib = load()
+    _dev_tensor(wq, "wq")
+    m, n = xq.shape[0], wq.shape[0]
+    ka = k // 2 if scheme == QLIN_W4A4 else k
+    kb = k if scheme == QLIN_W8A8 else k // 2
+    _need(xq, m * ka, "xq")
+    _need(wq, n * kb, "wq")
+    _need(x_scale, m * 4, "x_scale")
+    _need(w_scale, n * 4, "w_scale")
+    y = out if out is not None else torch.empty((m, n), dtype=y_dtype, device=wq.device)
+    _need(y, m * n * y.element_size(), "y")
+    st = lib.qlin_gemm_static_ws(scheme, xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
+                                 y.data_ptr(), _TORCH_TO_QLIN[y.dtype], _stream(wq.device))
+    _check(st, "qlin_gemm_static_ws")
     return y
 
 

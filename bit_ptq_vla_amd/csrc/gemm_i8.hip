@@ -34,6 +34,7 @@
 // Split-K writes int32 partial tiles; a second kernel sums them in a fixed
 // order (integer addition: bit-exact) and applies the epilogue.
 
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -825,6 +826,35 @@ hipError_t fill_gelu_neg_tab(hipStream_t st) {
 hipError_t ensure_gelu_neg_tab(hipStream_t st) { return fill_once_per_device(g_gtab_once, st, fill_gelu_neg_tab); }
 
 }  // namespace
+
+// Split-K scratch of the entry point for callers that cannot allocate: one
+// file-scope device array, held by every GPU the library runs on until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up
+// once per device and kept in g_scratch_dev.
+static __device__ __align__(256) int32_t scratch[kStaticScratchBytes / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+int32_t* g_scratch_dev[64] = {nullptr};
+}  // namespace
+
+hipError_t static_scratch(int32_t** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = static_cast<int32_t*>(p);
+    }
+    *ptr = g_scratch_dev[dev];
+    return hipSuccess;
+}
 
 GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool allow_split) {
     // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes

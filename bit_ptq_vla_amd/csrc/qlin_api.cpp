@@ -99,9 +99,14 @@ int64_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
     return qlin::plan_gemm(m, n, k, int4, a8, true).ws_bytes;
 }
 
+// Split-K scratch of a GEMM call: none (no split), the caller's workspace, or
+// the library's static device array.
+enum class Scratch { None, Caller, Static };
+
 qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
-                        int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* ws, int64_t ws_bytes,
-                        void* stream, bool int4, bool a8) {
+                        int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, Scratch mode, void* ws,
+                        int64_t ws_bytes, void* stream, bool int4, bool a8) {
+    const bool use_static = mode == Scratch::Static;
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !y) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
@@ -120,12 +125,20 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     const Span outs[2] = {{y, m * n * dtype_size(y_dtype)}, {ws, ws ? ws_bytes : 0}};
     const Span ins[4] = {{xq, m * ka}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
     if (any_overlap(outs, 2, ins, 4)) return QLIN_ERR_ALIAS;
+    if (use_static && gemm_ws_need(m, n, k, int4, a8) > QLIN_STATIC_SCRATCH_BYTES) return QLIN_ERR_WORKSPACE;
     if (m == 0) return QLIN_OK;
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
     if (m <= qlin::kSkinnyIntMaxM)
         return map_err(qlin::launch_skinny_int(xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, s));
+    if (use_static) {
+        int32_t* scratch_dev = nullptr;
+        if (qlin::static_scratch(&scratch_dev) != hipSuccess) return QLIN_ERR_DEVICE;
+        const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8, true);
+        return map_err(qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype,
+                                         scratch_dev, s));
+    }
     const qlin::GemmPlan plan = qlin::plan_gemm(m, n, k, int4, a8, ws != nullptr);
     return map_err(qlin::launch_gemm(plan, xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype,
                                      static_cast<int32_t*>(ws), s));
@@ -391,17 +404,18 @@ qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, i
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, true, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, false);
 }
 
 qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, false, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, false,
+                       false);
 }
 
 qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, nullptr, 0, stream, true, true);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, true);
 }
 
 int64_t qlin_gemm_workspace_bytes(qlin_scheme scheme, int64_t m, int64_t n, int64_t k) {
@@ -416,8 +430,8 @@ qlin_status qlin_gemm_ws(qlin_scheme scheme, const void* xq, const float* x_scal
                          void* workspace, int64_t workspace_bytes, void* stream) {
     bool int4 = false, a8 = false;
     if (!scheme_flags(scheme, &int4, &a8)) return QLIN_ERR_UNSUPPORTED;
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, workspace, workspace_bytes, stream, int4,
-                       a8);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::Caller, workspace, workspace_bytes,
+                       stream, int4, a8);
 }
 
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
@@ -454,6 +468,15 @@ qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, 
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
     return map_err(qlin::launch_gemv_w4a16(x, wq, w_scale, m, n, k, group, y, as_stream(stream)));
+}
+
+qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                                const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                                qlin_dtype y_dtype, void* stream) {
+    bool int4 = false, a8 = false;
+    if (!scheme_flags(scheme, &int4, &a8)) return QLIN_ERR_UNSUPPORTED;
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::Static, nullptr, 0, stream, int4,
+                       a8);
 }
 
 }  // extern "C"

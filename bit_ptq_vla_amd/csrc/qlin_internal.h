@@ -74,6 +74,10 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
                        const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st);
+// The library's static split-K scratch (kStaticScratchBytes per device):
+// its device address on the current device, looked up on first use.
+constexpr int64_t kStaticScratchBytes = 16LL << 20;
+hipError_t static_scratch(int32_t** ptr);
 // Gate|up GEMM with the GeGLU epilogue: n interleaved rows (blocks of 32 gate
 // rows then 32 up rows), y [m][n/2] = gelu(g) * u.  int4 only, no split-K.
 hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

@@ -302,6 +302,26 @@ qlin_status qlin_gemm_ws(qlin_scheme scheme, const void* xq, const float* x_scal
                          qlin_dtype y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * qlin_gemm_static_ws -- qlin_gemm_ws for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * device allocation): the split-K partials go to a static device array of
+ * QLIN_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, instead of a workspace argument.  Arguments,
+ * results, preconditions and errors as qlin_gemm_ws; the plan is the one
+ * qlin_gemm_ws takes with a large enough workspace, and a shape whose
+ * partials exceed QLIN_STATIC_SCRATCH_BYTES (qlin_gemm_workspace_bytes tells)
+ * returns QLIN_ERR_WORKSPACE.  Allocates nothing.  Every call on a GPU shares
+ * that GPU's array and it keeps the last call's contents (nothing in it needs
+ * clearing: each partial is written before it is read), so calls that
+ * overlap on one GPU (concurrent streams) race and must be serialized by the
+ * caller.
+ */
+#define QLIN_STATIC_SCRATCH_BYTES (16LL << 20)
+qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                                const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
+                                qlin_dtype y_dtype, void* stream);
+
+/*
  * qlin_gemm_w4a4_geglu -- the backbone MLP's gate and up projections with the
  * gated GeLU fused into the epilogue (FoldQuantVLA abstract: the projections
  * run natively in integer arithmetic; the gated GeLU joins them here so that

@@ -178,6 +178,22 @@ def test_gemm_ws_empty_and_no_workspace_ok(lib):
     assert gemm_ws(lib, m=0, wsb=16) == q.QLIN_OK            # no split needed for an empty call
 
 
+# ---- qlin_gemm_static_ws(scheme, xq, sx, wq, sw, m, n, k, y, ydt, stream)
+
+def test_gemm_static_ws_rejects(lib):
+    def call(scheme=q.QLIN_W8A8, m=DOWN["m"], n=DOWN["n"], k=DOWN["k"], xq=P, y=0x70000000):
+        return lib.qlin_gemm_static_ws(scheme, xq, P3, P2, P4, m, n, k, y, 1, None)
+    assert call(scheme=5) == q.QLIN_ERR_UNSUPPORTED
+    assert call(k=100) == q.QLIN_ERR_SHAPE
+    assert call(xq=None) == q.QLIN_ERR_NULL
+    assert call(y=P + 64) == q.QLIN_ERR_ALIAS
+    # 1024 x 4096 x 8192 W4A4: four splits of 128 x 256 tiles need 64 MiB > the 16 MiB scratch
+    if not torch.cuda.is_available():
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 1024, 4096, 8192) == 4 * 1024 * 4096 * 4
+    assert call(scheme=q.QLIN_W4A4, m=1024, n=4096, k=8192, y=0x78000000) == q.QLIN_ERR_WORKSPACE
+    assert call(m=0) == q.QLIN_OK
+
+
 # ---- qlin_gemm_w4a4_geglu(xq, sx, wq, sw, m, n2, k, h, hdt, stream)
 
 @pytest.mark.parametrize("kw,status", [
