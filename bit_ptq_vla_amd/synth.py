@@ -41,6 +41,26 @@ def normal_tensor(seed: int, name: str, shape, std: float = 1.0, dtype: str = "f
     return torch.from_numpy(a).to(_TORCH_DTYPES[dtype])
 
 
+def device_normal(seed: int, name: str, shape, device, std: float = 1.0, dtype: str = "f16",
+                  outliers: int = 0, outlier_scale: float = 1.0) -> torch.Tensor:
+    """Device tensor of the given storage dtype drawn on the device by torch's
+    Philox generator, seeded with (seed << 32) ^ crc32(name): float32 normals
+    times std, `outliers` input channels (last axis, chosen without
+    replacement from the same generator) times outlier_scale, rounded to the
+    storage dtype with round-half-to-even.  For the multi-gigabyte inputs of
+    the 18-layer sweep, which a host generator would take minutes to draw;
+    the oracle gets the same bytes by copying them back."""
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) << 32) ^ zlib.crc32(name.encode()))
+    a = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        a *= std
+    if outliers:
+        cols = torch.randperm(shape[-1], generator=g, device=device)[:outliers]
+        a[..., cols] *= outlier_scale
+    return a.to(_TORCH_DTYPES[dtype])
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a CPU tensor to a float64 NumPy array."""
     return t.detach().cpu().to(torch.float64).numpy()

@@ -55,6 +55,8 @@ class MlpBlock:
         self.hq = torch.empty((self.m, f), dtype=torch.int8, device=dev)
         self.hs = torch.empty(self.m, dtype=torch.float32, device=dev)
         self.y2 = torch.empty((self.m, self.dn.n), dtype=torch.bfloat16, device=dev)
+        # split-K scratch of the down GEMM (its 112 output tiles under-fill the chip)
+        self.ws_dn = q.gemm_workspace(q.QLIN_W8A8, self.m, self.dn.n, self.dn.k, dev)
         self.ops = 2 * self.m * (self.gu.n * self.gu.k + self.dn.n * self.dn.k)
         self.gemm1_ops = 2 * self.m * self.gu.n * self.gu.k
         # algorithmic HBM bytes of the gate|up GEMM: packed int4 X and W once,
@@ -78,88 +80,156 @@ class MlpBlock:
         else:
             q.qlin_rotate_quant_act(self.y1, k=self.dn.k, fold_inv_s=self.inv2, had_block=128, bits=8,
                                     pre=q.QLIN_PRE_GEGLU, out=(self.hq, self.hs))
-        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq2, self.ws2, self.dn.k, out=self.y2)
+        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq2, self.ws2, self.dn.k, out=self.y2, workspace=self.ws_dn)
 
 
-class SweepLayer:
-    """One layer of the mixed-precision backbone sweep (hidden 2048, MLP 16384)
-    at M tokens: q, k, v W4A4 from one int4 quantization of the attention input
-    (their weights stacked along n, one 6144-column GEMM; q, k and v are column
-    slices of its output), o W8A8 from the attention output, the fused gate|up
-    GeGLU GEMM (W4A4) from the MLP input, then h -> int8 -> down W8A8; Hadamard
-    block 128, bf16 out.
-    Inputs are synthetic (one tensor each for the attention input, the
-    attention output and the MLP input); weights are quantized once."""
+class SweepModel:
+    """The 18-layer mixed-precision backbone sweep (hidden 2048, MLP 16384,
+    Hadamard block 128, bf16 out) with distinct weights per layer.
 
-    def __init__(self, dev, m: int):
+    Per layer: q, k, v W4A4 from one int4 quantization of the attention input
+    (their weights stacked along n with one fold calibrated on the stacked
+    weights: one 6144-column GEMM whose column slices are q, k and v); o W8A8
+    from the attention output; the fused gate|up GeGLU GEMM (W4A4, gate and up
+    rows interleaved in blocks of 32) from the MLP input; then h -> fold,
+    Hadamard, int8 -> down W8A8.  8 launches per layer.
+
+    Inputs are synthetic, drawn on the device (synth.device_normal): one
+    tensor each for the attention input, the attention output and the MLP
+    input, N(0, 1) with 1% outlier channels x 30, shared by the layers (a
+    layer's work does not depend on the values).  Weights N(0, 0.02) fp16 per
+    layer and projection, quantized once (offline).  Buffers are sized for
+    m_max tokens; step(m) runs the first m tokens (row prefixes), so the
+    smaller batches of the sweep reuse the same weights and folds.
+    """
+
+    HID, FFN = 2048, 16384
+
+    def __init__(self, dev, m_max: int, layers: int = 18):
         import torch
 
         import bit_ptq_vla_amd as q
         from bit_ptq_vla_amd import synth
 
         self.q = q
-        self.m = m
+        self.dev = dev
+        self.m_max = m_max
+        self.layers = layers
         wl = synth.CFG5
-        p = {pr.name: pr for pr in wl.projs}
-        self.p = p
-        f = p["down"].k
+        self.wl = wl
+        hid, ffn = self.HID, self.FFN
+        nout = wl.n_outliers(hid)
+
+        def act(tag):
+            return synth.device_normal(wl.seed, f"{wl.name}/sweep/{tag}/m{m_max}", (m_max, hid), dev,
+                                       dtype=wl.x_dtype, outliers=nout, outlier_scale=wl.x_outlier_scale)
+
+        self.x_attn, self.x_o, self.x_mlp = act("attn_in"), act("attn_out"), act("mlp_in")
         bf = torch.bfloat16
+        self.xq4 = torch.empty((m_max, hid // 2), dtype=torch.uint8, device=dev)
+        self.xs4 = torch.empty(m_max, dtype=torch.float32, device=dev)
+        self.xq8 = torch.empty((m_max, hid), dtype=torch.int8, device=dev)
+        self.xs8 = torch.empty(m_max, dtype=torch.float32, device=dev)
+        self.h = torch.empty((m_max, ffn), dtype=bf, device=dev)
+        self.hq = torch.empty((m_max, ffn), dtype=torch.int8, device=dev)
+        self.hs = torch.empty(m_max, dtype=torch.float32, device=dev)
+        self.y_qkv = torch.empty((m_max, 3 * hid), dtype=bf, device=dev)
+        self.y_o = torch.empty((m_max, hid), dtype=bf, device=dev)
+        self.y_dn = torch.empty((m_max, hid), dtype=bf, device=dev)
+        self.layer = [self._build_layer(li) for li in range(layers)]
+        torch.cuda.synchronize(dev)
+        # int8 ops per token of one layer: q, k, v, o, gate|up, down
+        self.ops_per_token_layer = 2 * (3 * hid * hid + hid * hid + 2 * ffn * hid + hid * ffn)
+        self._ws = {}
 
-        def act(name, tag):
-            return synth.activation(wl, p[name], m, tag=tag).to(dev)
+    def weight(self, li: int, name: str, n: int, k: int):
+        """Float weights [n][k] of layer li's projection (fp16, on the device)."""
+        from bit_ptq_vla_amd import synth
 
-        def quant_w(name, x, bits, interleave=False):
-            w = synth.weight(wl, p[name], tag="/L0").to(dev)
-            if interleave:
-                w = q.interleave_gate_up(w[:f], w[f:])
-            s, inv = q.qlin_calibrate_fold(x, w)
-            wq, ws = q.qlin_quantize_weights(w, fold_s=s, had_block=128, bits=bits)
-            return s, inv, wq, ws
+        wl = self.wl
+        return synth.device_normal(wl.seed, f"{wl.name}/L{li}/{name}/w", (n, k), self.dev, std=wl.w_std,
+                                   dtype=wl.w_dtype)
 
-        self.x_attn = act("q", "/sweep_attn")
-        self.x_o = act("o", "/sweep_o")
-        self.x_mlp = act("gate_up", "/sweep_mlp")
-        # q, k, v share the attention input and its fold (calibrated on q's weights)
-        s_qkv, self.inv_qkv, self.wq_q, self.ws_q = quant_w("q", self.x_attn, 4)
-        wk = synth.weight(wl, p["k"], tag="/L0").to(dev)
-        wv = synth.weight(wl, p["v"], tag="/L0").to(dev)
-        wq_k, ws_k = q.qlin_quantize_weights(wk, fold_s=s_qkv, had_block=128, bits=4)
-        wq_v, ws_v = q.qlin_quantize_weights(wv, fold_s=s_qkv, had_block=128, bits=4)
-        del wk, wv
-        # per-row quantization: the stacked codes are the separate ones
-        self.wq_qkv = torch.cat([self.wq_q, wq_k, wq_v])
-        self.ws_qkv = torch.cat([self.ws_q, ws_k, ws_v])
-        del self.wq_q, self.ws_q, wq_k, wq_v
-        _, self.inv_o, self.wq_o, self.ws_o = quant_w("o", self.x_o, 8)
-        _, self.inv_gu, self.wq_gu, self.ws_gu = quant_w("gate_up", self.x_mlp, 4, interleave=True)
-        self.xq4 = torch.empty((m, 1024), dtype=torch.uint8, device=dev)
-        self.xs4 = torch.empty(m, dtype=torch.float32, device=dev)
-        self.xq8 = torch.empty((m, 2048), dtype=torch.int8, device=dev)
-        self.xs8 = torch.empty(m, dtype=torch.float32, device=dev)
-        self.h = torch.empty((m, f), dtype=bf, device=dev)
-        self.hq = torch.empty((m, f), dtype=torch.int8, device=dev)
-        self.hs = torch.empty(m, dtype=torch.float32, device=dev)
-        self.y = {n: torch.empty((m, p[n].n), dtype=bf, device=dev) for n in ("o", "down")}
-        self.y["qkv"] = torch.empty((m, p["q"].n + p["k"].n + p["v"].n), dtype=bf, device=dev)
-        q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))
-        q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, self.wq_gu, self.ws_gu, 2048, out=self.h)
-        wdn = synth.weight(wl, p["down"], tag="/L0").to(dev)
-        s2, self.inv_dn = q.qlin_calibrate_fold(self.h, wdn)
-        self.wq_dn, self.ws_dn = q.qlin_quantize_weights(wdn, fold_s=s2, had_block=128, bits=8)
-        del wdn
-        self.ops = 2 * m * sum(p[n].n * p[n].k for n in ("q", "k", "v", "o", "gate_up", "down"))
+    def _build_layer(self, li: int) -> dict:
+        import torch
 
-    def step(self):
         q = self.q
-        q.qlin_rotate_quant_act(self.x_attn, fold_inv_s=self.inv_qkv, had_block=128, bits=4,
-                                out=(self.xq4, self.xs4))
-        q.qlin_gemm_w4a4(self.xq4, self.xs4, self.wq_qkv, self.ws_qkv, 2048, out=self.y["qkv"])
-        q.qlin_rotate_quant_act(self.x_o, fold_inv_s=self.inv_o, had_block=128, bits=8, out=(self.xq8, self.xs8))
-        q.qlin_gemm_w8a8(self.xq8, self.xs8, self.wq_o, self.ws_o, 2048, out=self.y["o"])
-        q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=self.inv_gu, had_block=128, bits=4, out=(self.xq4, self.xs4))
-        q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, self.wq_gu, self.ws_gu, 2048, out=self.h)
-        q.qlin_rotate_quant_act(self.h, fold_inv_s=self.inv_dn, had_block=128, bits=8, out=(self.hq, self.hs))
-        q.qlin_gemm_w8a8(self.hq, self.hs, self.wq_dn, self.ws_dn, 16384, out=self.y["down"])
+        hid, ffn = self.HID, self.FFN
+        L = {}
+        w_qkv = torch.cat([self.weight(li, nm, hid, hid) for nm in ("q", "k", "v")])
+        s, L["inv_qkv"] = q.qlin_calibrate_fold(self.x_attn, w_qkv)
+        L["wq_qkv"], L["ws_qkv"] = q.qlin_quantize_weights(w_qkv, fold_s=s, had_block=128, bits=4)
+        del w_qkv
+        w_o = self.weight(li, "o", hid, hid)
+        s, L["inv_o"] = q.qlin_calibrate_fold(self.x_o, w_o)
+        L["wq_o"], L["ws_o"] = q.qlin_quantize_weights(w_o, fold_s=s, had_block=128, bits=8)
+        del w_o
+        w_gu = self.weight(li, "gate_up", 2 * ffn, hid)          # gate rows, then up rows
+        w_gu = q.interleave_gate_up(w_gu[:ffn], w_gu[ffn:])
+        s, L["inv_gu"] = q.qlin_calibrate_fold(self.x_mlp, w_gu)
+        L["wq_gu"], L["ws_gu"] = q.qlin_quantize_weights(w_gu, fold_s=s, had_block=128, bits=4)
+        del w_gu
+        # the down fold is calibrated on this layer's own h
+        q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=L["inv_gu"], had_block=128, bits=4, out=(self.xq4, self.xs4))
+        q.qlin_gemm_w4a4_geglu(self.xq4, self.xs4, L["wq_gu"], L["ws_gu"], hid, out=self.h)
+        w_dn = self.weight(li, "down", hid, ffn)
+        s, L["inv_dn"] = q.qlin_calibrate_fold(self.h, w_dn)
+        L["wq_dn"], L["ws_dn"] = q.qlin_quantize_weights(w_dn, fold_s=s, had_block=128, bits=8)
+        del w_dn
+        return L
+
+    def workspace(self, m: int):
+        """Split-K scratch of the down and o GEMMs at m tokens (None: no split)."""
+        if m not in self._ws:
+            q = self.q
+            a = q.gemm_workspace(q.QLIN_W8A8, m, self.HID, self.FFN, self.dev)
+            b = q.gemm_workspace(q.QLIN_W8A8, m, self.HID, self.HID, self.dev)
+            self._ws[m] = (a, b)
+        return self._ws[m]
+
+    def ops(self, m: int) -> int:
+        return self.layers * m * self.ops_per_token_layer
+
+    def run_layer(self, L: dict, m: int, ev=None, evs=None):
+        """One layer at m tokens.  ev: (start, end) events around the gate|up
+        GEMM; evs: a list of 9 events bracketing the 8 launches."""
+        q = self.q
+        hid, ffn = self.HID, self.FFN
+        ws_dn, ws_o = self.workspace(m)
+
+        def mark(i):
+            if evs is not None:
+                evs[i].record()
+
+        xq4, xs4, xq8, xs8 = self.xq4[:m], self.xs4[:m], self.xq8[:m], self.xs8[:m]
+        mark(0)
+        q.qlin_rotate_quant_act(self.x_attn[:m], fold_inv_s=L["inv_qkv"], had_block=128, bits=4, out=(xq4, xs4))
+        mark(1)
+        q.qlin_gemm_w4a4(xq4, xs4, L["wq_qkv"], L["ws_qkv"], hid, out=self.y_qkv[:m])
+        mark(2)
+        q.qlin_rotate_quant_act(self.x_o[:m], fold_inv_s=L["inv_o"], had_block=128, bits=8, out=(xq8, xs8))
+        mark(3)
+        q.qlin_gemm_w8a8(xq8, xs8, L["wq_o"], L["ws_o"], hid, out=self.y_o[:m], workspace=ws_o)
+        mark(4)
+        q.qlin_rotate_quant_act(self.x_mlp[:m], fold_inv_s=L["inv_gu"], had_block=128, bits=4, out=(xq4, xs4))
+        mark(5)
+        if ev is not None:
+            ev[0].record()
+        q.qlin_gemm_w4a4_geglu(xq4, xs4, L["wq_gu"], L["ws_gu"], hid, out=self.h[:m])
+        if ev is not None:
+            ev[1].record()
+        mark(6)
+        q.qlin_rotate_quant_act(self.h[:m], fold_inv_s=L["inv_dn"], had_block=128, bits=8,
+                                out=(self.hq[:m], self.hs[:m]))
+        mark(7)
+        q.qlin_gemm_w8a8(self.hq[:m], self.hs[:m], L["wq_dn"], L["ws_dn"], ffn, out=self.y_dn[:m], workspace=ws_dn)
+        mark(8)
+
+    def step(self, m: int, evs=None):
+        """All layers at m tokens; evs: per-layer (start, end) event pairs
+        around the gate|up GEMM launches."""
+        for li, L in enumerate(self.layer):
+            self.run_layer(L, m, ev=None if evs is None else evs[li])
 
 
 class ActionExpert:
@@ -268,6 +338,39 @@ class ActionExpert:
             for i in self.rest:
                 pr, xs_i, wq_i, ws_i, y_i = self.w4a16[i]
                 q.qlin_gemv_w4a16(xs_i[t], wq_i, ws_i, out=y_i)
+
+    def build_cold_copies(self, min_bytes: int):
+        """Distinct copies of the W4A4 and W4A16 weights, one per step of each
+        group of `steps` steps, until the copies total at least min_bytes (so
+        that a step's weights come from HBM, not from L2 / Infinity Cache).
+        Returns the list of groups; group c holds `steps` weight sets."""
+        per_set = sum(wq.numel() + ws.numel() * 4 for _, _, _, wq, ws, _, _, _ in self.w4a4)
+        per_set += sum(wq16.numel() + ws16.numel() * 2 for _, _, wq16, ws16, _ in self.w4a16)
+        groups = max(1, -(-min_bytes // (per_set * self.steps)))
+        self.cold = []
+        for _ in range(groups):
+            sets = []
+            for _t in range(self.steps):
+                sets.append(([(wq.clone(), ws.clone()) for _, _, _, wq, ws, _, _, _ in self.w4a4],
+                             [(wq16.clone(), ws16.clone()) for _, _, wq16, ws16, _ in self.w4a16]))
+            self.cold.append(sets)
+        return self.cold
+
+    def run_w4a4_cold(self, c: int):
+        """The W4A4 steps with group c of the cold weight copies (step t: set t)."""
+        q = self.q
+        for t in range(self.steps):
+            w4, _ = self.cold[c][t]
+            for (pr, xs, inv, _, _, xq, xsc, y), (wq, ws) in zip(self.w4a4, w4):
+                q.qlin_rotate_quant_act(xs[t], fold_inv_s=inv, had_block=64, bits=4, out=(xq, xsc))
+                q.qlin_gemm_w4a4(xq, xsc, wq, ws, pr.k, out=y)
+
+    def run_w4a16_cold(self, c: int):
+        q = self.q
+        for t in range(self.steps):
+            _, w16 = self.cold[c][t]
+            for (pr, xs, _, _, y), (wq16, ws16) in zip(self.w4a16, w16):
+                q.qlin_gemv_w4a16(xs[t], wq16, ws16, out=y)
 
     def run_w4a4_static(self):
         q = self.q
