@@ -46,6 +46,16 @@ namespace {
 
 constexpr int STAGE_BYTES = 64;   // bytes of one row per pipeline stage
 
+// f(std::integral_constant<int, Q>) for Q = B .. E-1 in order: loop bodies whose
+// indices must be compile-time constants (register arrays, instruction order).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 struct GemmParams {
     const int8_t* a;      // [m][kbytes]
     const int8_t* b;      // [n][kbytes]
@@ -59,6 +69,7 @@ struct GemmParams {
     int stages;           // ceil(kbytes / 64)
     int stages_per_split;
     int tiles_m, tiles_n, splits;
+    int group_m;          // tile order: 0 = rows fastest over the whole grid, else groups of group_m tile rows
     int y_dtype;
 };
 
@@ -472,8 +483,24 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     const int tiles_mn = p.tiles_m * p.tiles_n;
     const int split = bid / tiles_mn;
     const int t_mn = bid - split * tiles_mn;
-    const int tile_n = t_mn / p.tiles_m;
-    const int tile_m = t_mn - tile_n * p.tiles_m;
+    int tile_m, tile_n;
+    if (p.group_m > 0) {
+        // Groups of group_m tile rows, rows fastest inside a group: the tiles an
+        // XCD runs at once form a group_m x (CUs / group_m) patch, so each A
+        // panel is shared by the patch's columns and each B panel by its rows
+        // while they stream through that XCD's L2 (long k: the panels do not
+        // fit, only their current k-slabs do).
+        const int per_group = p.group_m * p.tiles_n;
+        const int g = t_mn / per_group;
+        const int first = g * p.group_m;
+        const int rows = (p.tiles_m - first) < p.group_m ? (p.tiles_m - first) : p.group_m;
+        const int r = t_mn - g * per_group;
+        tile_n = r / rows;
+        tile_m = first + (r - tile_n * rows);
+    } else {
+        tile_n = t_mn / p.tiles_m;
+        tile_m = t_mn - tile_n * p.tiles_m;
+    }
     const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
     const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
     const int s_begin = split * p.stages_per_split;
@@ -712,6 +739,324 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     }
 }
 
+// ---- 256 x 256 tiles, one block per CU ------------------------------------
+//
+// For grids with at least one 256 x 256 tile per CU.  Four waves, one per
+// SIMD, each owning a 128 x 128 accumulator tile (4 x 4 MFMA tiles, 256
+// accumulator registers): half the LDS bytes per MFMA of a 64 x 128 wave tile.
+// With one wave per SIMD nothing else hides a stall of that wave, so each
+// stage's instruction order is fixed by hand (sched_barrier between groups):
+//   - a few MFMAs of the stage first, issued before the stage's
+//     synchronisation (own DMA of the next stage landed, s_barrier), so the
+//     matrix pipe stays busy while the four waves meet;
+//   - then the remaining MFMAs, one at a time, each followed by one of the
+//     stage's memory instructions: the DMA of stage it + NS into the buffer
+//     this stage's fragments came from (free after the barrier), and the
+//     LDS reads of the next stage's fragments (published by the barrier);
+//   - int4 operands: the nibble unpack of the next k-slice runs under the
+//     current k-slice's MFMAs (3 VALU per MFMA).
+// Stages hold 64 bytes of a B row (int8: 2 k-slices of 32; int4: 4 k-slices;
+// W4A8: 4 k-slices, 128 bytes of an A row).  The ring, the swizzle, the
+// operand order, the epilogue and the tile order are those of gemm_i8_kernel.
+template <bool INT4, int OUT, bool A8>
+__global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmParams p) {
+    static_assert(!A8 || INT4, "W4A8 takes int4 weights");
+    constexpr int BM = 256, BN = 256, TM = 4, TN = 4;
+    constexpr int NS = A8 ? 3 : 4;
+    constexpr int SA = A8 ? 2 * STAGE_BYTES : STAGE_BYTES;
+    constexpr int A_INSTR = BM * SA / 4096;      // 16-byte DMA loads per lane per stage (A)
+    constexpr int B_INSTR = BN / 64;
+    constexpr int LOADS = A_INSTR + B_INSTR;
+    constexpr int STAGE = BM * SA + BN * STAGE_BYTES;
+    constexpr int ASH = A8 ? 4 : (INT4 ? 8 : 0);
+    constexpr bool GEGLU = OUT >= OUT_GEGLU;
+    constexpr int RING0 = GEGLU ? GTAB_BYTES : 0;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING0 + NS * STAGE];
+    int8_t* const ring = lds + RING0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int nblocks = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    int tile_m, tile_n;
+    {
+        const int t_mn = bid;   // no split-K on this path
+        if (p.group_m > 0) {
+            const int per_group = p.group_m * p.tiles_n;
+            const int g = t_mn / per_group;
+            const int first = g * p.group_m;
+            const int rows = (p.tiles_m - first) < p.group_m ? (p.tiles_m - first) : p.group_m;
+            const int r = t_mn - g * per_group;
+            tile_n = r / rows;
+            tile_m = first + (r - tile_n * rows);
+        } else {
+            tile_n = t_mn / p.tiles_m;
+            tile_m = t_mn - tile_n * p.tiles_m;
+        }
+    }
+    const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
+    const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
+    const int nst = p.stages;
+    // The loop runs a multiple of NS stages with the same instructions in every
+    // stage (no branch between MFMAs, so the accumulators stay in place): the
+    // DMA of a stage past the end takes an offset past the buffer's range, and
+    // the hardware fills zeros (no memory access), which add nothing.
+    constexpr int STEP = (NS % 2 == 0 || INT4) ? NS : 2 * NS;   // int8 also alternates register sets
+    const int nstp = (nst + STEP - 1) / STEP * STEP;
+    constexpr int OOB = 0x7FFFFFF0;
+
+    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes_a, (p.m - m0) * p.kbytes_a);
+    const v4i rsrc_b = make_rsrc(p.b + n0 * p.kbytes, (p.n - n0) * p.kbytes);
+
+    // DMA mapping (as gemm_i8_kernel): load i of wave w fills 16 rows
+    const int dma_row0 = wave * 16 + (lane >> 2);
+    const int dma_chunk = (lane & 3) ^ swz(dma_row0);
+    const int dma_voff = dma_row0 * static_cast<int>(p.kbytes) + dma_chunk * 16;
+    const int row64 = 64 * static_cast<int>(p.kbytes);
+    const int dma_row0_a = A8 ? wave * 8 + (lane >> 3) : dma_row0;
+    const int dma_chunk_a = A8 ? (lane & 7) ^ swz8(dma_row0_a) : dma_chunk;
+    const int dma_voff_a = dma_row0_a * static_cast<int>(p.kbytes_a) + dma_chunk_a * 16;
+    const int rowstep_a = (A8 ? 32 : 64) * static_cast<int>(p.kbytes_a);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // DMA load q (0 .. LOADS-1) of stage st into buffer buf (zeros past the last stage)
+    auto dma_one = [&](int st, int8_t* buf, int q) __attribute__((always_inline)) {
+        const uint32_t a_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + wave_u * 1024;
+        const bool live = st < nst;
+        if (q < A_INSTR)
+            dma16(rsrc_a, live ? dma_voff_a + st * SA + q * rowstep_a : OOB, a_dst + q * 4096);
+        else
+            dma16(rsrc_b, live ? dma_voff + st * STAGE_BYTES + (q - A_INSTR) * row64 : OOB,
+                  a_dst + BM * SA + (q - A_INSTR) * 4096);
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int l32 = lane & 31;
+    const int hsel = lane >> 5;
+    const int sw = swz(l32);
+    const int a_row = (wm * (BM / 2) + l32) * SA;
+    const int b_row = BM * SA + (wn * (BN / 2) + l32) * STAGE_BYTES;
+    const int sw8 = swz8(l32);
+    // the 16-byte operand read of row tile i (A) / column tile j (B) for chunk pair c (0 or 1)
+    auto rd_a = [&](const int8_t* st, int c, int i) __attribute__((always_inline)) -> uint4 {
+        return *reinterpret_cast<const uint4*>(st + a_row + ((2 * c + hsel) ^ sw) * 16 + i * 32 * SA);
+    };
+    auto rd_b = [&](const int8_t* st, int c, int j) __attribute__((always_inline)) -> uint4 {
+        return *reinterpret_cast<const uint4*>(st + b_row + ((2 * c + hsel) ^ sw) * 16 + j * 32 * STAGE_BYTES);
+    };
+    // W4A8: the int8 A values of B chunk (2c + hsel) are A chunks 2 (2c + hsel) + h
+    auto rd_a8 = [&](const int8_t* st, int c, int h, int i) __attribute__((always_inline)) -> uint4 {
+        return *reinterpret_cast<const uint4*>(st + a_row + ((2 * (2 * c + hsel) + h) ^ sw8) * 16 + i * 32 * SA);
+    };
+    // MFMA q (0 .. 15) of a k-slice: row tile q / 4, column tile q % 4 (q a compile-time constant)
+    auto mfma_one = [&](const v4i (&oa)[TM], const v4i (&ob)[TN], auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[q >> 2], ob[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+    };
+    // published: stage it + 1 landed for every wave (every stage issues the
+    // same LOADS DMAs, so NS - 2 later stages are in flight), buffer of stage it free
+    auto sync_next = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<(NS - 2) * LOADS>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    if constexpr (GEGLU) {
+        static_assert(GTAB_BYTES == 2 * 4 * 1024, "two 16-byte loads per lane");
+        const v4i rsrc_t = make_rsrc(reinterpret_cast<const int8_t*>(g_gelu_neg_tab), GTAB_BYTES);
+        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave_u * 1024;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(rsrc_t, (i * 4 + wave) * 1024 + lane * 16, t_dst + i * 4096);
+    }
+    {
+#pragma unroll
+        for (int pst = 0; pst < NS; ++pst)
+#pragma unroll
+            for (int q = 0; q < LOADS; ++q) dma_one(pst, ring + pst * STAGE, q);
+        wait_vmcnt<(NS - 1) * LOADS>();   // stage 0 (and the GeLU table, issued first) landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+
+    if constexpr (!INT4) {
+        // ---- int8 x int8: 2 k-slices per stage; fragments double-buffered
+        struct Frag {
+            uint4 a[2][TM];
+            uint4 b[2][TN];
+        };
+        Frag f[2];
+        auto read_frag = [&](const int8_t* st, Frag& fr) __attribute__((always_inline)) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fr.a[c][i] = rd_a(st, c, i);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fr.b[c][j] = rd_b(st, c, j);
+            }
+        };
+        read_frag(ring, f[0]);
+        auto stage = [&](auto par, int it, int8_t* buf, int8_t* nbuf) __attribute__((always_inline)) {
+            constexpr int P = decltype(par)::value;
+            Frag& cur = f[P];
+            Frag& nxt = f[P ^ 1];
+            v4i a0[TM], b0[TN], a1[TM], b1[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) { a0[i] = __builtin_bit_cast(v4i, cur.a[0][i]); a1[i] = __builtin_bit_cast(v4i, cur.a[1][i]); }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) { b0[j] = __builtin_bit_cast(v4i, cur.b[0][j]); b1[j] = __builtin_bit_cast(v4i, cur.b[1][j]); }
+            // 4 MFMAs cover the synchronisation
+            static_for<0, 4>([&](auto qc) __attribute__((always_inline)) { mfma_one(a0, b0, qc); });
+            __builtin_amdgcn_sched_barrier(0);
+            sync_next();
+            // 28 MFMAs, each followed by one memory instruction: 8 DMA, 16 LDS reads
+            static_for<4, 32>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr (q < 16) mfma_one(a0, b0, qc);
+                else mfma_one(a1, b1, std::integral_constant<int, q - 16>{});
+                constexpr int mi = q - 4;
+                if constexpr (mi < LOADS) {
+                    dma_one(it + NS, buf, mi);
+                } else if constexpr (mi < LOADS + 16) {
+                    constexpr int r = mi - LOADS, c = r >> 3, t = r & 7;
+                    if constexpr (t < TM) nxt.a[c][t] = rd_a(nbuf, c, t);
+                    else nxt.b[c][t - TM] = rd_b(nbuf, c, t - TM);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int it = 0; it < nstp; it += 4) {
+            stage(std::integral_constant<int, 0>{}, it, ring, ring + STAGE);
+            stage(std::integral_constant<int, 1>{}, it + 1, ring + STAGE, ring + 2 * STAGE);
+            stage(std::integral_constant<int, 0>{}, it + 2, ring + 2 * STAGE, ring + 3 * STAGE);
+            stage(std::integral_constant<int, 1>{}, it + 3, ring + 3 * STAGE, ring);
+        }
+    } else {
+        // ---- int4 weights (W4A4, W4A8): 4 k-slices per stage in two units of
+        // one 16-byte read per fragment (A8: two A reads per row tile)
+        constexpr int FRA = A8 ? 2 : 1;
+        struct Unit {
+            uint4 a[FRA][TM];
+            uint4 b[TN];
+        };
+        auto read_unit = [&](const int8_t* st, int c, Unit& u) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if constexpr (A8) {
+                    u.a[0][i] = rd_a8(st, c, 0, i);
+                    u.a[1][i] = rd_a8(st, c, 1, i);
+                } else {
+                    u.a[0][i] = rd_a(st, c, i);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) u.b[j] = rd_b(st, c, j);
+        };
+        // number of 16-byte reads of a unit, and the r-th of them (r a compile-time constant)
+        constexpr int UREADS = FRA * TM + TN;
+        auto read_one = [&](const int8_t* st, int c, Unit& u, auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (r < FRA * TM) {
+                if constexpr (A8) u.a[r / TM][r % TM] = rd_a8(st, c, r / TM, r % TM);
+                else u.a[0][r] = rd_a(st, c, r);
+            } else {
+                u.b[r - FRA * TM] = rd_b(st, c, r - FRA * TM);
+            }
+        };
+        // k-slice h (0: dwords x,y; 1: z,w) of a unit as MFMA operands
+        auto unpack_a = [&](const Unit& u, int h, int i) __attribute__((always_inline)) -> v4i {
+            if constexpr (A8) return order_int8_as_int4(u.a[h][i]);
+            else return h == 0 ? unpack_int4(u.a[0][i].x, u.a[0][i].y) : unpack_int4(u.a[0][i].z, u.a[0][i].w);
+        };
+        auto unpack_b = [&](const Unit& u, int h, int j) __attribute__((always_inline)) -> v4i {
+            return h == 0 ? unpack_int4(u.b[j].x, u.b[j].y) : unpack_int4(u.b[j].z, u.b[j].w);
+        };
+        Unit u0, u1;
+        v4i oa[TM], ob[TN], pa[TM], pb[TN];
+        read_unit(ring, 0, u0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) oa[i] = unpack_a(u0, 0, i);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) ob[j] = unpack_b(u0, 0, j);
+        // one MFMA, then operand f (0..7: row tiles then column tiles) of the
+        // next k-slice unpacked into (na, nb)
+        auto mfma_unpack = [&](const v4i (&ca)[TM], const v4i (&cb)[TN], auto qc, const Unit& src, int h,
+                               v4i (&na)[TM], v4i (&nb)[TN]) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mfma_one(ca, cb, qc);
+            if constexpr (q < TM) na[q] = unpack_a(src, h, q);
+            else if constexpr (q < TM + TN) nb[q - TM] = unpack_b(src, h, q - TM);
+        };
+        auto stage = [&](int it, int8_t* buf, int8_t* nbuf) __attribute__((always_inline)) {
+            // slice 0 (oa, ob): MFMAs with unit 1 read from this stage and slice 1 unpacked
+            static_for<0, 16>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                mfma_unpack(oa, ob, qc, u0, 1, pa, pb);
+                if constexpr (q < UREADS) read_one(buf, 1, u1, qc);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // slice 1 (pa, pb): 4 MFMAs, synchronisation, then MFMAs with the DMA of
+            // stage it + NS and slice 2 (unit 1, k-slice 0) unpacked
+            static_for<0, 4>([&](auto qc) __attribute__((always_inline)) { mfma_one(pa, pb, qc); });
+            __builtin_amdgcn_sched_barrier(0);
+            sync_next();
+            static_for<4, 16>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                mfma_one(pa, pb, qc);
+                constexpr int f = q - 4;   // 0 .. 11
+                if constexpr (f < TM) oa[f] = unpack_a(u1, 0, f);
+                else if constexpr (f < TM + TN) ob[f - TM] = unpack_b(u1, 0, f - TM);
+                if constexpr (f < LOADS) dma_one(it + NS, buf, f);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // slice 2 (oa, ob): MFMAs with the rest of the DMA, the next stage's unit 0
+            // read, and slice 3 (unit 1, k-slice 1) unpacked
+            static_for<0, 16>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                mfma_unpack(oa, ob, qc, u1, 1, pa, pb);
+                constexpr int f = q + 12;
+                if constexpr (f < LOADS) dma_one(it + NS, buf, f);
+                if constexpr (q >= 4 && q - 4 < UREADS) read_one(nbuf, 0, u0, std::integral_constant<int, q - 4>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // slice 3 (pa, pb): MFMAs with the next stage's slice 0 unpacked
+            static_for<0, 16>([&](auto qc) __attribute__((always_inline)) {
+                mfma_unpack(pa, pb, qc, u0, 0, oa, ob);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        for (int it = 0; it < nstp; it += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) stage(it + u, ring + u * STAGE, ring + ((u + 1) % NS) * STAGE);
+        }
+    }
+
+    // ---- epilogue: the zero-fill DMAs past the last stage have landed and every
+    // wave is done with the ring; each wave takes one buffer's worth
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (m0 + wm * (BM / 2) >= p.m) return;   // no output rows in this wave
+    constexpr int REGION = NS * STAGE / 4 / 16 * 16;
+    if constexpr (GEGLU) {
+        store_tile_geglu<BM, BN, ASH, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2),
+                                                                lane, reinterpret_cast<const float*>(lds),
+                                                                ring + wave * REGION);
+    } else {
+        store_tile_lds<BM, BN, ASH, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                                  ring + wave * REGION, p.y);
+    }
+}
+
 // Sum of split-K partials in split order (integer: bit-exact), then the
 // epilogue; four consecutive outputs per lane (n % 4 == 0), else one.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* ws, int splits, int64_t m,
@@ -793,6 +1138,24 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <bool INT4, int OUT, bool A8>
+hipError_t launch_256(const GemmParams& p, hipStream_t st) {
+    dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n));
+    hipLaunchKernelGGL((gemm256_kernel<INT4, OUT, A8>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <bool INT4, bool A8>
+hipError_t launch_256_out(const GemmParams& p, hipStream_t st) {
+    switch (p.y_dtype) {
+        case BF16: return launch_256<INT4, BF16, A8>(p, st);
+        case F16: return launch_256<INT4, F16, A8>(p, st);
+        case F32: return launch_256<INT4, F32, A8>(p, st);
+        case I32: return launch_256<INT4, I32, A8>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int BM, int BN, int MINB, int NS, bool INT4, bool A8 = false>
 hipError_t launch_out(const GemmParams& p, hipStream_t st) {
     if (p.splits > 1) return launch_tile<BM, BN, MINB, NS, INT4, -1, A8>(p, st);
@@ -863,12 +1226,28 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
     // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per
     // CU; so does W4A8, whose 128 x 256 stage would not leave room for 3 stages.)
     GemmPlan g;
+    const int64_t cus = device_cus();
+    const int64_t kbytes = int4 ? k / 2 : k;
+    const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
+    g.group_m = 0;
+    // int8 activations with enough 256 x 256 tiles for every CU: one block per
+    // CU, each wave a 128 x 128 accumulator tile (half the LDS bytes per MFMA of
+    // a 64 x 128 wave tile), tiles in 4-row groups.  (W4A4 stays on the two-
+    // blocks-per-CU tiles below: its int4 unpack and epilogue VALU work is
+    // covered there by the co-resident block's MFMAs; measured 45.6% against
+    // 40.7% of the int8 peak for the 52224 x 32768 x 2048 gate|up GEMM.)
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles256 >= cus && (!int4 || a8)) {
+        g.bm = g.bn = 256;
+        g.splits = 1;
+        g.deep = false;
+        g.group_m = 4;
+        g.ws_bytes = 0;
+        return g;
+    }
     g.bm = 128;
     g.bn = (n >= 4096 && int4 && !a8) ? 256 : 128;
     const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
-    const int64_t kbytes = int4 ? k / 2 : k;
-    const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
-    const int64_t cus = device_cus();
     const int64_t slots = 2 * cus;   // two resident blocks per CU
     int splits = 1;
     // split K only when the tile grid fills under half of the block slots,
@@ -887,6 +1266,8 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
         if (deep_splits >= 2 && tiles * deep_splits * 4 >= cus * 3 && tiles * splits > cus) splits = deep_splits;
     }
     g.splits = splits;
+    // Many rounds of tiles: groups of 8 tile rows (see gemm_i8_kernel's tile order)
+    if (tiles * splits >= 2 * slots) g.group_m = 8;
     // A grid of at most one block per CU gets the whole LDS for a deeper ring:
     // with one wave per SIMD nothing else covers the DMA latency.
     g.deep = tiles * splits <= cus;
@@ -909,9 +1290,15 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     p.stages_per_split = (p.stages + plan.splits - 1) / plan.splits;
     p.tiles_m = static_cast<int>((m + plan.bm - 1) / plan.bm);
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
+    p.group_m = plan.group_m;
     p.y_dtype = y_dtype;
     hipError_t e;
-    if (a8) {
+    if (plan.bm == 256) {
+        if (plan.splits != 1) return hipErrorInvalidValue;
+        if (a8) e = launch_256_out<true, true>(p, st);
+        else if (int4) e = launch_256_out<true, false>(p, st);
+        else e = launch_256_out<false, false>(p, st);
+    } else if (a8) {
         if (!int4 || plan.bn != 128) return hipErrorInvalidValue;
         e = plan.deep ? launch_out<128, 128, 1, 6, true, true>(p, st) : launch_out<128, 128, 2, 3, true, true>(p, st);
     } else if (plan.bn == 256) {
@@ -965,7 +1352,16 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
     p.stages_per_split = p.stages;
     p.tiles_m = static_cast<int>((m + plan.bm - 1) / plan.bm);
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
+    p.group_m = plan.group_m;
     p.y_dtype = y_dtype;
+    if (plan.bm == 256) {
+        switch (p.y_dtype) {
+            case BF16: return launch_256<true, OUT_GEGLU + BF16, false>(p, st);
+            case F16: return launch_256<true, OUT_GEGLU + F16, false>(p, st);
+            case F32: return launch_256<true, OUT_GEGLU + F32, false>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     if (plan.bn == 256)
         return plan.deep ? launch_geglu_out<128, 256, 1, 6, true>(p, st) : launch_geglu_out<128, 256, 2, 3, true>(p, st);
     return plan.deep ? launch_geglu_out<128, 128, 1, 8, true>(p, st) : launch_geglu_out<128, 128, 2, 4, true>(p, st);

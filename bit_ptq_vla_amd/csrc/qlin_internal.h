@@ -66,6 +66,7 @@ struct GemmPlan {
     int bm, bn;     // block tile
     int splits;     // split-K factor (1 = fused epilogue)
     bool deep;      // grid fits one block per CU: one block per CU with a deeper DMA ring
+    int group_m;    // tile order: 0 = rows fastest, else groups of group_m tile rows
     int64_t ws_bytes;
 };
 // a8 (with int4): int8 activations against int4 weights (W4A8).  Split-K

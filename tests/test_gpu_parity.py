@@ -437,6 +437,17 @@ BIG_GRID_SHAPES = [
     ("w4a4", 1100, 3968, 256),    # 9 x 31 tiles of 128 x 128
     ("w4a4", 2100, 4096, 256),    # 17 x 16 tiles of 128 x 256
     ("w4a8", 1100, 3968, 512),    # 9 x 31 tiles of 128 x 128
+    # at least one 256 x 256 tile per CU: int8 and W4A8 operands take the
+    # one-block-per-CU 256 x 256 launch with tiles in groups of 4 tile rows,
+    # W4A4 the 128 x 256 launch in groups of 8 (ragged last group, ragged M
+    # and N edges)
+    ("w8a8", 4100, 4000, 512),    # 17 x 16 tiles of 256 x 256
+    ("w4a4", 4100, 4000, 512),    # 33 x 16 tiles of 128 x 256
+    ("w4a8", 4100, 4096, 256),
+    ("w8a8", 6528, 2560, 1024),   # 26 x 10 tiles, the last tile row half empty
+    ("w8a8", 4100, 4096, 192),    # 3 k-stages: one zero-filled stage pads the 4-stage ring
+    ("w4a4", 4352, 4096, 384),    # 34 x 16 tiles of 128 x 256, 3 k-stages
+    ("w4a8", 4352, 4096, 512),    # 4 k-stages, padded to 6 (3-stage ring)
 ]
 
 
@@ -452,7 +463,7 @@ def test_gemm_big_grid_sampled_rows(scheme, m, n, k):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
 
-@pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256)])
+@pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256), (4100, 2048, 512), (2050, 8192, 256)])
 def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
     say(f"gemm geglu big grid {m}x{f}x{k}")
     n2 = 2 * f
