@@ -13,6 +13,9 @@ Blocchi"; LoopQ abstract for plain RTN weights and the W4A16 weight-only form):
   rotate          v @ blockdiag(H_b / sqrt(b))          (dense f64 matmul per block)
   quantize        per-row symmetric, round-half-even   (per-token dynamic / RTN)
   integer GEMM    int64 dot products of the codes
+  E2M3 storage    int4-grid codes (-7 .. 7) as FP6 E2M3 fields packed densely
+                  (OCP MX v1.0 element encoding): the same integers, a second
+                  storage form of the W4A4 operands
   epilogue        acc * s_x[m] * s_w[n]  -> f32 -> f16/bf16 (RNE)
   GeGLU epilogue  gate|up rows interleaved in blocks of 32; h = gelu(g) * u
                   from the bf16-rounded dequantized g, u (the fused form of the
@@ -42,6 +45,10 @@ from .qlin_ref import (  # noqa: F401
     quantize_groups_w4a16,
     pack_int4,
     unpack_int4,
+    e2m3_value,
+    e2m3_code_of_int,
+    pack_e2m3,
+    unpack_e2m3,
     gelu,
     geglu,
     rotate_quant_act,

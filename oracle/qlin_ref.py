@@ -211,6 +211,73 @@ def unpack_int4(p: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP6 E2M3 storage of int4-grid codes
+#   [FQ] abstract (W4A4 integer execution): the codes and their products are
+#   those of the int4 path; only their storage differs.  The encoding is the
+#   FP6 E2M3 element of the OCP Microscaling Formats (MX) v1.0 specification:
+#   1 sign bit, 2 exponent bits (bias 1), 3 mantissa bits, subnormals at
+#   exponent 0, no infinities or NaN.  Every integer -7 .. 7 is exact in it,
+#   so a dot product of two such code vectors accumulated in fp32 (|sum| <
+#   2^24 for k < 2^18) equals the integer dot product.
+# --------------------------------------------------------------------------
+
+
+def e2m3_value(code: int) -> float:
+    """Real value of a 6-bit E2M3 code (bit 5 sign, bits 4..3 exponent field,
+    bits 2..0 mantissa field): subnormal m/8 at exponent field 0, else
+    2^(e - 1) * (1 + m/8)."""
+    if not 0 <= code < 64:
+        raise ValueError("E2M3 codes are 6 bits")
+    s = -1.0 if code & 0x20 else 1.0
+    e = (code >> 3) & 3
+    m = code & 7
+    mag = m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 8.0)
+    return s * mag
+
+
+def e2m3_code_of_int(v: int) -> int:
+    """The E2M3 code whose value is the integer v (-7 .. 7), found by search
+    over the 32 non-negative codes (+0 for zero)."""
+    if not -7 <= v <= 7:
+        raise ValueError("only -7 .. 7 are codes of the int4 grid")
+    for c in range(32):
+        if e2m3_value(c) == abs(v):
+            return c | (0x20 if v < 0 else 0)
+    raise AssertionError("unreachable: every integer 0 .. 7 is an E2M3 value")
+
+
+def pack_e2m3(q: np.ndarray) -> np.ndarray:
+    """Int4-grid codes (-7 .. 7) along the last axis as E2M3 codes packed
+    densely, little-endian: code j occupies bits 6j .. 6j+5 of the row's bit
+    string, bit b of byte i being bit 8i + b.  Last axis a multiple of 4
+    (3 bytes per 4 codes)."""
+    q = np.asarray(q, dtype=np.int64)
+    if q.shape[-1] % 4:
+        raise ValueError("E2M3 packing needs a last dimension divisible by 4")
+    if np.any(q < -7) or np.any(q > 7):
+        raise ValueError("E2M3 storage holds the int4 grid -7 .. 7")
+    table = np.array([e2m3_code_of_int(v) for v in range(-7, 8)], dtype=np.int64)
+    codes = table[q + 7]
+    bits = ((codes[..., None] >> np.arange(6)) & 1).astype(np.uint8)
+    bits = bits.reshape(q.shape[:-1] + (q.shape[-1] * 6,))
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def unpack_e2m3(p: np.ndarray) -> np.ndarray:
+    """Inverse of pack_e2m3: the integer value of every 6-bit field, int64
+    (a field whose value is not an integer raises)."""
+    p = np.asarray(p, dtype=np.uint8)
+    bits = np.unpackbits(p, axis=-1, bitorder="little").astype(np.int64)
+    k = bits.shape[-1] // 6
+    fields = bits[..., :6 * k].reshape(p.shape[:-1] + (k, 6))
+    codes = np.sum(fields << np.arange(6), axis=-1)
+    values = np.array([e2m3_value(c) for c in range(64)])[codes]
+    if np.any(values != np.rint(values)):
+        raise ValueError("field is not an integer E2M3 value")
+    return np.rint(values).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
 # GeGLU glue between the gate/up and down projections of an MLP block
 # --------------------------------------------------------------------------
 
