@@ -33,7 +33,8 @@ QLIN_ERR_WORKSPACE = 10
 
 QLIN_F16, QLIN_BF16, QLIN_F32, QLIN_I32 = 0, 1, 2, 3
 QLIN_PRE_NONE, QLIN_PRE_GEGLU = 0, 1
-QLIN_W4A4, QLIN_W8A8, QLIN_W4A8 = 0, 1, 2
+QLIN_W4A4, QLIN_W8A8, QLIN_W4A8, QLIN_W4A4_E2M3 = 0, 1, 2, 3
+QLIN_BITS_E2M3 = 6
 _SCHEME = {"qlin_gemm_w4a4": QLIN_W4A4, "qlin_gemm_w8a8": QLIN_W8A8, "qlin_gemm_w4a8": QLIN_W4A8}
 
 _TORCH_TO_QLIN = {torch.float16: QLIN_F16, torch.bfloat16: QLIN_BF16,
@@ -56,6 +57,7 @@ SIGNATURES = {
     "qlin_gemm_workspace_bytes": [_I32, _I64, _I64, _I64],
     "qlin_gemm_static_ws": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
+    "qlin_gemm_geglu": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
     "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
     "qlin_rotate_quant_act_static": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P],
@@ -130,6 +132,24 @@ def _need(t, nbytes: int, name: str) -> None:
         raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
 
 
+def code_row_bytes(k: int, bits: int) -> int:
+    """Bytes of one row of k codes: int8 (bits 8), packed int4 (bits 4) or
+    int4-grid codes in E2M3 storage (bits 6, three bytes per four codes)."""
+    return {8: k, 4: k // 2, QLIN_BITS_E2M3: k // 4 * 3}[bits]
+
+
+def _codes(rows: int, k: int, bits: int, device) -> torch.Tensor:
+    """An uninitialised code tensor: int8 [rows][k], or uint8 [rows][row bytes]."""
+    return torch.empty((rows, code_row_bytes(k, bits)), dtype=torch.int8 if bits == 8 else torch.uint8,
+                       device=device)
+
+
+def _operand_bytes(scheme: int, k: int) -> Tuple[int, int]:
+    """Row bytes of the activation and weight codes of a GEMM scheme."""
+    return {QLIN_W4A4: (k // 2, k // 2), QLIN_W8A8: (k, k), QLIN_W4A8: (k, k // 2),
+            QLIN_W4A4_E2M3: (k // 4 * 3, k // 4 * 3)}[scheme]
+
+
 # --------------------------------------------------------------------------
 # entry points
 # --------------------------------------------------------------------------
@@ -153,13 +173,13 @@ def qlin_calibrate_fold(x: torch.Tensor, w: torch.Tensor, pre: int = QLIN_PRE_NO
 
 def qlin_quantize_weights(w: torch.Tensor, fold_s: Optional[torch.Tensor] = None, had_block: int = 0,
                           bits: int = 4, group: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Codes (int8 [n][k] or packed uint8 [n][k/2]) and scales (float32 [n],
-    or fp16 [n][k/group] for group quantization) of weights w [n][k]."""
+    """Codes (int8 [n][k], packed uint8 [n][k/2], or E2M3 uint8 [n][3k/4] for
+    bits 6) and scales (float32 [n], or fp16 [n][k/group] for group
+    quantization) of weights w [n][k]."""
     lib = load()
     _dev_tensor(w, "w")
     n, k = w.shape
-    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
-                     device=w.device)
+    wq = _codes(n, k, bits, w.device)
     ws = (torch.empty((n, k // group), dtype=torch.float16, device=w.device) if group
           else torch.empty(n, dtype=torch.float32, device=w.device))
     st = lib.qlin_quantize_weights(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
@@ -182,12 +202,11 @@ def qlin_rotate_quant_act(x: torch.Tensor, k: Optional[int] = None, fold_inv_s: 
     if x.dim() != 2 or x.stride(1) != 1 or (2 * k if pre == QLIN_PRE_GEGLU else k) > x.shape[1]:
         raise ValueError("x must be a row-major [m][>= k] tensor ([m][>= 2k] with the GeGLU pre-op)")
     if out is None:
-        xq = torch.empty((m, k // 2) if bits == 4 else (m, k), dtype=torch.uint8 if bits == 4 else torch.int8,
-                         device=x.device)
+        xq = _codes(m, k, bits, x.device)
         xs = torch.empty(m, dtype=torch.float32, device=x.device)
     else:
         xq, xs = out
-    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    _need(xq, m * code_row_bytes(k, bits), "xq")
     _need(xs, m * 4, "x_scale")
     st = lib.qlin_rotate_quant_act(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0), pre,
                                    _ptr(fold_inv_s), had_block, bits, xq.data_ptr(), xs.data_ptr(),
@@ -229,10 +248,8 @@ def qlin_rotate_quant_act_static(x: torch.Tensor, table: torch.Tensor, k: Option
     lib = load()
     k = _rows_arg(x, k)
     m = x.shape[0]
-    xq = out if out is not None else torch.empty((m, k // 2) if bits == 4 else (m, k),
-                                                 dtype=torch.uint8 if bits == 4 else torch.int8,
-                                                 device=x.device)
-    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    xq = out if out is not None else _codes(m, k, bits, x.device)
+    _need(xq, m * code_row_bytes(k, bits), "xq")
     _need(table, k * 4, "table")
     _need(fold_inv_s, k * 4, "fold_inv_s")
     st = lib.qlin_rotate_quant_act_static(x.data_ptr(), _TORCH_TO_QLIN[x.dtype], m, k, x.stride(0),
@@ -252,8 +269,7 @@ def qlin_quantize_weights_step(w: torch.Tensor, table: torch.Tensor, fold_s: Opt
     _need(w, n * k * w.element_size(), "w")
     _need(table, k * 4, "table")
     _need(fold_s, k * 4, "fold_s")
-    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
-                     device=w.device)
+    wq = _codes(n, k, bits, w.device)
     ws = torch.empty(n, dtype=torch.float32, device=w.device)
     st = lib.qlin_quantize_weights_step(w.data_ptr(), _TORCH_TO_QLIN[w.dtype], n, k, _ptr(fold_s), had_block,
                                         bits, table.data_ptr(), wq.data_ptr(), ws.data_ptr(), _stream(w.device))
@@ -295,12 +311,11 @@ def qlin_rotate_quant_act_composite(x: torch.Tensor, perm: torch.Tensor, rot: to
     k = _rows_arg(x, k)
     m, b = x.shape[0], rot.shape[-1]
     if out is None:
-        xq = torch.empty((m, k // 2) if bits == 4 else (m, k), dtype=torch.uint8 if bits == 4 else torch.int8,
-                         device=x.device)
+        xq = _codes(m, k, bits, x.device)
         xs = torch.empty(m, dtype=torch.float32, device=x.device)
     else:
         xq, xs = out
-    _need(xq, m * (k // 2 if bits == 4 else k), "xq")
+    _need(xq, m * code_row_bytes(k, bits), "xq")
     _need(xs, m * 4, "x_scale")
     _need(perm, k * 4, "perm")
     _need(rot, k * b * 4, "rot")
@@ -328,8 +343,7 @@ def qlin_quantize_weights_composite(w: torch.Tensor, perm: torch.Tensor, rot: to
     _need(perm, k * 4, "perm")
     _need(rot, k * b * 4, "rot")
     _need(fold_s, k * 4, "fold_s")
-    wq = torch.empty((n, k // 2) if bits == 4 else (n, k), dtype=torch.uint8 if bits == 4 else torch.int8,
-                     device=w.device)
+    wq = _codes(n, k, bits, w.device)
     ws = torch.empty(n, dtype=torch.float32, device=w.device)
     if work is None:
         work = torch.empty(n * k, dtype=torch.float32, device=w.device)
@@ -360,8 +374,7 @@ def _gemm(fn_name: str, xq, x_scale, wq, w_scale, k: int, y_dtype, out, workspac
     lib = load()
     _dev_tensor(wq, "wq")
     m, n = xq.shape[0], wq.shape[0]
-    ka = k // 2 if fn_name == "qlin_gemm_w4a4" else k
-    kb = k if fn_name == "qlin_gemm_w8a8" else k // 2
+    ka, kb = _operand_bytes(_SCHEME[fn_name], k)
     _need(xq, m * ka, "xq")
     _need(wq, n * kb, "wq")
     _need(x_scale, m * 4, "x_scale")
@@ -392,8 +405,7 @@ def qlin_gemm_static_ws(scheme: int, xq, x_scale, wq, w_scale, k: int, y_dtype=t
     lib = load()
     _dev_tensor(wq, "wq")
     m, n = xq.shape[0], wq.shape[0]
-    ka = k // 2 if scheme == QLIN_W4A4 else k
-    kb = k if scheme == QLIN_W8A8 else k // 2
+    ka, kb = _operand_bytes(scheme, k)
     _need(xq, m * ka, "xq")
     _need(wq, n * kb, "wq")
     _need(x_scale, m * 4, "x_scale")
@@ -423,6 +435,47 @@ def qlin_gemm_w4a8(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out
                    workspace=None) -> torch.Tensor:
     """y [m][n] from int8 activation codes xq [m][k] and packed int4 weight codes wq [n][k/2]."""
     return _gemm("qlin_gemm_w4a8", xq, x_scale, wq, w_scale, k, y_dtype, out, workspace)
+
+
+def qlin_gemm_e2m3(xq, x_scale, wq, w_scale, k: int, y_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """y [m][n] from int4-grid codes in E2M3 storage, xq [m][3k/4] and wq
+    [n][3k/4] (qlin_gemm_ws with scheme QLIN_W4A4_E2M3, which takes no
+    workspace): the results of qlin_gemm_w4a4 on the same codes."""
+    lib = load()
+    _dev_tensor(wq, "wq")
+    m, n = xq.shape[0], wq.shape[0]
+    ka, kb = _operand_bytes(QLIN_W4A4_E2M3, k)
+    _need(xq, m * ka, "xq")
+    _need(wq, n * kb, "wq")
+    _need(x_scale, m * 4, "x_scale")
+    _need(w_scale, n * 4, "w_scale")
+    y = out if out is not None else torch.empty((m, n), dtype=y_dtype, device=wq.device)
+    _need(y, m * n * y.element_size(), "y")
+    st = lib.qlin_gemm_ws(QLIN_W4A4_E2M3, xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n, k,
+                          y.data_ptr(), _TORCH_TO_QLIN[y.dtype], None, 0, _stream(wq.device))
+    _check(st, "qlin_gemm_ws")
+    return y
+
+
+def qlin_gemm_geglu(scheme: int, xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat16,
+                    out=None) -> torch.Tensor:
+    """h [m][n2/2] = gelu(gate) * up from activation codes xq and the gate|up
+    weight codes wq [n2] with rows interleaved in blocks of 32, both packed
+    int4 (QLIN_W4A4) or both in E2M3 storage (QLIN_W4A4_E2M3)."""
+    lib = load()
+    _dev_tensor(wq, "wq")
+    m, n2 = xq.shape[0], wq.shape[0]
+    ka, kb = _operand_bytes(scheme, k)
+    _need(xq, m * ka, "xq")
+    _need(wq, n2 * kb, "wq")
+    _need(x_scale, m * 4, "x_scale")
+    _need(w_scale, n2 * 4, "w_scale")
+    h = out if out is not None else torch.empty((m, n2 // 2), dtype=h_dtype, device=wq.device)
+    _need(h, m * (n2 // 2) * h.element_size(), "h")
+    st = lib.qlin_gemm_geglu(scheme, xq.data_ptr(), _ptr(x_scale), wq.data_ptr(), _ptr(w_scale), m, n2, k,
+                             h.data_ptr(), _TORCH_TO_QLIN[h.dtype], _stream(wq.device))
+    _check(st, "qlin_gemm_geglu")
+    return h
 
 
 def qlin_gemm_w4a4_geglu(xq, x_scale, wq, w_scale, k: int, h_dtype=torch.bfloat16, out=None) -> torch.Tensor:

@@ -54,7 +54,7 @@ struct RowQuantParams {
     int g;              // lanes per row (power of two, 8..256)
     int nch;            // chunk passes actually used (<= NCH)
     int had_block;      // 0/1: none
-    int bits;           // 4 or 8
+    int bits;           // 8 (int8), 4 (packed int4) or 6 (int4 grid stored as E2M3)
     void* q;            // codes out (column maxima as float bits in ROWQ_COLMAX)
     float* scale;       // per-row scale out (unused in ROWQ_STATIC and ROWQ_COLMAX)
     const float* post;  // per-channel table after the rotation (ROWQ_STATIC, ROWQ_POSTMUL)
@@ -248,6 +248,71 @@ __device__ __forceinline__ uint32_t pack8_i4(const uint32_t cb[8]) {
     return (e & 0x0F0F0F0Fu) | ((o << 4) & 0xF0F0F0F0u);
 }
 
+// E2M3 fields (FP6: sign, 2 exponent bits with bias 1, 3 mantissa bits) of
+// the int4-grid codes 0 .. 7, and of n - 16 for the two's complement nibbles
+// n = 9 .. 15, by byte (n = 8, the code -8, never occurs: the grid is
+// symmetric).  1 = 1.0 x 2^0 is 0b001000, 3 = 1.5 x 2^1 is 0b010100,
+// 7 = 1.75 x 2^2 is 0b011110; negative codes set bit 5.
+constexpr uint32_t kE2m3PosLo = 0x14100800u, kE2m3PosHi = 0x1E1C1A18u;
+constexpr uint32_t kE2m3NegLo = 0x3A3C3E00u, kE2m3NegHi = 0x28303438u;
+
+// Eight codes held as the low bytes of magic-biased floats -> 48 bits of
+// E2M3 fields, code j at bits 6j .. 6j+5 (w.x bits 0..31, then w.y bits 0..15).
+// Per byte: the field of the low three bits from the positive or the negative
+// table (v_perm_b32 byte lookups), chosen by the byte's sign, which v_perm
+// selectors 8 .. 11 replicate (the sign bits of bytes 1 and 3 of each source:
+// x << 8 supplies bytes 0 and 2 there).
+__device__ __forceinline__ uint2 pack8_e2m3(const uint32_t cb[8]) {
+    const uint2 bytes = pack8_i8(cb);
+    uint32_t f24[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t x = h ? bytes.y : bytes.x;
+        const uint32_t sel = x & 0x07070707u;
+        const uint32_t pos = __builtin_amdgcn_perm(kE2m3PosHi, kE2m3PosLo, sel);
+        const uint32_t neg = __builtin_amdgcn_perm(kE2m3NegHi, kE2m3NegLo, sel);
+        const uint32_t negm = __builtin_amdgcn_perm(x << 8, x, 0x090B080Au);
+        const uint32_t c = (neg & negm) | (pos & ~negm);
+        // four 6-bit fields from four bytes: pairs to 12 bits, then 24
+        const uint32_t t = (c & 0x003F003Fu) | ((c >> 2) & 0x0FC00FC0u);
+        f24[h] = (t & 0xFFFu) | ((t >> 4) & 0x00FFF000u);
+    }
+    return make_uint2(f24[0] | (f24[1] << 24), f24[1] >> 8);
+}
+
+// E2M3 store of a lane's eight codes at columns col .. col+7 of a row whose
+// codes start at row_out (3 bytes per 4 codes).  The lanes 2j and 2j+1 hold
+// consecutive chunks of the same row (their columns are 8 apart), so the pair
+// forms 12 bytes at a 4-byte aligned offset and the even lane stores them.
+// Both lanes of a pair must be active (same row, same column validity).
+__device__ __forceinline__ void store8_e2m3(const uint32_t cb[8], uint8_t* row_out, int64_t col, int lane) {
+    const uint2 w = pack8_e2m3(cb);
+    // quad_perm [1, 0, 3, 2]: the partner lane's 48 bits
+    const uint32_t o0 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(w.x), 0xB1, 0xF, 0xF, false));
+    const uint32_t o1 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(w.y), 0xB1, 0xF, 0xF, false));
+    if ((lane & 1) == 0) {
+        uint32_t* out = reinterpret_cast<uint32_t*>(row_out + (col >> 3) * 6);
+        out[0] = w.x;
+        out[1] = (w.y & 0xFFFFu) | (o0 << 16);
+        out[2] = (o0 >> 16) | (o1 << 16);
+    }
+}
+
+// Codes of one chunk (eight magic-biased floats) to their storage: int8, packed
+// int4 (two per byte) or E2M3 (see store8_e2m3).
+__device__ __forceinline__ void store8_codes(int bits, const uint32_t cb[8], void* q, int64_t row, int64_t k,
+                                             int64_t col, int lane) {
+    if (bits == 8) {
+        int8_t* out = static_cast<int8_t*>(q) + row * k + col;
+        *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
+    } else if (bits == 4) {
+        uint8_t* out = static_cast<uint8_t*>(q) + row * (k / 2) + col / 2;
+        *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
+    } else {
+        store8_e2m3(cb, static_cast<uint8_t*>(q) + row * (k / 4 * 3), col, lane);
+    }
+}
+
 // Rows of k values; TPB lanes per block, g lanes per row (g <= TPB, RPB =
 // TPB / g rows per block and iteration), NCH chunk passes of 8 values per
 // lane.  Blocks are persistent: block i handles row groups i, i + grid, ...
@@ -315,7 +380,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
     }
     // fp32 of 1/sqrt(b), correctly rounded (exact for b = 4^j)
     const float nrm = static_cast<float>(1.0 / sqrt(static_cast<double>(b)));
-    const float qmax = (p.bits == 8) ? 127.f : 7.f;
+    const float qmax = (p.bits == 8) ? 127.f : 7.f;   // 4 and 6: the int4 grid
     // lane sign left by the cross-lane stages (lane bits below b/8)
     const int lane_bits = (b > 8) ? (lane & (b / 8 - 1)) : 0;
     const float sigma = (__builtin_popcount(lane_bits) & 1) ? -1.f : 1.f;
@@ -438,13 +503,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
                 uint32_t cb[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(qb[e], M - qmax, M + qmax));
-                if (p.bits == 8) {
-                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
-                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
-                } else {
-                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
-                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
-                }
+                store8_codes(p.bits, cb, p.q, row, p.k, col, lane);
             }
         }
 
@@ -478,13 +537,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_rows_kernel(RowQuantParams p
                 uint32_t cb[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(qb[e], M - qmax, M + qmax));
-                if (p.bits == 8) {
-                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
-                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
-                } else {
-                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
-                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
-                }
+                store8_codes(p.bits, cb, p.q, row, p.k, col, lane);
             }
         }
         if constexpr (PF) {
@@ -688,13 +741,7 @@ __global__ __launch_bounds__(TPB) void rotate_quant_bf16_kernel(RowQuantParams p
                 uint32_t cb[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cb[e] = __float_as_uint(qb[e]);
-                if constexpr (BITS == 8) {
-                    int8_t* out = static_cast<int8_t*>(p.q) + row * p.k + col;
-                    *reinterpret_cast<uint2*>(out) = pack8_i8(cb);
-                } else {
-                    uint8_t* out = static_cast<uint8_t*>(p.q) + row * (p.k / 2) + col / 2;
-                    *reinterpret_cast<uint32_t*>(out) = pack8_i4(cb);
-                }
+                store8_codes(BITS, cb, p.q, row, p.k, col, lane);
             }
         }
         if constexpr (PF) {
@@ -893,10 +940,20 @@ hipError_t launch_fast_tpb(const RowQuantParams& p, hipStream_t st) {
     return launch_fast_nch<GEGLU, HB, BITS, 256>(p, st);
 }
 
+template <bool GEGLU, int HB>
+hipError_t launch_fast_bits(const RowQuantParams& p, hipStream_t st) {
+    switch (p.bits) {
+        case 8: return launch_fast_tpb<GEGLU, HB, 8>(p, st);
+        case 4: return launch_fast_tpb<GEGLU, HB, 4>(p, st);
+        case 6: return launch_fast_tpb<GEGLU, HB, 6>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <bool GEGLU>
 hipError_t launch_fast_geglu(const RowQuantParams& p, hipStream_t st) {
-    if (p.had_block == 64) return p.bits == 8 ? launch_fast_tpb<GEGLU, 64, 8>(p, st) : launch_fast_tpb<GEGLU, 64, 4>(p, st);
-    return p.bits == 8 ? launch_fast_tpb<GEGLU, 128, 8>(p, st) : launch_fast_tpb<GEGLU, 128, 4>(p, st);
+    if (p.had_block == 64) return launch_fast_bits<GEGLU, 64>(p, st);
+    return launch_fast_bits<GEGLU, 128>(p, st);
 }
 
 hipError_t launch_bf16_fast(const RowQuantParams& p, bool geglu, hipStream_t st) {

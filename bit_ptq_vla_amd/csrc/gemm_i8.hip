@@ -197,9 +197,10 @@ __device__ __forceinline__ float gelu_outside_tab(uint32_t bits) {
 // T table kept in LDS (16 table reads in flight per group, one branch per
 // group for values outside it), h = gelu(g) * u is rounded to the output
 // dtype and staged through LDS for 16-byte row stores of the (BM/2) x (BN/4)
-// h tile.
-template <int BM, int BN, int ASH, int ODT, int STAGE>
-__device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
+// h tile.  V: v16i (int32 accumulators) or v16f (fp32 accumulators holding
+// exact integers).
+template <int BM, int BN, int ASH, int ODT, int STAGE, typename V>
+__device__ __forceinline__ void store_tile_geglu(const V (&acc)[BM / 64][BN / 64], const GemmParams& p,
                                                  int64_t row0, int64_t col0, int lane, const float* tab,
                                                  int8_t* region) {
     constexpr int TM = BM / 64, TN = BN / 64;
@@ -333,8 +334,8 @@ __device__ __forceinline__ void store_tile_geglu(const v16i (&acc)[BM / 64][BN /
 // elements) so that the two half-waves, which write rows 4 apart, hit
 // different banks.  OUT: -1 raw int32 partial, I32 raw accumulators, else
 // the dequantized value acc * x_scale[row] * w_scale[col] rounded to OUT.
-template <int BM, int BN, int ASH, int OUT, int STAGE>
-__device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 64], const GemmParams& p,
+template <int BM, int BN, int ASH, int OUT, int STAGE, typename V>
+__device__ __forceinline__ void store_tile_lds(const V (&acc)[BM / 64][BN / 64], const GemmParams& p,
                                                int64_t row0, int64_t col0, int lane, int8_t* region,
                                                void* dst) {
     constexpr int TM = BM / 64, TN = BN / 64;
@@ -391,7 +392,8 @@ __device__ __forceinline__ void store_tile_lds(const v16i (&acc)[BM / 64][BN / 6
                     // rows rl and rl + 1 of this lane's column
                     const int rl = ti * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     int8_t* at = region + rl * PITCH + (j * 32 + l32) * E;
-                    int32_t a0 = acc[i][j][r], a1 = acc[i][j][r + 1];
+                    // (an fp32 accumulator holds an exact integer)
+                    int32_t a0 = static_cast<int32_t>(acc[i][j][r]), a1 = static_cast<int32_t>(acc[i][j][r + 1]);
                     if constexpr (FLOAT_OUT) {
                         const float v0 = static_cast<float>(a0) * sxv[r >> 2][r & 3] * swv[j];
                         const float v1 = static_cast<float>(a1) * sxv[r >> 2][(r & 3) + 1] * swv[j];
@@ -1057,6 +1059,226 @@ __global__ __launch_bounds__(256, 1) void gemm256_kernel(GemmParams p) {
     }
 }
 
+// ---- E2M3 operands: W4A4 codes on the FP6 matrix cores ---------------------
+//
+// The int4-grid codes (-7 .. 7) stored as FP6 E2M3 fields, 32 per 24 bytes,
+// code j of a row at bits 6j .. 6j+5, feed v_mfma_scale_f32_32x32x64_f8f6f4
+// with both operands E2M3 and unit block scales (E8M0 127).  Every grid value
+// is exact in E2M3, a product of two is exact in fp32, and every partial sum
+// is an integer of magnitude below 49 k < 2^24, so the fp32 accumulator holds
+// exactly the int32 accumulator of the integer kernels.  The instruction does
+// 32 x 32 x 64 in the cycles the int8 one takes for 32 x 32 x 32.
+//
+// A lane supplies 32 fields (six dwords) of one row per issue.  A stage holds
+// 128 k of a row: 96 bytes, six 16-byte chunks.  Lane half h reads chunks
+// 3h .. 3h+2 with three ds_read_b128; the first 24 bytes feed the stage's
+// first k-step and the last 24 its second.  A and B fragments are read the
+// same way, so each issue pairs equal k.  In LDS, chunk c of row r sits at
+// chunk slot c ^ ((r >> 3) & 1): with a 96-byte pitch rows r and r + 8 start
+// on the same banks, and the swizzle gives them slots of opposite parity
+// (16 lanes of a ds_read_b128 then reach 16 distinct 16-byte bank groups).
+// The ring is three stages deep; buffers are addressed at run time, so the
+// branch-free loop body covers two stages (the fragment register parity) and
+// K pads to an even stage count at most.  Tiles: 256 x 256 (one block per CU,
+// waves 128 x 128) for grids that fill the chip, else 128 x 128 (two blocks
+// per CU, waves 64 x 64).
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef int v12i_t __attribute__((ext_vector_type(12)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN, int MINB, int OUT>
+__global__ __launch_bounds__(256, MINB) void gemm_f6_kernel(GemmParams p) {
+    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int NS = 3;
+    constexpr int SB = 96;                          // bytes of a row per stage (128 codes)
+    constexpr int STAGE = (BM + BN) * SB;
+    constexpr int LOADS = (BM + BN) * SB / 4096;    // 16-byte DMA loads per lane per stage
+    constexpr int LA = BM * SB / 4096;              // ... of them for A
+    static_assert(LA * 4096 == BM * SB && LOADS * 4096 == STAGE, "whole 1 KB loads per wave");
+    constexpr int MF = 2 * TM * TN;                 // MFMAs per stage
+    constexpr int READS = 3 * (TM + TN);            // 16-byte fragment reads per stage
+    constexpr int OPS = LOADS + READS;
+    constexpr bool GEGLU = OUT >= OUT_GEGLU;
+    constexpr int RING0 = GEGLU ? GTAB_BYTES : 0;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING0 + NS * STAGE];
+    int8_t* const ring = lds + RING0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int nblocks = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    int tile_m, tile_n;
+    if (p.group_m > 0) {
+        const int per_group = p.group_m * p.tiles_n;
+        const int g = bid / per_group;
+        const int first = g * p.group_m;
+        const int rows = (p.tiles_m - first) < p.group_m ? (p.tiles_m - first) : p.group_m;
+        const int r = bid - g * per_group;
+        tile_n = r / rows;
+        tile_m = first + (r - tile_n * rows);
+    } else {
+        tile_n = bid / p.tiles_m;
+        tile_m = bid - tile_n * p.tiles_m;
+    }
+    const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
+    const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
+    const int nst = p.stages;
+    const int nstp = (nst + 1) & ~1;
+    constexpr int OOB = 0x7FFFFFF0;
+    const int kb = static_cast<int>(p.kbytes);
+
+    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes, (p.m - m0) * p.kbytes);
+    const v4i rsrc_b = make_rsrc(p.b + n0 * p.kbytes, (p.n - n0) * p.kbytes);
+
+    // DMA: load q of wave w fills the 64 chunk slots at stage offset (4q + w) KB
+    // (A rows first, then B rows); the lane's slot holds chunk pos ^ swizzle of its row
+    int dvoff[LOADS];
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+        const int slot = (4 * q + wave) * 64 + lane;
+        const int s2 = q < LA ? slot : slot - BM * 6;
+        const int r = s2 / 6, pos = s2 - r * 6;
+        dvoff[q] = r * kb + (pos ^ ((r >> 3) & 1)) * 16;
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+    auto dma_one = [&](int st, uint32_t buf_addr, int q) __attribute__((always_inline)) {
+        const int off = st < nst ? dvoff[q] + st * SB : OOB;
+        dma16(q < LA ? rsrc_a : rsrc_b, off, buf_addr + wave_u * 1024 + q * 4096);
+    };
+
+    v16f_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // the three chunks this lane reads of a row (lane half h: chunks 3h .. 3h+2)
+    const int l32 = lane & 31;
+    const int hsel = lane >> 5;
+    const int sw = (l32 >> 3) & 1;
+    const int a_row = (wm * (BM / 2) + l32) * SB;
+    const int b_row = BM * SB + (wn * (BN / 2) + l32) * SB;
+    int coff[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) coff[t] = ((3 * hsel + t) ^ sw) * 16;
+
+    // a fragment: the 48 bytes (12 dwords) of one row for the stage's two k-steps,
+    // held as one 12-dword vector so that each k-step's six dwords are a
+    // contiguous register range of it
+    struct Frag {
+        v12i_t a[TM];
+        v12i_t b[TN];
+    };
+    Frag f[2];
+    // read r (0 .. READS-1) of a fragment set from the stage buffer at st
+    auto read_one = [&](const int8_t* st, Frag& fr, auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int which = r / 3, t = r % 3;
+        const v4i d = (which < TM)
+                          ? *reinterpret_cast<const v4i*>(st + a_row + coff[t] + which * 32 * SB)
+                          : *reinterpret_cast<const v4i*>(st + b_row + coff[t] + (which - TM) * 32 * SB);
+        v12i_t& v = (which < TM) ? fr.a[which < TM ? which : 0] : fr.b[which < TM ? 0 : which - TM];
+        v[4 * t + 0] = d.x;
+        v[4 * t + 1] = d.y;
+        v[4 * t + 2] = d.z;
+        v[4 * t + 3] = d.w;
+    };
+    // the six dwords of k-step ks (0, 1) of a fragment
+    auto operand = [](const v12i_t& c, auto kc) __attribute__((always_inline)) -> v8i_t {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks == 0)
+            return __builtin_shufflevector(c, c, 0, 1, 2, 3, 4, 5, -1, -1);
+        else
+            return __builtin_shufflevector(c, c, 6, 7, 8, 9, 10, 11, -1, -1);
+    };
+    // MFMA q (0 .. MF-1) of a stage: k-step q / (TM TN), row tile (q % (TM TN)) / TN, column tile q % TN
+    auto mfma_one = [&](const Frag& fr, auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int ks = q / (TM * TN), i = (q % (TM * TN)) / TN, j = q % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            operand(fr.a[i], std::integral_constant<int, ks>{}), operand(fr.b[j], std::integral_constant<int, ks>{}),
+            acc[i][j], 2, 2, 0, 127, 0, 127);
+    };
+    auto sync_next = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<(NS - 2) * LOADS>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    if constexpr (GEGLU) {
+        static_assert(GTAB_BYTES == 2 * 4 * 1024, "two 16-byte loads per lane");
+        const v4i rsrc_t = make_rsrc(reinterpret_cast<const int8_t*>(g_gelu_neg_tab), GTAB_BYTES);
+        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave_u * 1024;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(rsrc_t, (i * 4 + wave) * 1024 + lane * 16, t_dst + i * 4096);
+    }
+#pragma unroll
+    for (int pst = 0; pst < NS; ++pst)
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) dma_one(pst, ring_addr + pst * STAGE, q);
+    wait_vmcnt<(NS - 1) * LOADS>();   // stage 0 (and the GeLU table, issued first) landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    static_for<0, READS>([&](auto rc) __attribute__((always_inline)) { read_one(ring, f[0], rc); });
+
+    // one stage: 4 MFMAs, the synchronisation, then the remaining MFMAs with the
+    // DMA of stage it + NS into this stage's buffer and the next stage's
+    // fragment reads spread over them
+    auto stage = [&](auto par, int it, int bi) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        const Frag& cur = f[P];
+        Frag& nxt = f[P ^ 1];
+        const int nbi = bi == NS - 1 ? 0 : bi + 1;
+        const uint32_t buf_addr = ring_addr + bi * STAGE;
+        const int8_t* nbuf = ring + nbi * STAGE;
+        static_for<0, 4>([&](auto qc) __attribute__((always_inline)) { mfma_one(cur, qc); });
+        __builtin_amdgcn_sched_barrier(0);
+        sync_next();
+        static_for<4, MF>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mfma_one(cur, qc);
+            // the memory operations o with 4 + o (MF - 4) / OPS == q
+            static_for<0, OPS>([&](auto oc) __attribute__((always_inline)) {
+                constexpr int o = decltype(oc)::value;
+                if constexpr (4 + o * (MF - 4) / OPS == q) {
+                    if constexpr (o < LOADS) dma_one(it + NS, buf_addr, o);
+                    else read_one(nbuf, nxt, std::integral_constant<int, o - LOADS>{});
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    int bi = 0;
+    for (int it = 0; it < nstp; it += 2) {
+        stage(std::integral_constant<int, 0>{}, it, bi);
+        bi = bi == NS - 1 ? 0 : bi + 1;
+        stage(std::integral_constant<int, 1>{}, it + 1, bi);
+        bi = bi == NS - 1 ? 0 : bi + 1;
+    }
+
+    // ---- epilogue (as gemm256_kernel): the ring is free once every wave is past it
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (m0 + wm * (BM / 2) >= p.m) return;
+    constexpr int REGION = NS * STAGE / 4 / 16 * 16;
+    if constexpr (GEGLU) {
+        store_tile_geglu<BM, BN, 0, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                                             reinterpret_cast<const float*>(lds),
+                                                             ring + wave * REGION);
+    } else {
+        store_tile_lds<BM, BN, 0, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                               ring + wave * REGION, p.y);
+    }
+}
+
 // Sum of split-K partials in split order (integer: bit-exact), then the
 // epilogue; four consecutive outputs per lane (n % 4 == 0), else one.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* ws, int splits, int64_t m,
@@ -1174,6 +1396,32 @@ hipError_t launch_geglu_out(const GemmParams& p, hipStream_t st) {
         case BF16: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + BF16>(p, st);
         case F16: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + F16>(p, st);
         case F32: return launch_tile<BM, BN, MINB, NS, INT4, OUT_GEGLU + F32>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int MINB, int OUT>
+hipError_t launch_f6(const GemmParams& p, hipStream_t st) {
+    dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n));
+    hipLaunchKernelGGL((gemm_f6_kernel<BM, BN, MINB, OUT>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int MINB>
+hipError_t launch_f6_out(const GemmParams& p, bool geglu, hipStream_t st) {
+    if (geglu) {
+        switch (p.y_dtype) {
+            case BF16: return launch_f6<BM, BN, MINB, OUT_GEGLU + BF16>(p, st);
+            case F16: return launch_f6<BM, BN, MINB, OUT_GEGLU + F16>(p, st);
+            case F32: return launch_f6<BM, BN, MINB, OUT_GEGLU + F32>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
+    switch (p.y_dtype) {
+        case BF16: return launch_f6<BM, BN, MINB, BF16>(p, st);
+        case F16: return launch_f6<BM, BN, MINB, F16>(p, st);
+        case F32: return launch_f6<BM, BN, MINB, F32>(p, st);
+        case I32: return launch_f6<BM, BN, MINB, I32>(p, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1331,6 +1579,52 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
         e = hipGetLastError();
     }
     return e;
+}
+
+GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k) {
+    (void)k;
+    GemmPlan g;
+    const int64_t cus = device_cus();
+    g.splits = 1;
+    g.deep = false;
+    g.ws_bytes = 0;
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles256 >= cus) {   // at least one 256 x 256 tile per CU
+        g.bm = g.bn = 256;
+        g.group_m = 4;
+        return g;
+    }
+    g.bm = g.bn = 128;
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    g.group_m = tiles >= 4 * cus ? 8 : 0;
+    return g;
+}
+
+hipError_t launch_gemm_f6(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
+                          const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, int y_dtype, bool geglu,
+                          hipStream_t st) {
+    if (plan.splits != 1) return hipErrorInvalidValue;
+    if (geglu) {
+        hipError_t e = ensure_gelu_neg_tab(st);
+        if (e != hipSuccess) return e;
+    }
+    GemmParams p;
+    p.a = static_cast<const int8_t*>(xq);
+    p.b = static_cast<const int8_t*>(wq);
+    p.sx = x_scale; p.sw = w_scale; p.y = y; p.ws = nullptr;
+    p.m = m; p.n = n;
+    p.kbytes = k / 4 * 3;
+    p.kbytes_a = p.kbytes;
+    p.stages = static_cast<int>(k / 128);
+    p.splits = 1;
+    p.stages_per_split = p.stages;
+    p.tiles_m = static_cast<int>((m + plan.bm - 1) / plan.bm);
+    p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
+    p.group_m = plan.group_m;
+    p.y_dtype = y_dtype;
+    if (plan.bm == 256) return launch_f6_out<256, 256, 1>(p, geglu, st);
+    if (plan.bm == 128 && plan.bn == 128) return launch_f6_out<128, 128, 2>(p, geglu, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,

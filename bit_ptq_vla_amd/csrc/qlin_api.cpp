@@ -82,6 +82,16 @@ constexpr int64_t kMaxRowK = 32768;
 // GEMM k bound (exclusive): 2^17.
 constexpr int64_t kMaxGemmK = 131072;
 
+// Code widths of the quantizers: int8, packed int4, or int4 codes in E2M3
+// storage (k a multiple of 128 there, the GEMM's stage).
+bool bits_ok(int32_t bits) { return bits == 4 || bits == 8 || bits == QLIN_BITS_E2M3; }
+bool bits_k_ok(int32_t bits, int64_t k) { return bits != QLIN_BITS_E2M3 || k % 128 == 0; }
+int64_t code_bytes(int64_t rows, int64_t k, int32_t bits) {
+    if (bits == 8) return rows * k;
+    if (bits == 4) return rows * (k / 2);
+    return rows * (k / 4 * 3);
+}
+
 // Shape checks of the integer GEMM schemes (before any pointer check).
 bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, bool int4) {
     // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
@@ -94,7 +104,8 @@ bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, bool int4) {
 }
 
 // Split-K partial bytes of the plan a call with a workspace takes (0: no split).
-int64_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool int4, bool a8) {
+int64_t gemm_ws_need(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool f6) {
+    if (f6) return 0;                                     // the E2M3 kernels never split
     if (m == 0 || m <= qlin::kSkinnyIntMaxM) return 0;   // the small-M kernel never splits
     return qlin::plan_gemm(m, n, k, int4, a8, true).ws_bytes;
 }
@@ -105,7 +116,7 @@ enum class Scratch { None, Caller, Static };
 
 qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                         int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, Scratch mode, void* ws,
-                        int64_t ws_bytes, void* stream, bool int4, bool a8) {
+                        int64_t ws_bytes, void* stream, bool int4, bool a8, bool f6) {
     const bool use_static = mode == Scratch::Static;
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !y) return QLIN_ERR_NULL;
@@ -118,18 +129,21 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale) ||
         !aligned16(ws))
         return QLIN_ERR_ALIGN;
-    const int64_t need = ws ? gemm_ws_need(m, n, k, int4, a8) : 0;
+    const int64_t need = ws ? gemm_ws_need(m, n, k, int4, a8, f6) : 0;
     if (ws && ws_bytes < need) return QLIN_ERR_WORKSPACE;
-    const int64_t kb = int4 ? k / 2 : k;
-    const int64_t ka = (int4 && !a8) ? k / 2 : k;
+    const int64_t kb = f6 ? k / 4 * 3 : int4 ? k / 2 : k;
+    const int64_t ka = f6 ? k / 4 * 3 : (int4 && !a8) ? k / 2 : k;
     const Span outs[2] = {{y, m * n * dtype_size(y_dtype)}, {ws, ws ? ws_bytes : 0}};
     const Span ins[4] = {{xq, m * ka}, {wq, n * kb}, {x_scale, m * 4}, {w_scale, n * 4}};
     if (any_overlap(outs, 2, ins, 4)) return QLIN_ERR_ALIAS;
-    if (use_static && gemm_ws_need(m, n, k, int4, a8) > QLIN_STATIC_SCRATCH_BYTES) return QLIN_ERR_WORKSPACE;
+    if (use_static && gemm_ws_need(m, n, k, int4, a8, f6) > QLIN_STATIC_SCRATCH_BYTES) return QLIN_ERR_WORKSPACE;
     if (m == 0) return QLIN_OK;
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
+    if (f6)
+        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n, k), xq, x_scale, wq, w_scale, m, n, k, y,
+                                            y_dtype, false, s));
     if (m <= qlin::kSkinnyIntMaxM)
         return map_err(qlin::launch_skinny_int(xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, s));
     if (use_static) {
@@ -144,11 +158,13 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
                                      static_cast<int32_t*>(ws), s));
 }
 
-bool scheme_flags(qlin_scheme scheme, bool* int4, bool* a8) {
+bool scheme_flags(qlin_scheme scheme, bool* int4, bool* a8, bool* f6) {
+    *f6 = false;
     switch (scheme) {
         case QLIN_W4A4: *int4 = true; *a8 = false; return true;
         case QLIN_W8A8: *int4 = false; *a8 = false; return true;
         case QLIN_W4A8: *int4 = true; *a8 = true; return true;
+        case QLIN_W4A4_E2M3: *int4 = true; *a8 = false; *f6 = true; return true;
     }
     return false;
 }
@@ -159,9 +175,10 @@ qlin_status table_rows_check(const void* x, qlin_dtype dt, int64_t rows, int64_t
     if (!table) return QLIN_ERR_NULL;
     if (rows > 0 && !x) return QLIN_ERR_NULL;
     if (!is_float_in(dt)) return QLIN_ERR_DTYPE;
-    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_ok(bits)) return QLIN_ERR_UNSUPPORTED;
     if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
     if (rows < 0 || k < 8 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < k) return QLIN_ERR_SHAPE;
+    if (!bits_k_ok(bits, k)) return QLIN_ERR_SHAPE;
     if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
     if (k > kMaxRowK) return QLIN_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(fold) || !aligned16(table)) return QLIN_ERR_ALIGN;
@@ -232,18 +249,18 @@ qlin_status qlin_quantize_weights(const void* w, qlin_dtype w_dtype, int64_t n, 
                                   void* wq, void* w_scale, void* stream) {
     if (!w || !wq || !w_scale) return QLIN_ERR_NULL;
     if (!is_float_in(w_dtype)) return QLIN_ERR_DTYPE;
-    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_ok(bits)) return QLIN_ERR_UNSUPPORTED;
     if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
     if (group != 0 && group != 128) return QLIN_ERR_UNSUPPORTED;
     if (group == 128 && (bits != 4 || fold_s != nullptr || had_block > 1)) return QLIN_ERR_UNSUPPORTED;
     if (n < 1 || k < 8 || (k % 8) != 0) return QLIN_ERR_SHAPE;
+    if (!bits_k_ok(bits, k)) return QLIN_ERR_SHAPE;
     if (group && (k % group) != 0) return QLIN_ERR_SHAPE;
     if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
     if (!group && k > kMaxRowK) return QLIN_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(fold_s)) return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
     const int64_t scale_bytes = group ? n * (k / group) * 2 : n * 4;
-    const Span outs[2] = {{wq, code_bytes}, {w_scale, scale_bytes}};
+    const Span outs[2] = {{wq, code_bytes(n, k, bits)}, {w_scale, scale_bytes}};
     const Span ins[2] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}};
     if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
     qlin_status st = check_device();
@@ -259,16 +276,16 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
                                   void* xq, float* x_scale, void* stream) {
     if (m > 0 && (!x || !xq || !x_scale)) return QLIN_ERR_NULL;
     if (!is_float_in(x_dtype)) return QLIN_ERR_DTYPE;
-    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_ok(bits)) return QLIN_ERR_UNSUPPORTED;
     if (!pow2_block_ok(had_block)) return QLIN_ERR_UNSUPPORTED;
     if (pre != QLIN_PRE_NONE && pre != QLIN_PRE_GEGLU) return QLIN_ERR_UNSUPPORTED;
     const int64_t width = (pre == QLIN_PRE_GEGLU) ? 2 * k : k;
     if (m < 0 || k < 8 || (k % 8) != 0 || (ldx % 8) != 0 || ldx < width) return QLIN_ERR_SHAPE;
+    if (!bits_k_ok(bits, k)) return QLIN_ERR_SHAPE;
     if (had_block > 1 && (k % had_block) != 0) return QLIN_ERR_SHAPE;
     if (k > kMaxRowK) return QLIN_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || !aligned16(fold_inv_s)) return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
-    const Span outs[2] = {{xq, code_bytes}, {x_scale, m * 4}};
+    const Span outs[2] = {{xq, code_bytes(m, k, bits)}, {x_scale, m * 4}};
     const Span ins[2] = {{x, m > 0 ? ((m - 1) * ldx + width) * dtype_size(x_dtype) : 0},
                          {fold_inv_s, fold_inv_s ? k * 4 : 0}};
     if (any_overlap(outs, 2, ins, 2)) return QLIN_ERR_ALIAS;
@@ -301,8 +318,7 @@ qlin_status qlin_rotate_quant_act_static(const void* x, qlin_dtype x_dtype, int6
     if (st != QLIN_OK) return st;
     if (m > 0 && !xq) return QLIN_ERR_NULL;
     if (!aligned16(xq)) return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
-    const Span outs[1] = {{xq, code_bytes}};
+    const Span outs[1] = {{xq, code_bytes(m, k, bits)}};
     const Span ins[3] = {{x, m > 0 ? ((m - 1) * ldx + k) * dtype_size(x_dtype) : 0},
                          {fold_inv_s, fold_inv_s ? k * 4 : 0}, {table, k * 4}};
     if (any_overlap(outs, 1, ins, 3)) return QLIN_ERR_ALIAS;
@@ -321,8 +337,7 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
     if (!wq || !w_scale) return QLIN_ERR_NULL;
     if (n < 1) return QLIN_ERR_SHAPE;
     if (!aligned16(wq) || !aligned16(w_scale)) return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
-    const Span outs[2] = {{wq, code_bytes}, {w_scale, n * 4}};
+    const Span outs[2] = {{wq, code_bytes(n, k, bits)}, {w_scale, n * 4}};
     const Span ins[3] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}, {table, k * 4}};
     if (any_overlap(outs, 2, ins, 3)) return QLIN_ERR_ALIAS;
     st = check_device();
@@ -365,12 +380,12 @@ qlin_status qlin_rotate_quant_act_composite(const void* x, qlin_dtype x_dtype, i
     if (st != QLIN_OK) return st;
     if (!perm || !rot) return QLIN_ERR_NULL;
     if (m > 0 && (!xq || !x_scale || !work)) return QLIN_ERR_NULL;
-    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_ok(bits)) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_k_ok(bits, k)) return QLIN_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(fold_inv_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(xq) ||
         !aligned16(x_scale) || !aligned16(work))
         return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? m * k / 2 : m * k;
-    const Span outs[3] = {{xq, code_bytes}, {x_scale, m * 4}, {work, m * k * 4}};
+    const Span outs[3] = {{xq, code_bytes(m, k, bits)}, {x_scale, m * 4}, {work, m * k * 4}};
     const Span ins[4] = {{x, m > 0 ? ((m - 1) * ldx + k) * dtype_size(x_dtype) : 0},
                          {fold_inv_s, fold_inv_s ? k * 4 : 0}, {perm, k * 4}, {rot, k * had_block * 4}};
     if (any_overlap(outs, 3, ins, 4)) return QLIN_ERR_ALIAS;
@@ -388,12 +403,12 @@ qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, i
     if (st != QLIN_OK) return st;
     if (!w || !perm || !rot || !wq || !w_scale || !work) return QLIN_ERR_NULL;
     if (n < 1) return QLIN_ERR_SHAPE;
-    if (bits != 4 && bits != 8) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_ok(bits)) return QLIN_ERR_UNSUPPORTED;
+    if (!bits_k_ok(bits, k)) return QLIN_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(fold_s) || !aligned16(perm) || !aligned16(rot) || !aligned16(wq) ||
         !aligned16(w_scale) || !aligned16(work))
         return QLIN_ERR_ALIGN;
-    const int64_t code_bytes = (bits == 4) ? n * k / 2 : n * k;
-    const Span outs[3] = {{wq, code_bytes}, {w_scale, n * 4}, {work, n * k * 4}};
+    const Span outs[3] = {{wq, code_bytes(n, k, bits)}, {w_scale, n * 4}, {work, n * k * 4}};
     const Span ins[4] = {{w, n * k * dtype_size(w_dtype)}, {fold_s, fold_s ? k * 4 : 0}, {perm, k * 4},
                          {rot, k * had_block * 4}};
     if (any_overlap(outs, 3, ins, 4)) return QLIN_ERR_ALIAS;
@@ -404,38 +419,48 @@ qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, i
 
 qlin_status qlin_gemm_w4a4(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, false);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, false,
+                       false);
 }
 
 qlin_status qlin_gemm_w8a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
     return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, false,
-                       false);
+                       false, false);
 }
 
 qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                            int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype, void* stream) {
-    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, true);
+    return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::None, nullptr, 0, stream, true, true,
+                       false);
 }
 
 int64_t qlin_gemm_workspace_bytes(qlin_scheme scheme, int64_t m, int64_t n, int64_t k) {
-    bool int4 = false, a8 = false;
-    if (!scheme_flags(scheme, &int4, &a8)) return -1;
+    bool int4 = false, a8 = false, f6 = false;
+    if (!scheme_flags(scheme, &int4, &a8, &f6)) return -1;
     if (!gemm_shape_ok(m, n, k, int4)) return -1;
-    return gemm_ws_need(m, n, k, int4, a8);
+    return gemm_ws_need(m, n, k, int4, a8, f6);
 }
 
 qlin_status qlin_gemm_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
                          const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, qlin_dtype y_dtype,
                          void* workspace, int64_t workspace_bytes, void* stream) {
-    bool int4 = false, a8 = false;
-    if (!scheme_flags(scheme, &int4, &a8)) return QLIN_ERR_UNSUPPORTED;
+    bool int4 = false, a8 = false, f6 = false;
+    if (!scheme_flags(scheme, &int4, &a8, &f6)) return QLIN_ERR_UNSUPPORTED;
     return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::Caller, workspace, workspace_bytes,
-                       stream, int4, a8);
+                       stream, int4, a8, f6);
 }
 
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                                  int64_t m, int64_t n2, int64_t k, void* h, qlin_dtype h_dtype, void* stream) {
+    return qlin_gemm_geglu(QLIN_W4A4, xq, x_scale, wq, w_scale, m, n2, k, h, h_dtype, stream);
+}
+
+qlin_status qlin_gemm_geglu(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                            const float* w_scale, int64_t m, int64_t n2, int64_t k, void* h, qlin_dtype h_dtype,
+                            void* stream) {
+    if (scheme != QLIN_W4A4 && scheme != QLIN_W4A4_E2M3) return QLIN_ERR_UNSUPPORTED;
+    const bool f6 = scheme == QLIN_W4A4_E2M3;
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !h || !w_scale || (!x_scale && m > 0)) return QLIN_ERR_NULL;
     if (h_dtype != QLIN_F16 && h_dtype != QLIN_BF16 && h_dtype != QLIN_F32) return QLIN_ERR_DTYPE;
@@ -443,7 +468,7 @@ qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const voi
     if (m > 0x7FFFFFFF || n2 > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(h) || !aligned16(x_scale) || !aligned16(w_scale))
         return QLIN_ERR_ALIGN;
-    const int64_t kb = k / 2;
+    const int64_t kb = f6 ? k / 4 * 3 : k / 2;
     const Span outs[1] = {{h, m * (n2 / 2) * dtype_size(h_dtype)}};
     const Span ins[4] = {{xq, m * kb}, {wq, n2 * kb}, {x_scale, m * 4}, {w_scale, n2 * 4}};
     if (any_overlap(outs, 1, ins, 4)) return QLIN_ERR_ALIAS;
@@ -451,6 +476,9 @@ qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const voi
     qlin_status st = check_device();
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
+    if (f6)
+        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n2, k), xq, x_scale, wq, w_scale, m, n2, k, h,
+                                            h_dtype, true, s));
     return map_err(qlin::launch_gemm_geglu(xq, x_scale, wq, w_scale, m, n2, k, true, h, h_dtype, s));
 }
 
@@ -473,10 +501,10 @@ qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, 
 qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
                                 const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
                                 qlin_dtype y_dtype, void* stream) {
-    bool int4 = false, a8 = false;
-    if (!scheme_flags(scheme, &int4, &a8)) return QLIN_ERR_UNSUPPORTED;
+    bool int4 = false, a8 = false, f6 = false;
+    if (!scheme_flags(scheme, &int4, &a8, &f6)) return QLIN_ERR_UNSUPPORTED;
     return gemm_common(xq, x_scale, wq, w_scale, m, n, k, y, y_dtype, Scratch::Static, nullptr, 0, stream, int4,
-                       a8);
+                       a8, f6);
 }
 
 }  // extern "C"

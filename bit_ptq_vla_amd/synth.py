@@ -174,6 +174,13 @@ def random_codes(seed: int, name: str, rows: int, k: int, bits: int) -> torch.Te
     return torch.from_numpy(rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8))
 
 
+def random_grid_codes(seed: int, name: str, rows: int, k: int) -> np.ndarray:
+    """Uniform codes of the symmetric int4 grid, -7 .. 7 (the codes the
+    quantizers write), as int8 [rows][k] (numpy; storage is up to the caller)."""
+    rng = rng_for(seed, name)
+    return rng.integers(-7, 8, size=(rows, k), dtype=np.int8)
+
+
 def random_scales(seed: int, name: str, n: int) -> torch.Tensor:
     """Positive float32 scales spread over two decades."""
     rng = rng_for(seed, name)

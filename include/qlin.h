@@ -39,6 +39,14 @@
  *    byte, uint8_t[rows][k/2], element 2j in the low nibble and 2j+1 in the
  *    high nibble, two's complement.  Both grids are symmetric: codes lie in
  *    [-7, 7] or [-127, 127].
+ *  - E2M3 codes (bits == QLIN_BITS_E2M3 in the quantizers, scheme
+ *    QLIN_W4A4_E2M3 in the GEMMs): the int4 grid's codes, the same integers
+ *    -7 .. 7, each stored as the 6-bit FP6 E2M3 element of the OCP
+ *    Microscaling (MX) v1.0 format whose value is that integer (sign bit 5,
+ *    exponent bits 4..3 with bias 1, mantissa bits 2..0), packed densely
+ *    little-endian: code j of a row at bits 6j .. 6j+5 of the row's bytes,
+ *    uint8_t[rows][3k/4].  This is the operand format of the FP6 matrix
+ *    cores; the projection's results are those of the packed-int4 form.
  *  - Rounding is round-half-to-even everywhere (codes and fp16/bf16 outputs).
  */
 #ifndef QLIN_H
@@ -50,7 +58,7 @@
 extern "C" {
 #endif
 
-#define QLIN_ABI_VERSION 2
+#define QLIN_ABI_VERSION 3
 
 typedef int32_t qlin_status;
 enum {
@@ -73,9 +81,14 @@ enum { QLIN_F16 = 0, QLIN_BF16 = 1, QLIN_F32 = 2, QLIN_I32 = 3 };
 typedef int32_t qlin_preop;
 enum { QLIN_PRE_NONE = 0, QLIN_PRE_GEGLU = 1 };
 
-/* Integer GEMM schemes: activation codes x weight codes. */
+/* Integer GEMM schemes: activation codes x weight codes.  QLIN_W4A4_E2M3 is
+ * W4A4 with both operands in E2M3 storage (see the conventions above). */
 typedef int32_t qlin_scheme;
-enum { QLIN_W4A4 = 0, QLIN_W8A8 = 1, QLIN_W4A8 = 2 };
+enum { QLIN_W4A4 = 0, QLIN_W8A8 = 1, QLIN_W4A8 = 2, QLIN_W4A4_E2M3 = 3 };
+
+/* `bits` value of the quantizers for int4-grid codes (qmax 7) written in
+ * E2M3 storage; k must then be a multiple of 128. */
+#define QLIN_BITS_E2M3 6
 
 /* Version of this ABI (QLIN_ABI_VERSION). */
 int32_t qlin_abi_version(void);
@@ -119,8 +132,9 @@ qlin_status qlin_calibrate_fold(const void* x, qlin_dtype x_dtype, int64_t m, in
  *   fold_s   float[k] fold vector or NULL (no fold).
  *   had_block Hadamard block b: 0 or 1 = none, else a power of two <= 256
  *            dividing k.  Sylvester (natural) order, orthonormal.
- *   bits     4 or 8.   wq: out codes (layout above).
- * Preconditions: n, k >= 1; k % 8 == 0; k % group == 0.
+ *   bits     4, 8 or QLIN_BITS_E2M3 (group 0 only).   wq: out codes (layout
+ *            above).
+ * Preconditions: n, k >= 1; k % 8 == 0 (k % 128 == 0 for E2M3); k % group == 0.
  */
 qlin_status qlin_quantize_weights(const void* w, qlin_dtype w_dtype, int64_t n, int64_t k,
                                   const float* fold_s, int32_t had_block, int32_t bits,
@@ -136,10 +150,11 @@ qlin_status qlin_quantize_weights(const void* w, qlin_dtype w_dtype, int64_t n, 
  *   pre == GEGLU: x holds [gate | up] (2k values per row, ldx >= 2k) and
  *                 v is computed from gelu(gate) * up (exact erf form, fp32).
  *   x_dtype F16/BF16/F32; fold_inv_s float[k] (1/s) or NULL;
- *   had_block 0/1 = none, else a power of two <= 256 dividing k; bits 4 or 8.
- *   xq: out codes [m][k] int8 or [m][k/2] packed int4; x_scale: out float[m].
- *   A zero row gives scale 0 and codes 0.
- * Preconditions: k >= 8, k % 8 == 0; ldx % 8 == 0.
+ *   had_block 0/1 = none, else a power of two <= 256 dividing k; bits 4, 8
+ *   or QLIN_BITS_E2M3 (the int4 codes in E2M3 storage).
+ *   xq: out codes [m][k] int8, [m][k/2] packed int4 or [m][3k/4] E2M3;
+ *   x_scale: out float[m].  A zero row gives scale 0 and codes 0.
+ * Preconditions: k >= 8, k % 8 == 0 (k % 128 == 0 for E2M3); ldx % 8 == 0.
  */
 qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
                                   int64_t ldx, qlin_preop pre, const float* fold_inv_s,
@@ -175,8 +190,8 @@ qlin_status qlin_rotate_quant_act(const void* x, qlin_dtype x_dtype, int64_t m, 
  * Arguments as qlin_rotate_quant_act / qlin_quantize_weights; table is
  * float[k], 16-byte aligned, read (or written) on the device.  Preconditions:
  * k >= 8, k % 8 == 0, ldx % 8 == 0, ldx >= k; had_block 0/1 or a power of two
- * <= 256 dividing k; bits 4 or 8.  Errors as those entry points (NULL
- * table: QLIN_ERR_NULL).
+ * <= 256 dividing k; bits 4, 8 or QLIN_BITS_E2M3 (then k % 128 == 0).  Errors
+ * as those entry points (NULL table: QLIN_ERR_NULL).
  */
 qlin_status qlin_calibrate_step_scales(const void* x, qlin_dtype x_dtype, int64_t m, int64_t k,
                                        int64_t ldx, const float* fold_inv_s, int32_t had_block,
@@ -221,7 +236,7 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
  * qlin_quantize_weights_composite -- weights w [n][k] with fold_s (s or
  *   NULL); wq, w_scale out; work as above (n * k floats).
  * Preconditions: had_block b in {16, 32, 64, 128} dividing k; k % 8 == 0;
- * k <= 32768; bits 4 or 8;
+ * k <= 32768; bits 4, 8 or QLIN_BITS_E2M3 (then k % 128 == 0);
  * perm a permutation of 0 .. k-1 (other values are clamped into range).
  * Errors as the Hadamard entry points.
  */
@@ -282,6 +297,12 @@ qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
  * qlin_gemm_ws -- the integer GEMM of qlin_gemm_w4a4 / _w8a8 / _w4a8
  * (scheme QLIN_W4A4, QLIN_W8A8 or QLIN_W4A8; same arguments, results and
  * preconditions) with a caller-owned workspace for split-K partial sums.
+ * Scheme QLIN_W4A4_E2M3 takes both operands in E2M3 storage
+ * (qlin_rotate_quant_act / qlin_quantize_weights with bits QLIN_BITS_E2M3,
+ * rows of 3k/4 bytes) and gives the results of QLIN_W4A4 on the same codes:
+ * it runs on the FP6 matrix cores, whose fp32 sums of grid products are
+ * exact integers (|acc| <= 49 k < 2^24); k a multiple of 128, below 131072.
+ * It never splits k (its workspace size is 0).
  * When the output tile grid leaves the chip under-filled and k is long, the
  * call splits k over several blocks per tile: each split writes int32 partial
  * accumulators to the workspace ([splits][m][n]) and a second kernel adds
@@ -345,6 +366,17 @@ qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float*
 qlin_status qlin_gemm_w4a4_geglu(const void* xq, const float* x_scale, const void* wq,
                                  const float* w_scale, int64_t m, int64_t n2, int64_t k, void* h,
                                  qlin_dtype h_dtype, void* stream);
+
+/*
+ * qlin_gemm_geglu -- qlin_gemm_w4a4_geglu for a given code storage: scheme
+ * QLIN_W4A4 (packed int4, identical to qlin_gemm_w4a4_geglu) or
+ * QLIN_W4A4_E2M3 (both operands in E2M3 storage, rows of 3k/4 bytes; the
+ * same h for the same codes).  Other schemes: QLIN_ERR_UNSUPPORTED.
+ * Arguments, results, preconditions and errors as qlin_gemm_w4a4_geglu.
+ */
+qlin_status qlin_gemm_geglu(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
+                            const float* w_scale, int64_t m, int64_t n2, int64_t k, void* h,
+                            qlin_dtype h_dtype, void* stream);
 
 /*
  * qlin_gemv_w4a16 -- weight-only int4 projection for small batches (LoopQ

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
               "qlin_status_string", "qlin_calibrate_step_scales", "qlin_rotate_quant_act_static",
               "qlin_quantize_weights_step", "qlin_calibrate_composite", "qlin_rotate_quant_act_composite",
               "qlin_quantize_weights_composite", "qlin_calibrate_composite_work_bytes", "qlin_gemm_ws",
-              "qlin_gemm_workspace_bytes"):
+              "qlin_gemm_workspace_bytes", "qlin_gemm_static_ws", "qlin_gemm_geglu"):
         assert n in names
 
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qlin_abi_version() == 2
+    assert lib.qlin_abi_version() == 3
     for s in range(0, 11):
         assert lib.qlin_status_string(s).decode() not in ("", "unknown status")
     assert lib.qlin_status_string(99).decode() == "unknown status"
@@ -150,7 +150,9 @@ def test_gemm_workspace_bytes(lib):
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 52224, 2048, 16384) == 0    # large grid: no split
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 50, 1024, 4096) == 0        # small-M kernel: no split
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 192) == -1       # int4 k step is 128
-    assert lib.qlin_gemm_workspace_bytes(3, 816, 2048, 16384) == -1               # no such scheme
+    assert lib.qlin_gemm_workspace_bytes(4, 816, 2048, 16384) == -1               # no such scheme
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 16384) == 0  # E2M3 never splits
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 192) == -1
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 0, 2048, 16384) == 0
 
 
@@ -160,7 +162,7 @@ def gemm_ws(lib, scheme=q.QLIN_W8A8, xq=P, sx=P3, wq=P2, sw=P4, m=DOWN["m"], n=D
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(scheme=3), q.QLIN_ERR_UNSUPPORTED), (dict(scheme=-1), q.QLIN_ERR_UNSUPPORTED),
+    (dict(scheme=4), q.QLIN_ERR_UNSUPPORTED), (dict(scheme=-1), q.QLIN_ERR_UNSUPPORTED),
     (dict(ws=None), q.QLIN_ERR_NULL),                      # bytes > 0 with no buffer
     (dict(wsb=-16), q.QLIN_ERR_SHAPE), (dict(ws=0x7C000008), q.QLIN_ERR_ALIGN),
     (dict(wsb=1024), q.QLIN_ERR_WORKSPACE),                # smaller than the split plan needs
@@ -214,6 +216,57 @@ def test_gemm_geglu_rejects(lib, kw, status):
 
 def test_gemm_geglu_empty_is_ok(lib):
     assert lib.qlin_gemm_w4a4_geglu(None, None, P2, P4, 0, 128, 512, 0x70000000, 1, None) == q.QLIN_OK
+
+
+# ---- E2M3 storage of int4-grid codes (bits QLIN_BITS_E2M3, scheme QLIN_W4A4_E2M3)
+
+def test_e2m3_quantizers_take_k_in_multiples_of_128(lib):
+    e = q.QLIN_BITS_E2M3
+    # k = 576: a multiple of 8 and of the Hadamard block, not of 128
+    assert rqa(lib, bits=e, m=0, k=576, ldx=576) == q.QLIN_ERR_SHAPE
+    assert rqa(lib, bits=e, m=0) == q.QLIN_OK
+    assert qw(lib, bits=e, k=576) == q.QLIN_ERR_SHAPE
+    assert qw(lib, bits=e, group=128, b=0) == q.QLIN_ERR_UNSUPPORTED
+    assert lib.qlin_rotate_quant_act_static(None, 0, 0, 576, 576, None, 64, e, P3, None, None) == q.QLIN_ERR_SHAPE
+    assert lib.qlin_rotate_quant_act_static(None, 0, 0, 512, 512, None, 64, e, P3, None, None) == q.QLIN_OK
+    assert lib.qlin_rotate_quant_act_composite(None, 0, 0, 576, 576, None, P3, P4, 64, e, None, None, None,
+                                               None) == q.QLIN_ERR_SHAPE
+    assert lib.qlin_rotate_quant_act_composite(None, 0, 0, 512, 512, None, P3, P4, 64, e, None, None, None,
+                                               None) == q.QLIN_OK
+
+
+def test_e2m3_code_bytes_in_alias_checks(lib):
+    # m = 4 rows of k = 512 codes: 4 x 384 bytes in E2M3 (4 x 256 as packed int4)
+    e = q.QLIN_BITS_E2M3
+    assert rqa(lib, bits=e, xq=P2, xs=P2 + 4 * 384 - 16) == q.QLIN_ERR_ALIAS
+    assert rqa(lib, bits=4, xq=P2, xs=P2 + 4 * 384 - 16) != q.QLIN_ERR_ALIAS
+    # weights: 8 rows x 384 bytes
+    assert qw(lib, bits=e, wq=P2, ws=P2 + 8 * 384 - 16) == q.QLIN_ERR_ALIAS
+
+
+def test_gemm_e2m3_validation(lib):
+    e = q.QLIN_W4A4_E2M3
+    assert gemm_ws(lib, scheme=e, k=192, ws=None, wsb=0) == q.QLIN_ERR_SHAPE
+    assert gemm_ws(lib, scheme=e, m=0, ws=None, wsb=0) == q.QLIN_OK
+    # y overlapping the last bytes of xq (m rows of 3k/4 bytes) is an alias; just past them it is not
+    m, k = 16, 512
+    assert gemm_ws(lib, scheme=e, m=m, k=k, y=P + m * k * 3 // 4 - 16, ws=None, wsb=0) == q.QLIN_ERR_ALIAS
+    assert gemm_ws(lib, scheme=e, m=m, k=k, y=P + m * k * 3 // 4, ws=None, wsb=0) != q.QLIN_ERR_ALIAS
+    assert lib.qlin_gemm_static_ws(e, P, P3, P2, P4, 0, 2048, 16384, 0x70000000, 1, None) == q.QLIN_OK
+
+
+@pytest.mark.parametrize("scheme,status", [(q.QLIN_W4A4, q.QLIN_OK), (q.QLIN_W4A4_E2M3, q.QLIN_OK),
+                                           (q.QLIN_W8A8, q.QLIN_ERR_UNSUPPORTED), (7, q.QLIN_ERR_UNSUPPORTED)])
+def test_gemm_geglu_schemes(lib, scheme, status):
+    assert lib.qlin_gemm_geglu(scheme, None, None, P2, P4, 0, 128, 512, 0x70000000, 1, None) == status
+
+
+def test_gemm_geglu_e2m3_shapes(lib):
+    e = q.QLIN_W4A4_E2M3
+    assert lib.qlin_gemm_geglu(e, P, P3, P2, P4, 16, 96, 512, 0x70000000, 1, None) == q.QLIN_ERR_SHAPE
+    assert lib.qlin_gemm_geglu(e, P, P3, P2, P4, 16, 128, 192, 0x70000000, 1, None) == q.QLIN_ERR_SHAPE
+    # h overlapping the E2M3 weights (128 rows x 384 bytes)
+    assert lib.qlin_gemm_geglu(e, P, P3, P2, P4, 16, 128, 512, P2 + 128 * 384 - 16, 1, None) == q.QLIN_ERR_ALIAS
 
 
 # ---- qlin_gemv_w4a16(x, wq, ws, m, n, k, group, y, stream)
