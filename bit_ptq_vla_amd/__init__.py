@@ -17,7 +17,10 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlin.so")
+# QLIN_LIB_PATH selects another build of the library with the same entry
+# points (the host-only sanitizer build of the argument validation is tested
+# this way); by default the in-tree libqlin.so.
+LIB_PATH = os.environ.get("QLIN_LIB_PATH") or os.path.join(_HERE, "libqlin.so")
 
 QLIN_OK = 0
 QLIN_ERR_NULL = 1

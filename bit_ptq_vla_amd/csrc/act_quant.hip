@@ -864,20 +864,6 @@ __global__ void fold_finish_kernel(float* s, float* inv_s, int64_t k) {
 // ---- host launchers ----------------------------------------------------------
 
 // Compute units of the current device (cached per device).
-int device_cus() {
-    static std::mutex mu;
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
-}
-
 namespace {
 
 template <int DT, int NCH, bool GEGLU, int TPB, int MODE = ROWQ_DYNAMIC>

@@ -474,9 +474,6 @@ hipError_t launch_calibrate_composite(const void* w, int dtype, int64_t n, int64
     return hipGetLastError();
 }
 
-int64_t composite_calib_work_bytes(int64_t n, int64_t k, int b) {
-    const int64_t chunks = (n + 255) / 256;
-    return (chunks * k + k + k * b) * 8;
-}
+
 
 }  // namespace qlin

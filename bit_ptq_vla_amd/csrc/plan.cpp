@@ -1,0 +1,113 @@
+// Host-side planning of the qlin kernels: the device's compute-unit count,
+// the GEMM tile / split-K plans and the composite calibration's scratch size.
+// Plain C++ over the HIP runtime API (no device code), so that the argument
+// validation of the C ABI can be built and tested without the kernels.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <mutex>
+
+#include "qlin_internal.h"
+
+namespace qlin {
+
+namespace {
+constexpr int STAGE_BYTES = 64;   // bytes of one row per pipeline stage of the integer GEMM
+}  // namespace
+
+int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool allow_split) {
+    // 128-row tiles, 256 columns wide when N is large (fewer L2 -> LDS bytes
+    // per MFMA), two blocks per CU (one block's per-stage barrier and LDS
+    // latency is covered by the other block's MFMAs).
+    // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per
+    // CU; so does W4A8, whose 128 x 256 stage would not leave room for 3 stages.)
+    GemmPlan g;
+    const int64_t cus = device_cus();
+    const int64_t kbytes = int4 ? k / 2 : k;
+    const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
+    g.group_m = 0;
+    // int8 activations with enough 256 x 256 tiles for every CU: one block per
+    // CU, each wave a 128 x 128 accumulator tile (half the LDS bytes per MFMA of
+    // a 64 x 128 wave tile), tiles in 4-row groups.  (W4A4 stays on the two-
+    // blocks-per-CU tiles below: its int4 unpack and epilogue VALU work is
+    // covered there by the co-resident block's MFMAs; measured 45.6% against
+    // 40.7% of the int8 peak for the 52224 x 32768 x 2048 gate|up GEMM.)
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles256 >= cus && (!int4 || a8)) {
+        g.bm = g.bn = 256;
+        g.splits = 1;
+        g.deep = false;
+        g.group_m = 4;
+        g.ws_bytes = 0;
+        return g;
+    }
+    g.bm = 128;
+    g.bn = (n >= 4096 && int4 && !a8) ? 256 : 128;
+    const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
+    const int64_t slots = 2 * cus;   // two resident blocks per CU
+    int splits = 1;
+    // split K only when the tile grid fills under half of the block slots,
+    // keeping at least 16 stages (1 KiB of k per row) in every split
+    if (allow_split && tiles * 2 <= slots) {
+        while (tiles * splits * 2 <= slots && stages / (splits * 2) >= 16) splits *= 2;
+    }
+    // int8 x int8 with few tiles: the largest split that still gives every
+    // block a CU of its own (the deep ring below), when it fills at least 3/4
+    // of the CUs.  At 816 x 2048 x 16384 that is two splits on 224 CUs: the
+    // GEMM takes the time of four splits at two blocks per CU (38.1 us) and
+    // the reduction reads half the partials (4.8 us instead of 7.2 us).
+    if (allow_split && !int4 && !a8) {
+        int deep_splits = 1;
+        while (tiles * deep_splits * 2 <= cus && stages / (deep_splits * 2) >= 16) deep_splits *= 2;
+        if (deep_splits >= 2 && tiles * deep_splits * 4 >= cus * 3 && tiles * splits > cus) splits = deep_splits;
+    }
+    g.splits = splits;
+    // Many rounds of tiles: groups of 8 tile rows (see gemm_i8_kernel's tile order)
+    if (tiles * splits >= 2 * slots) g.group_m = 8;
+    // A grid of at most one block per CU gets the whole LDS for a deeper ring:
+    // with one wave per SIMD nothing else covers the DMA latency.
+    g.deep = tiles * splits <= cus;
+    g.ws_bytes = (splits > 1) ? static_cast<int64_t>(splits) * m * n * 4 : 0;
+    return g;
+}
+
+GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k) {
+    (void)k;
+    GemmPlan g;
+    const int64_t cus = device_cus();
+    g.splits = 1;
+    g.deep = false;
+    g.ws_bytes = 0;
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles256 >= cus) {   // at least one 256 x 256 tile per CU
+        g.bm = g.bn = 256;
+        g.group_m = 4;
+        return g;
+    }
+    g.bm = g.bn = 128;
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    g.group_m = tiles >= 4 * cus ? 8 : 0;
+    return g;
+}
+
+int64_t composite_calib_work_bytes(int64_t n, int64_t k, int b) {
+    const int64_t chunks = (n + 255) / 256;
+    return (chunks * k + k + k * b) * 8;
+}
+
+}  // namespace qlin

@@ -2,7 +2,7 @@
 // device check, launch, and HIP error mapping.  Declarations and the meaning
 // of every argument are in include/qlin.h.
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdint>
 #include <cstring>

@@ -1,7 +1,7 @@
 // Internal launchers of the qlin library (host side).  Not part of the ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace qlin {

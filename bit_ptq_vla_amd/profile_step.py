@@ -7,7 +7,8 @@ Two parts:
              traffic counters), then a few repetitions of one workload:
                mlp     the M = 816 backbone MLP block step
                sweep   one layer of the 18-layer backbone sweep at --m tokens
-               gemm    integer GEMMs at the sweep shapes (--m tokens)
+               gemm    integer GEMMs at the sweep shapes (--m tokens); the
+                       *_e2m3 ones take codes from the E2M3 quantizers
                gemv    the batch-1 W4A16 GEMVs of a 7B-decoder layer, weight
                        copies cycled so that the weights stream from HBM
   summarize  reads the FETCH_SIZE and WRITE_SIZE collections of two such runs
@@ -74,6 +75,7 @@ def _copy_reference(dev):
 SWEEP_GEMMS = {  # name: (n, k, scheme) of the sweep's projections
     "qkv": (6144, 2048, "w4a4"), "o": (2048, 2048, "w8a8"), "gate_up": (32768, 2048, "geglu"),
     "down": (2048, 16384, "w8a8"), "gate_up_w4a8": (32768, 2048, "w4a8"),
+    "qkv_e2m3": (6144, 2048, "e2m3"), "gate_up_e2m3": (32768, 2048, "geglu_e2m3"),
 }
 
 
@@ -101,6 +103,22 @@ def run(workload: str, steps: int, m: int, gemms) -> None:
 
         for name in gemms:
             n, k, sch = SWEEP_GEMMS[name]
+            if sch in ("e2m3", "geglu_e2m3"):
+                # E2M3 codes from the library's quantizers on synthetic rows
+                x = synth.device_normal(0, f"prof/x/{name}", (m, k), dev, dtype="bf16")
+                w = synth.device_normal(0, f"prof/w/{name}", (n, k), dev, std=0.02, dtype="f16")
+                xq, xs = q.qlin_rotate_quant_act(x, had_block=128, bits=q.QLIN_BITS_E2M3)
+                wq, ws = q.qlin_quantize_weights(w, had_block=128, bits=q.QLIN_BITS_E2M3)
+                del x, w
+                for _ in range(steps):
+                    if sch == "geglu_e2m3":
+                        q.qlin_gemm_geglu(q.QLIN_W4A4_E2M3, xq, xs, wq, ws, k)
+                    else:
+                        q.qlin_gemm_e2m3(xq, xs, wq, ws, k)
+                torch.cuda.synchronize()
+                del xq, wq
+                torch.cuda.empty_cache()
+                continue
             abits = 8 if sch in ("w8a8", "w4a8") else 4
             wbits = 8 if sch == "w8a8" else 4
             a = synth.device_normal(0, f"prof/a/{name}", (m, k), dev).clamp(-7, 7).round().to(torch.int8)

@@ -94,7 +94,8 @@ E2M3_BIG = [
     (4100, 4000, 512),   # 17 x 16 tiles
     (4352, 4096, 384),   # three k-stages, padded to four
     (6528, 2560, 1024),  # the last tile row half empty
-    (4096, 4352, 128),   # one k-stage
+    (4096, 4352, 128),   # one k-stage, padded to two
+    (8100, 8000, 256),   # 32 x 32 tiles, ragged M and N edges
 ]
 
 
