@@ -7,9 +7,10 @@
 //   v[c'] = x[perm[c']] * mult[perm[c']]            (gather, optional fold)
 //   v[B_j] = v[B_j] @ R_j                           (b x b rotation per block)
 //   per-row symmetric quantization of v (scale = max |v| / qmax, RNE codes).
-// The rotation is a dense product: dot products of b terms, fp32 operands
-// with exact fp64 products and an fp64 sum, rounded to fp32 once.  One kernel
-// applies block j's rotation (staged in LDS once) to a tile of rows and
+// The rotation is a dense product: dot products of b terms of fp32 operands,
+// on the matrix cores with fp32 accumulation for b >= 32 (within
+// gamma_b sum |x| |R| of the exact product), as fp64 sums rounded to fp32
+// for b = 16.  One kernel applies block j's rotation to a tile of rows and
 // writes the rotated rows (fp32) to a workspace; the row quantizer of the
 // Hadamard path then quantizes them as they stand (no fold, no rotation).
 //
@@ -161,6 +162,96 @@ __global__ __launch_bounds__(256) void composite_rotate_kernel(CompParams p) {
             *reinterpret_cast<float4*>(p.v + row * p.k + static_cast<int64_t>(j) * B + c0 + 4 * cg) =
                 make_float4(static_cast<float>(acc[u][0]), static_cast<float>(acc[u][1]),
                             static_cast<float>(acc[u][2]), static_cast<float>(acc[u][3]));
+    }
+}
+
+// The same rotation on the matrix cores (b = 32, 64, 128): fp32 operands,
+// v_mfma_f32_32x32x2_f32 with fp32 accumulation.  A workgroup of four waves
+// covers 32 * 4 / (b / 32) rows of block j; each wave one 32 x 32 output tile
+// (b / 32 column tiles side by side, 128 / b row tiles).  The gathered,
+// folded rows are staged in LDS (pitch b + 4 floats: the 16 lanes of a
+// ds_read_b128 reach 16 distinct 16-byte bank groups); a wave's 32 columns
+// of R_j are loaded into registers once.  MFMA step s pairs channel
+// 8 (s / 4) + 4 h + s % 4 of both operands for lane half h, so a lane reads
+// four consecutive channels of its row per four steps; the steps feed four
+// accumulators in turn (independent MFMA chains), added pairwise at the end.
+// Each output is thus a sum of b fp32 products with at most b fp32
+// roundings: within gamma_b * sum_i |x_i| |R_ij| of the exact product of the
+// fp32 operands (gamma_n = n u / (1 - n u), u = 2^-24).
+typedef float v16f_c __attribute__((ext_vector_type(16)));
+
+template <int DT, int B>
+__global__ __launch_bounds__(256) void composite_rotate_mfma_kernel(CompParams p) {
+    static_assert(B == 32 || B == 64 || B == 128, "32 x 32 output tiles");
+    constexpr int NC = B / 32;            // column tiles
+    constexpr int NR = 4 / NC;            // row tiles
+    constexpr int RT = 32 * NR;           // rows per workgroup
+    constexpr int P = B + 4;              // LDS row pitch, floats
+    constexpr int STEPS = B / 2;          // MFMA steps (two channels each)
+    __shared__ __attribute__((aligned(16))) float xs[RT * P];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = blockIdx.x;
+    const int k = static_cast<int>(p.k);
+    const int64_t row0 = static_cast<int64_t>(blockIdx.y) * RT;
+    const int ct = wave % NC, rt = wave / NC;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // this wave's columns of R_j: rv[s] = R_j[c(s, h)][32 ct + l32]
+    float rv[STEPS];
+    {
+        const float* rj = p.rot + static_cast<int64_t>(j) * B * B + 32 * ct + l32;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) rv[s] = rj[(8 * (s / 4) + 4 * h + (s % 4)) * B];
+    }
+    // gathered, folded rows: thread -> channel i = tid % B of rows tid / B + (256 / B) u
+    {
+        constexpr int RS = 256 / B;
+        constexpr int NU = RT * B / 256;
+        const int i = tid % B, r0 = tid / B;
+        int sidx = p.perm[j * B + i];
+        sidx = sidx < 0 ? 0 : (sidx >= k ? k - 1 : sidx);   // (a valid permutation never clamps)
+        const float f = p.mult ? p.mult[sidx] : 1.f;
+        const char* xb = static_cast<const char*>(p.x);
+        const int64_t pitch = p.ldx * (DT == F32 ? 4 : 2);
+        float xv[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int64_t row = row0 + r0 + RS * u;
+            xv[u] = load1<DT>(xb + (row < p.m ? row : 0) * pitch, sidx);
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int64_t row = row0 + r0 + RS * u;
+            xs[(r0 + RS * u) * P + i] = row < p.m ? mul_rn(xv[u], f) : 0.f;
+        }
+    }
+    __syncthreads();
+    // four independent accumulator chains (steps s % 4), added at the end
+    v16f_c acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    const float* xr = xs + (32 * rt + l32) * P + 4 * h;
+#pragma unroll
+    for (int t = 0; t < STEPS / 4; ++t) {
+        const float4 a4 = *reinterpret_cast<const float4*>(xr + 8 * t);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, rv[4 * t + 0], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, rv[4 * t + 1], acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, rv[4 * t + 2], acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, rv[4 * t + 3], acc[3], 0, 0, 0);
+    }
+    v16f_c sum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum[r] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+    // acc: column 32 ct + l32 of block j, rows 8 (r / 4) + 4 h + r % 4 of the row tile
+    float* vcol = p.v + static_cast<int64_t>(j) * B + 32 * ct + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + 32 * rt + 8 * (r / 4) + 4 * h + (r % 4);
+        if (row < p.m) vcol[row * p.k] = sum[r];
     }
 }
 
@@ -403,13 +494,22 @@ hipError_t launch_rot_rpt(const CompParams& p, hipStream_t st) {
     return launch_rot_b<DT, B, 1>(p, st);
 }
 
+template <int DT, int B>
+hipError_t launch_rot_mfma(const CompParams& p, hipStream_t st) {
+    constexpr int RT = 32 * (4 / (B / 32));
+    dim3 grid(static_cast<unsigned>(p.k / B), static_cast<unsigned>((p.m + RT - 1) / RT));
+    hipLaunchKernelGGL((composite_rotate_mfma_kernel<DT, B>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// b >= 32 on the matrix cores; b = 16 (too narrow for a 32 x 32 tile) as fp64 sums
 template <int DT>
 hipError_t launch_rot_dt(const CompParams& p, hipStream_t st) {
     switch (p.b) {
         case 16: return launch_rot_rpt<DT, 16>(p, st);
-        case 32: return launch_rot_rpt<DT, 32>(p, st);
-        case 64: return launch_rot_rpt<DT, 64>(p, st);
-        case 128: return launch_rot_rpt<DT, 128>(p, st);
+        case 32: return launch_rot_mfma<DT, 32>(p, st);
+        case 64: return launch_rot_mfma<DT, 64>(p, st);
+        case 128: return launch_rot_mfma<DT, 128>(p, st);
     }
     return hipErrorInvalidValue;
 }

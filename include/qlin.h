@@ -214,9 +214,12 @@ qlin_status qlin_quantize_weights_step(const void* w, qlin_dtype w_dtype, int64_
  * then quantized per row (x_scale / w_scale = fp32(max |v| / qmax), codes
  * clamp(rne(v / scale), +-qmax), layouts as the Hadamard entry points; codes
  * are in the permuted channel order on both sides, so the GEMM is unchanged).
- * The dot products take fp32 operands with an fp64 sum, rounded to fp32;
- * the rotated rows pass through the caller's fp32 scratch `work` (device,
- * 16-byte aligned, rows * k floats, contents overwritten; required).
+ * Arithmetic: v[c'] is the fp32 product; for b >= 32 the dot products of b
+ * fp32 terms run on the matrix cores with fp32 accumulation, each within
+ * gamma_b * sum_i |v_i| |R_ij| of the exact product of its fp32 operands
+ * (gamma_n = n u / (1 - n u), u = 2^-24); for b = 16 they are fp64 sums
+ * rounded to fp32.  The rotated rows (fp32) are left in the caller's scratch
+ * `work` (device, 16-byte aligned, rows * k floats; required).
  *
  * qlin_calibrate_composite -- perm and R from the weights w [n][k] (times
  *   fold_s): channels ranked by descending L2 norm of their column (lower

@@ -217,10 +217,51 @@ def _composite_weights(n, k, dtype, tag):
     return (w.float() * spread[None, :]).to(w.dtype)
 
 
+U32 = 2.0 ** -24
+
+
+def _composite_bounded(v_gpu, q_gpu, s_gpu, vin, perm, rot, bits, what):
+    """The composite path's results against the oracle within the stated
+    error bound: every rotated value within
+        E = (gamma_b + 3u) sum_i |v_i| |R_ij| + u |v_ref|,   u = 2^-24,
+    of the exact product of the oracle's fold (gamma_b: b fp32 roundings of
+    the matrix-core sum; 3u: the fp32 fold product and 1/s; u |v|: the final
+    fp32 rounding of the b = 16 path's fp64 sum); scales within the row's
+    largest E over qmax (+2 ulp); a code differing by at most one, and only
+    where the oracle's quotient lies within the propagated bound of a
+    rounding boundary (half-integer)."""
+    b = rot.shape[-1]
+    qmax = oracle.qmax_of(bits)
+    gamma = b * U32 / (1 - b * U32)
+    v_ref = oracle.rotate_composite(vin, perm, rot)
+    mag = oracle.rotate_composite(np.abs(vin), perm, np.abs(rot.astype(np.float64)))
+    bound = (gamma + 3 * U32) * mag + U32 * np.abs(v_ref) + 1e-30
+    dv = np.abs(v_gpu.astype(np.float64) - v_ref)
+    worst = np.max(dv / bound)
+    assert worst <= 1.0, f"{what}: rotated value off by {worst:.3f} x the bound"
+    q_ref, s_ref, r_ref = oracle.quantize_rows(v_ref, bits)
+    row_e = np.max(bound, axis=1)
+    s64 = s_gpu.astype(np.float64)
+    assert np.all(np.abs(s64 - s_ref) <= row_e / qmax + 2 * U32 * s_ref + 1e-45), f"{what}: scale beyond the bound"
+    d = q_gpu.astype(np.int64) - q_ref
+    assert np.max(np.abs(d)) <= 1, f"{what}: a code differs by more than one"
+    zero = s_ref == 0                      # all-zero rows: scale 0 and codes 0 on both sides
+    assert np.all(s64[zero] == 0) and not np.any(q_gpu[zero]), f"{what}: zero row not quantized to zeros"
+    if np.any(d):
+        sref = np.where(zero, 1.0, s_ref)[:, None]
+        tol = bound / sref + np.abs(r_ref) * (row_e[:, None] / (sref * qmax) + 4 * U32)
+        tol = np.maximum(tol, 1e-5 * np.maximum(1.0, np.abs(r_ref)))   # the quantizer's own tie window
+        dist = np.abs(np.abs(r_ref - np.floor(r_ref)) - 0.5)
+        far = (d != 0) & (dist > tol)
+        assert not np.any(far), f"{what}: {int(np.count_nonzero(far))} code flips away from a rounding boundary"
+    return int(np.count_nonzero(d))
+
+
 @pytest.mark.parametrize("m,k,b,bits,dtype,fold", COMPOSITE_CASES)
 def test_composite_quant_parity(m, k, b, bits, dtype, fold):
     """Activations and weights with the oracle's permutation and rotations
-    (fp32) as inputs: codes and scales against the oracle."""
+    (fp32) as inputs: rotated rows, scales and codes against the oracle within
+    the stated error bound of the rotation's arithmetic."""
     say(f"composite quant m={m} k={k} b={b} bits={bits} {dtype}")
     x = synth.normal_tensor(SEED, f"cx/{m}/{k}", (m, k), dtype=dtype, outliers=max(1, k // 100), outlier_scale=25.0)
     x[m // 2] = 0
@@ -232,16 +273,18 @@ def test_composite_quant_parity(m, k, b, bits, dtype, fold):
     rot = oracle.composite_rotations(wf, perm, b).astype(np.float32)
     pd, rd = torch.from_numpy(perm.astype(np.int32)).to(DEV), torch.from_numpy(rot).to(DEV)
     inv = (1.0 / s).to(DEV) if fold else None
-    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), pd, rd, fold_inv_s=inv, bits=bits)
-    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), pd, rd, fold_s=s.to(DEV) if fold else None, bits=bits)
+    xwork = torch.empty(m * k, dtype=torch.float32, device=DEV)
+    wwork = torch.empty(64 * k, dtype=torch.float32, device=DEV)
+    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), pd, rd, fold_inv_s=inv, bits=bits, work=xwork)
+    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), pd, rd, fold_s=s.to(DEV) if fold else None, bits=bits,
+                                               work=wwork)
     torch.cuda.synchronize()
-    qx_ref, sx_ref, rx = oracle.rotate_quant_act_composite(synth.to_f64(x), sg, perm, rot, bits)
-    assert_ok(oracle.compare_scales(xs.cpu().numpy(), sx_ref), "act scales")
-    assert_ok(oracle.compare_codes(codes_np(xq, bits), qx_ref, rx), "act codes")
+    xin = synth.to_f64(x) / (sg.astype(np.float64)[None, :] if fold else 1.0)
+    _composite_bounded(xwork.view(m, k).cpu().numpy(), codes_np(xq, bits), xs.cpu().numpy(), xin, perm, rot, bits,
+                       "activations")
     assert xs[m // 2].item() == 0.0
-    qw_ref, sw_ref, rw = oracle.quantize_weights_composite(synth.to_f64(w), sg, perm, rot, bits)
-    assert_ok(oracle.compare_scales(ws.cpu().numpy(), sw_ref), "weight scales")
-    assert_ok(oracle.compare_codes(codes_np(wq, bits), qw_ref, rw), "weight codes")
+    _composite_bounded(wwork.view(64, k).cpu().numpy(), codes_np(wq, bits), ws.cpu().numpy(), wf, perm, rot, bits,
+                       "weights")
 
 
 @pytest.mark.parametrize("n,k,b,dtype,fold", [(96, 1024, 64, "f16", True), (256, 2048, 128, "bf16", True),
@@ -289,17 +332,18 @@ def test_composite_linear_end_to_end():
     w = synth.weight(wl, pr)
     x = synth.activation(wl, pr, 50, tag="/t0", std=synth.cfg3_sigma(0))
     perm, rot = q.qlin_calibrate_composite(w.to(DEV), 64)
-    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), perm, rot, bits=4)
-    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), perm, rot, bits=4)
+    xwork = torch.empty(50 * pr.k, dtype=torch.float32, device=DEV)
+    wwork = torch.empty(pr.n * pr.k, dtype=torch.float32, device=DEV)
+    xq, xs = q.qlin_rotate_quant_act_composite(x.to(DEV), perm, rot, bits=4, work=xwork)
+    wq, ws = q.qlin_quantize_weights_composite(w.to(DEV), perm, rot, bits=4, work=wwork)
     y = q.qlin_gemm_w4a4(xq, xs, wq, ws, pr.k, y_dtype=torch.float16)
     torch.cuda.synchronize()
     pg, rg = perm.cpu().numpy().astype(np.int64), rot.cpu().numpy()
-    qx_ref, sx_ref, rx = oracle.rotate_quant_act_composite(synth.to_f64(x), None, pg, rg, 4)
-    assert_ok(oracle.compare_codes(codes_np(xq, 4), qx_ref, rx), "act codes")
-    assert_ok(oracle.compare_scales(xs.cpu().numpy(), sx_ref), "act scales")
+    _composite_bounded(xwork.view(50, pr.k).cpu().numpy(), codes_np(xq, 4), xs.cpu().numpy(), synth.to_f64(x), pg,
+                       rg, 4, "activations")
     rws = _sample_rows(pr.n, 32)
-    qw_ref, sw_ref, rw = oracle.quantize_weights_composite(synth.to_f64(w[rws]), None, pg, rg, 4)
-    assert_ok(oracle.compare_codes(codes_np(wq, 4)[rws], qw_ref, rw), "weight codes")
+    _composite_bounded(wwork.view(pr.n, pr.k).cpu().numpy()[rws], codes_np(wq, 4)[rws], ws.cpu().numpy()[rws],
+                       synth.to_f64(w[rws]), pg, rg, 4, "weights")
     _, _, y_ref = oracle.gemm(codes_np(xq, 4), xs.cpu().numpy(), codes_np(wq, 4), ws.cpu().numpy(), "f16")
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
     y_true = synth.to_f64(x) @ synth.to_f64(w).T
