@@ -50,10 +50,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+FP6_PEAK_TOPS = 10100.0   # MI355X dense fp6 / fp4 MFMA, 10.1 POP/s
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 # FETCH_SIZE / WRITE_SIZE summary of the sweep's kernels and the gate|up GEMM's name in it
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_sweep_m52224.txt")
-GATE_UP_TAG = "gemm_geglu"
+# the gate|up GEMM with the GeGLU epilogue (bf16 h) at the sweep's M, in the traffic summary
+GATE_UP_TAG = "gemm_i8_kernel<128,256,2,3,true,17,"
 
 
 _T0 = time.perf_counter()
@@ -413,6 +415,47 @@ def w4a8_leg(block, reps=20):
             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
+def e2m3_leg(dev, m=52224, reps=3):
+    """The sweep's W4A4 GEMMs at M = 52224 with the codes in E2M3 storage (the
+    int4 grid as FP6 values, on the FP6 matrix cores) beside the packed-int4
+    path on the same inputs: q|k|v 52224 x 6144 x 2048 and gate|up 52224 x
+    32768 x 2048 with the GeGLU epilogue; codes from the quantizers (b = 128)
+    of synthetic rows.  Rates against the int8 peak and the fp6 peak."""
+    import torch
+
+    import bit_ptq_vla_amd as q
+    from bit_ptq_vla_amd import synth
+
+    k = 2048
+    x = synth.device_normal(7, "e2m3/x", (m, k), dev, dtype="bf16", outliers=k // 100, outlier_scale=30.0)
+    xq = {b: q.qlin_rotate_quant_act(x, had_block=128, bits=b) for b in (4, q.QLIN_BITS_E2M3)}
+    del x
+    res = {"m": m, "timing": "median of 5 trials"}
+    for name, n, geglu in (("qkv", 6144, False), ("gate_up", 32768, True)):
+        w = synth.device_normal(7, f"e2m3/w/{name}", (n, k), dev, std=0.02, dtype="f16")
+        wq = {b: q.qlin_quantize_weights(w, had_block=128, bits=b) for b in (4, q.QLIN_BITS_E2M3)}
+        del w
+        y = torch.empty((m, n // 2 if geglu else n), dtype=torch.bfloat16, device=dev)
+        r = {}
+        for tag, b in (("int4", 4), ("e2m3", q.QLIN_BITS_E2M3)):
+            (a, sx), (bq, sw) = xq[b], wq[b]
+            scheme = q.QLIN_W4A4 if b == 4 else q.QLIN_W4A4_E2M3
+            if geglu:
+                fn = lambda: q.qlin_gemm_geglu(scheme, a, sx, bq, sw, k, out=y)
+            elif b == 4:
+                fn = lambda: q.qlin_gemm_w4a4(a, sx, bq, sw, k, out=y)
+            else:
+                fn = lambda: q.qlin_gemm_e2m3(a, sx, bq, sw, k, out=y)
+            us = _median_us(fn, reps)
+            tops = 2 * m * n * k / (us * 1e-6) / 1e12
+            r[tag] = {"us": round(us, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                      "frac_fp6_peak": round(tops / FP6_PEAK_TOPS, 4)}
+        res[f"{name}_{m}x{n}x{k}"] = r
+        del wq, y
+        torch.cuda.empty_cache()
+    return res
+
+
 def decoder_m256_leg(dev, reps=5):
     """The 7B-decoder projections at M = 256, W8A8 per-token / per-channel
     (no fold, no rotation): int8 quantization of X and the integer GEMM for
@@ -483,7 +526,9 @@ def layer_p(layer):
 def gemv_leg(dev, reps=5):
     """Batch-1 W4A16 GEMV over a 7B-decoder layer; distinct weight copies
     (>= 512 MB in total) are cycled so that the weights stream from HBM.
-    Launches are replayed from a captured HIP graph."""
+    Launches are replayed from a captured HIP graph.  Beside each rate, the
+    streaming-read ceiling: the plain 16-byte read reference
+    (qlin_stream_read) over the same byte counts, launch for launch, cold."""
     import torch
 
     import bit_ptq_vla_amd as q
@@ -535,11 +580,44 @@ def gemv_leg(dev, reps=5):
         nbytes = n * k // 2 + n * (k // 128) * 2 + 2 * k + 2 * n
         shapes[f"{n}x{k}"] = {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                               "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    # streaming-read ceiling: the same byte counts read once by the plain
+    # 16-byte streaming-read reference, from cold slices of a 1 GiB buffer
+    del layers
+    torch.cuda.empty_cache()
+    buf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(q.QLIN_STREAM_READ_SINK_WORDS, dtype=torch.int32, device=dev)
+
+    def ceiling_gbs(sizes):
+        sizes = [(b + 15) // 16 * 16 for b in sizes]
+        offs, off = [], 0
+        for _ in range(copies):
+            for b in sizes:
+                if off + b > buf.numel():
+                    off = 0
+                offs.append((off, b))
+                off += (b + 255) // 256 * 256
+        gr = _graph(lambda: [q.qlin_stream_read(buf[o:o + b], b, sink=sink) for o, b in offs])
+        us = _median_us(gr.replay, reps) / copies
+        return sum(sizes) / (us * 1e-6) / 1e9
+
+    wbytes = {p.name: p.n * p.k // 2 + p.n * (p.k // 128) * 2 for p, _, _ in layer}
+    layer_ceil = ceiling_gbs([wbytes[p.name] for p, _, _ in layer])
+    merged_ceil = ceiling_gbs([sum(wbytes[nm] for nm in names) for names in
+                               (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))])
+    for key, v in shapes.items():
+        n, k = (int(t) for t in key.split("x"))
+        c = ceiling_gbs([n * k // 2 + n * (k // 128) * 2])
+        v["read_ceiling_GB/s"] = round(c, 1)
+        v["frac_of_read_ceiling"] = round(v["GB/s"] / c, 4)
+    del buf
     return {"workload": "decoder7b_layer_m1_w4a16_g128", "layer_MB": round(layer_bytes / 1e6, 2),
             "weight_copies": copies, "layer_us": round(layer_us, 2), "GB/s": round(layer_gbs, 1),
             "frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "timing": "HIP graph replay, cold weights, median of 5",
+            "read_ceiling_GB/s": round(layer_ceil, 1), "frac_of_read_ceiling": round(layer_gbs / layer_ceil, 4),
             "merged_qkv_gate_up": {"launches": 4, "layer_us": round(merged_us, 2), "GB/s": round(merged_gbs, 1),
-                                   "frac_hbm": round(merged_gbs / HBM_PEAK_GBS, 4)},
+                                   "frac_hbm": round(merged_gbs / HBM_PEAK_GBS, 4),
+                                   "read_ceiling_GB/s": round(merged_ceil, 1),
+                                   "frac_of_read_ceiling": round(merged_gbs / merged_ceil, 4)},
             "shapes": shapes}
 
 
@@ -725,6 +803,8 @@ def main():
             log("bench: W4A8 GEMM leg")
             out["w4a8"] = leg("w4a8", lambda: w4a8_leg(block))
             del block
+        log("bench: E2M3 (FP6 matrix core) W4A4 GEMM leg")
+        out["w4a4_e2m3"] = leg("w4a4_e2m3", lambda: e2m3_leg(dev))
         log("bench: 7B-decoder M = 256 W8A8 leg")
         out["decoder7b_m256_w8a8"] = leg("decoder7b_m256_w8a8", lambda: decoder_m256_leg(dev))
         log("bench: action expert leg (M = 50, 10 steps)")

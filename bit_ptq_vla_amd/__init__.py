@@ -62,6 +62,7 @@ SIGNATURES = {
     "qlin_gemm_w4a4_geglu": [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemm_geglu": [_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I32, _P],
     "qlin_gemv_w4a16": [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _P],
+    "qlin_stream_read": [_P, _I64, _P, _P],
     "qlin_calibrate_step_scales": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P],
     "qlin_rotate_quant_act_static": [_P, _I32, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P],
     "qlin_quantize_weights_step": [_P, _I32, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P],
@@ -527,3 +528,23 @@ def qlin_gemv_w4a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, gr
                              _stream(x.device))
     _check(st, "qlin_gemv_w4a16")
     return y
+
+
+QLIN_STREAM_READ_SINK_WORDS = 4096
+
+
+def qlin_stream_read(src: torch.Tensor, nbytes: Optional[int] = None, sink: Optional[torch.Tensor] = None
+                     ) -> torch.Tensor:
+    """Streaming read of the first nbytes (default: all) of the contiguous
+    device tensor src (measurement aid); returns the sink words."""
+    lib = load()
+    _dev_tensor(src, "src")
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    _need(src, nbytes, "src")
+    if sink is None:
+        sink = torch.empty(QLIN_STREAM_READ_SINK_WORDS, dtype=torch.int32, device=src.device)
+    _need(sink, QLIN_STREAM_READ_SINK_WORDS * 4, "sink")
+    _check(lib.qlin_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src.device)), "qlin_stream_read")
+    return sink
+

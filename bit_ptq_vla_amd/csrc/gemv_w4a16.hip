@@ -277,6 +277,48 @@ hipError_t launch_ch(const void* x, const void* wq, const void* ws, int64_t m, i
 
 }  // namespace
 
+namespace {
+
+// Streaming-read reference: every byte of src read once with 16-byte loads,
+// UNR loads in flight per lane, xor-folded into one word per block (so the
+// loads are not dead).  bytes is a multiple of 16.
+constexpr int kReadUnroll = 4;
+__global__ __launch_bounds__(256) void stream_read_kernel(const v4i* src, int64_t words16, uint32_t* sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kReadUnroll - 1) * stride < words16; i += kReadUnroll * stride) {
+        v4i v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) acc ^= static_cast<uint32_t>(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
+    }
+    for (; i < words16; i += stride) {
+        const v4i v = __builtin_nontemporal_load(src + i);
+        acc ^= static_cast<uint32_t>(v.x ^ v.y ^ v.z ^ v.w);
+    }
+    __shared__ uint32_t red[4];
+    for (int o = 32; o > 0; o >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, hipStream_t st) {
+    const int64_t words16 = bytes / 16;
+    int64_t blocks = (words16 + 256 * kReadUnroll - 1) / (256 * kReadUnroll);
+    const int64_t cap = static_cast<int64_t>(device_cus()) * 8;
+    if (blocks > cap) blocks = cap;
+    if (blocks > sink_words) blocks = sink_words;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       static_cast<const v4i*>(src), words16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st) {
     (void)group;  // 128, checked by the caller

@@ -80,4 +80,8 @@ hipError_t launch_skinny_int(const void*, const float*, const void*, const float
     return hipErrorNoBinaryForGpu;
 }
 
+hipError_t launch_stream_read(const void*, int64_t, uint32_t*, int64_t, hipStream_t) {
+    return hipErrorNoBinaryForGpu;
+}
+
 }  // namespace qlin

@@ -498,6 +498,18 @@ qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, 
     return map_err(qlin::launch_gemv_w4a16(x, wq, w_scale, m, n, k, group, y, as_stream(stream)));
 }
 
+qlin_status qlin_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink) return QLIN_ERR_NULL;
+    if (bytes < 16 || (bytes % 16) != 0) return QLIN_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(sink)) return QLIN_ERR_ALIGN;
+    const Span outs[1] = {{sink, QLIN_STREAM_READ_SINK_WORDS * 4}};
+    const Span ins[1] = {{src, bytes}};
+    if (any_overlap(outs, 1, ins, 1)) return QLIN_ERR_ALIAS;
+    qlin_status st = check_device();
+    if (st != QLIN_OK) return st;
+    return map_err(qlin::launch_stream_read(src, bytes, sink, QLIN_STREAM_READ_SINK_WORDS, as_stream(stream)));
+}
+
 qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float* x_scale, const void* wq,
                                 const float* w_scale, int64_t m, int64_t n, int64_t k, void* y,
                                 qlin_dtype y_dtype, void* stream) {

@@ -93,6 +93,9 @@ hipError_t launch_gemm_f6(const GemmPlan& plan, const void* xq, const float* x_s
                           const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, int y_dtype, bool geglu,
                           hipStream_t st);
 
+// Streaming read of bytes (a multiple of 16) at src; one word per block to sink.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, hipStream_t st);
+
 hipError_t launch_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                              int64_t n, int64_t k, int group, void* y, hipStream_t st);
 

@@ -394,6 +394,23 @@ qlin_status qlin_gemm_geglu(qlin_scheme scheme, const void* xq, const float* x_s
 qlin_status qlin_gemv_w4a16(const void* x, const void* wq, const void* w_scale, int64_t m,
                             int64_t n, int64_t k, int32_t group, void* y, void* stream);
 
+/*
+ * qlin_stream_read -- measurement aid, not a step of the projection: reads
+ * `bytes` bytes at src once with 16-byte loads spread over the whole device
+ * and writes the xor of the words a workgroup read to sink (one uint32 per
+ * workgroup, at most QLIN_STREAM_READ_SINK_WORDS).  Its rate on the bytes a
+ * memory-bound call reads (the packed weights and scales of
+ * qlin_gemv_w4a16) is the streaming-read ceiling that call is compared with
+ * (LoopQ abstract: the batch-1 projections of the action expert are
+ * memory-bound).
+ *   src   device, 16-byte aligned; bytes a positive multiple of 16.
+ *   sink  device uint32[QLIN_STREAM_READ_SINK_WORDS], 16-byte aligned, not
+ *         overlapping src.
+ * Errors: QLIN_ERR_NULL, QLIN_ERR_SHAPE, QLIN_ERR_ALIGN, QLIN_ERR_ALIAS.
+ */
+#define QLIN_STREAM_READ_SINK_WORDS 4096
+qlin_status qlin_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
               "qlin_status_string", "qlin_calibrate_step_scales", "qlin_rotate_quant_act_static",
               "qlin_quantize_weights_step", "qlin_calibrate_composite", "qlin_rotate_quant_act_composite",
               "qlin_quantize_weights_composite", "qlin_calibrate_composite_work_bytes", "qlin_gemm_ws",
-              "qlin_gemm_workspace_bytes", "qlin_gemm_static_ws", "qlin_gemm_geglu"):
+              "qlin_gemm_workspace_bytes", "qlin_gemm_static_ws", "qlin_gemm_geglu", "qlin_stream_read"):
         assert n in names
 
 
@@ -422,3 +422,16 @@ def test_binding_raises_qlin_error(lib):
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass validation; the device check then fails cleanly (no GPU here)
     assert rqa(lib) == q.QLIN_ERR_DEVICE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), q.QLIN_ERR_NULL), (dict(sink=None), q.QLIN_ERR_NULL),
+    (dict(nbytes=0), q.QLIN_ERR_SHAPE), (dict(nbytes=4100), q.QLIN_ERR_SHAPE), (dict(nbytes=-16), q.QLIN_ERR_SHAPE),
+    (dict(src=BAD), q.QLIN_ERR_ALIGN), (dict(sink=BAD), q.QLIN_ERR_ALIGN),
+    (dict(sink=P + 1024), q.QLIN_ERR_ALIAS),
+])
+def test_stream_read_rejects(lib, kw, status):
+    a = dict(src=P, nbytes=4096, sink=P2)
+    a.update(kw)
+    assert lib.qlin_stream_read(a["src"], a["nbytes"], a["sink"], None) == status
+

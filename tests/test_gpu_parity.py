@@ -679,6 +679,20 @@ def test_gemv_w4a16_parity(m, n, k):
     assert_ok(oracle.compare_outputs(f64(y), y_ref), "output")
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 8 * 2 ** 20 + 256 * 1024, 46 * 2 ** 20 + 48])
+def test_stream_read_reads_every_word_once(nbytes):
+    """The streaming-read reference folds every 16-byte word it reads into
+    the sink by xor, so the xor of the sink equals the xor of the bytes read."""
+    say(f"stream read {nbytes} bytes")
+    g = torch.Generator().manual_seed(nbytes)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4 + 64,), dtype=torch.int32, generator=g)
+    sink = torch.zeros(q.QLIN_STREAM_READ_SINK_WORDS, dtype=torch.int32, device=DEV)
+    q.qlin_stream_read(src.to(DEV), nbytes, sink=sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src[: nbytes // 4].numpy())
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == want
+
+
 @pytest.mark.parametrize("m", [2, 20])
 def test_gemv_w4a16_subnormal_and_large_x(m):
     # fp16 subnormal, zero and near-maximum activations (the vector kernel folds a
