@@ -21,7 +21,7 @@ struct OncePerDevice {
 };
 hipError_t fill_once_per_device(OncePerDevice& once, hipStream_t caller, hipError_t (*fill)(hipStream_t));
 
-int row_quant_lanes(int64_t k);
+int row_quant_lanes(int64_t k, int64_t m);
 int row_quant_chunks(int64_t k, int g);
 
 hipError_t launch_rotate_quant(const void* x, int dtype, int64_t m, int64_t k, int64_t ldx,

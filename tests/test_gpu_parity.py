@@ -33,6 +33,8 @@ def say(msg):
 
 def codes_np(t: torch.Tensor, bits: int) -> np.ndarray:
     a = t.cpu().numpy()
+    if bits == 6:
+        return oracle.unpack_e2m3(a).astype(np.int64)
     return oracle.unpack_int4(a) if bits == 4 else a.astype(np.int64)
 
 
@@ -59,6 +61,11 @@ ACT_CASES = [
     (300, 256, 128, 4, "bf16", True),   # several rows per block
     (3, 14336, 128, 8, "bf16", True),   # 512 lanes, chunk count 4 (not a power-of-two row)
     (4, 32768, 128, 4, "bf16", True),   # longest rows: 1024 lanes, 4 chunks
+    # many rows (m * k >= 2^21): k / 32 lanes per row, four chunks each
+    (1030, 2048, 128, 4, "bf16", True),   # one wave per row, ragged row groups
+    (2049, 1024, 256, 8, "bf16", True),   # 32 lanes = one Hadamard block of 256
+    (513, 4096, 64, 6, "f16", True),      # E2M3 storage, 128 lanes
+    (1024, 2048, 128, 8, "f32", False),
 ]
 
 
@@ -75,13 +82,16 @@ def test_rotate_quant_act_parity(m, k, b, bits, dtype, fold):
     inv_s = (1.0 / s).to(DEV) if fold else None
     xq, xs = q.qlin_rotate_quant_act(xd, fold_inv_s=inv_s, had_block=b, bits=bits)
     torch.cuda.synchronize()
-    q_ref, s_ref, r_ref = oracle.rotate_quant_act(synth.to_f64(x), s.numpy() if fold else None, b, bits)
+    # E2M3 storage (bits 6) holds the codes of the int4 grid
+    q_ref, s_ref, r_ref = oracle.rotate_quant_act(synth.to_f64(x), s.numpy() if fold else None, b,
+                                                  4 if bits == 6 else bits)
     assert_ok(oracle.compare_scales(xs.cpu().numpy(), s_ref), "scales")
     assert_ok(oracle.compare_codes(codes_np(xq, bits), q_ref, r_ref), "codes")
     assert xs[m // 2].item() == 0.0 and np.all(codes_np(xq, bits)[m // 2] == 0)
 
 
-@pytest.mark.parametrize("m,k,dtype", [(9, 2048, "bf16"), (4, 16384, "bf16"), (6, 512, "f16")])
+@pytest.mark.parametrize("m,k,dtype", [(9, 2048, "bf16"), (4, 16384, "bf16"), (6, 512, "f16"),
+                                       (1100, 2048, "bf16"), (1030, 1024, "f16")])
 def test_rotate_quant_act_geglu_parity(m, k, dtype):
     say(f"act geglu m={m} k={k} {dtype}")
     gu = synth.normal_tensor(SEED, f"geglu/{m}/{k}", (m, 2 * k), dtype=dtype)
