@@ -1496,6 +1496,9 @@ hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scal
     } else if (plan.bn == 256) {
         if (!int4) return hipErrorInvalidValue;
         e = plan.deep ? launch_out<128, 256, 1, 6, true>(p, st) : launch_out<128, 256, 2, 3, true>(p, st);
+    } else if (plan.bm == 64) {
+        if (int4 || a8 || !plan.deep || plan.splits != 1) return hipErrorInvalidValue;
+        e = launch_out<64, 64, 1, 8, false>(p, st);
     } else if (plan.deep) {
         e = int4 ? launch_out<128, 128, 1, 8, true>(p, st) : launch_out<128, 128, 1, 8, false>(p, st);
     } else {

@@ -56,6 +56,27 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
         g.ws_bytes = 0;
         return g;
     }
+    // int8 x int8 grids that fill at most half the CUs with 128 x 128 tiles
+    // but half to all of them with 64 x 64 tiles (the 7B decoder's 4096-row
+    // weights at 256 tokens): 64 x 64 tiles, one block per CU with the deep
+    // ring, no split.  Each block then pulls half the bytes of a 128 x 128
+    // block through its ring, whose bytes in flight bound a CU's rate here
+    // (cold weights, 256 x 4096 x 4096: 12.8 us against 21.9 us).  Long-k
+    // grids smaller than that keep split-K: 64-byte stages of 2 MFMAs per
+    // wave are then barrier-bound.  With a workspace, k past 128 stages also
+    // keeps split-K (256 x 4096 x 11008: four splits and the reduction,
+    // 26.7 us, against 28.5 us for 64 x 64 tiles).
+    if (!int4 && !a8 && (!allow_split || stages <= 128)) {
+        const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+        const int64_t t64 = ((m + 63) / 64) * ((n + 63) / 64);
+        if (t128 * 2 <= cus && t64 * 2 >= cus && t64 <= cus) {
+            g.bm = g.bn = 64;
+            g.splits = 1;
+            g.deep = true;
+            g.ws_bytes = 0;
+            return g;
+        }
+    }
     g.bm = 128;
     g.bn = (n >= 4096 && int4 && !a8) ? 256 : 128;
     const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);

@@ -444,6 +444,7 @@ GEMM_SHAPES = [
     (70, 99, 2048),      # split-K, odd n: one output per reduce lane
     (65, 256, 16384),    # split-K
     (1000, 1800, 4096),  # int8 x int8: two K splits, one block per CU (240 CUs); ragged M and N
+    (250, 4000, 256),    # int8 x int8: 64 x 64 tiles, one per CU (252); ragged M and N
 ]
 
 
@@ -502,6 +503,8 @@ BIG_GRID_SHAPES = [
     ("w8a8", 4100, 4096, 192),    # 3 k-stages: one zero-filled stage pads the 4-stage ring
     ("w4a4", 4352, 4096, 384),    # 34 x 16 tiles of 128 x 256, 3 k-stages
     ("w4a8", 4352, 4096, 512),    # 4 k-stages, padded to 6 (3-stage ring)
+    ("w8a8", 256, 4096, 2048),    # the 7B decoder's 256 tokens: 64 x 64 tiles, one per CU
+    ("w8a8", 256, 11008, 512),    # 172 tiles of 128 x 128 (the deep ring), not 64 x 64
 ]
 
 
@@ -538,7 +541,8 @@ def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
                                           ("w8a8", 40, 100, 4096), ("w4a4", 17, 99, 2048),
                                           ("w4a8", 300, 520, 1024), ("w4a8", 64, 256, 16384),
                                           ("w4a8", 17, 99, 2048), ("w4a4", 50, 1024, 1024),
-                                          ("w8a8", 80, 100, 4096), ("w4a8", 9, 1000, 1024)])
+                                          ("w8a8", 80, 100, 4096), ("w4a8", 9, 1000, 1024),
+                                          ("w8a8", 250, 4000, 256)])
 def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     say(f"gemm {out} {scheme} {m}x{n}x{k}")
     a, b, abits, wbits, fn = scheme_codes(scheme, "e", m, n, k)
