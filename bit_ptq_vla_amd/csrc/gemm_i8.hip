@@ -45,6 +45,7 @@ namespace qlin {
 namespace {
 
 constexpr int STAGE_BYTES = 64;   // bytes of one row per pipeline stage
+constexpr int OOB_OFFSET = 0x7FFFFFF0;   // a buffer offset past every range: the hardware returns zeros
 
 // f(std::integral_constant<int, Q>) for Q = B .. E-1 in order: loop bodies whose
 // indices must be compile-time constants (register arrays, instruction order).
@@ -533,15 +534,23 @@ __global__ __launch_bounds__(256, MINB) void gemm_i8_kernel(GemmParams p) {
     const int rowstep_a = (A8 ? 32 : 64) * static_cast<int>(p.kbytes_a);
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // W4A4 with k % 128 == 64: the last stage holds 32 bytes of each row; the
+    // lanes of its other two chunks take an offset past the buffer range, so
+    // those LDS chunks receive zeros (which add nothing) instead of the next
+    // row's bytes.  Both operands share the lane's chunk.
+    const int kbytes_i = static_cast<int>(p.kbytes);
     auto issue = [&](int st, int8_t* buf) {
         const int kb = (s_begin + st) * STAGE_BYTES;
         const int ka = (s_begin + st) * SA;
         const uint32_t a_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + wave_u * 1024;
         const uint32_t b_dst = a_dst + BM * SA;
+        bool live = true;
+        if constexpr (INT4 && !A8) live = kb + dma_chunk * 16 < kbytes_i;
 #pragma unroll
-        for (int i = 0; i < A_INSTR; ++i) dma16(rsrc_a, dma_voff_a + ka + i * rowstep_a, a_dst + i * 4096);
+        for (int i = 0; i < A_INSTR; ++i)
+            dma16(rsrc_a, live ? dma_voff_a + ka + i * rowstep_a : OOB_OFFSET, a_dst + i * 4096);
 #pragma unroll
-        for (int i = 0; i < B_INSTR; ++i) dma16(rsrc_b, dma_voff + kb + i * row64, b_dst + i * 4096);
+        for (int i = 0; i < B_INSTR; ++i) dma16(rsrc_b, live ? dma_voff + kb + i * row64 : OOB_OFFSET, b_dst + i * 4096);
     };
 
     v16i acc[TM][TN];

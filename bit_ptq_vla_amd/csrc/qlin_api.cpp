@@ -92,10 +92,13 @@ int64_t code_bytes(int64_t rows, int64_t k, int32_t bits) {
     return rows * (k / 4 * 3);
 }
 
+// Step of k the GEMM schemes take: 64 (W8A8, and W4A4, whose last 64-byte
+// stage of 128 codes may then be half full), 128 for W4A8 (a stage holds
+// 128 k of both operands) and E2M3 (128 codes per 96-byte stage).
+int64_t gemm_k_step(bool int4, bool a8, bool f6) { return (f6 || (int4 && a8)) ? 128 : 64; }
+
 // Shape checks of the integer GEMM schemes (before any pointer check).
-bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, bool int4) {
-    // one pipeline stage is 64 bytes of a row: 64 int8 or 128 int4 codes
-    const int64_t kstep = int4 ? 128 : 64;
+bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, int64_t kstep) {
     if (m < 0 || n < 1 || k < kstep || (k % kstep) != 0) return false;
     // k < 2^17: the accumulator, 256 * acc for W4A4 and 16 * acc for W4A8,
     // stays below 2^31 in magnitude for any codes (|code| <= 8 int4, 128 int8)
@@ -123,7 +126,7 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     if (y_dtype != QLIN_I32 && ((!x_scale && m > 0) || !w_scale)) return QLIN_ERR_NULL;
     if (y_dtype != QLIN_F16 && y_dtype != QLIN_BF16 && y_dtype != QLIN_F32 && y_dtype != QLIN_I32)
         return QLIN_ERR_DTYPE;
-    if (!gemm_shape_ok(m, n, k, int4)) return QLIN_ERR_SHAPE;
+    if (!gemm_shape_ok(m, n, k, gemm_k_step(int4, a8, f6))) return QLIN_ERR_SHAPE;
     if (ws_bytes < 0) return QLIN_ERR_SHAPE;
     if (!ws && ws_bytes > 0) return QLIN_ERR_NULL;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale) ||
@@ -438,7 +441,7 @@ qlin_status qlin_gemm_w4a8(const void* xq, const float* x_scale, const void* wq,
 int64_t qlin_gemm_workspace_bytes(qlin_scheme scheme, int64_t m, int64_t n, int64_t k) {
     bool int4 = false, a8 = false, f6 = false;
     if (!scheme_flags(scheme, &int4, &a8, &f6)) return -1;
-    if (!gemm_shape_ok(m, n, k, int4)) return -1;
+    if (!gemm_shape_ok(m, n, k, gemm_k_step(int4, a8, f6))) return -1;
     return gemm_ws_need(m, n, k, int4, a8, f6);
 }
 
@@ -464,7 +467,8 @@ qlin_status qlin_gemm_geglu(qlin_scheme scheme, const void* xq, const float* x_s
     if (!xq && m > 0) return QLIN_ERR_NULL;
     if (!wq || !h || !w_scale || (!x_scale && m > 0)) return QLIN_ERR_NULL;
     if (h_dtype != QLIN_F16 && h_dtype != QLIN_BF16 && h_dtype != QLIN_F32) return QLIN_ERR_DTYPE;
-    if (m < 0 || n2 < 64 || (n2 % 64) != 0 || k < 128 || (k % 128) != 0 || k >= kMaxGemmK) return QLIN_ERR_SHAPE;
+    const int64_t kstep = gemm_k_step(true, false, f6);
+    if (m < 0 || n2 < 64 || (n2 % 64) != 0 || k < kstep || (k % kstep) != 0 || k >= kMaxGemmK) return QLIN_ERR_SHAPE;
     if (m > 0x7FFFFFFF || n2 > 0x7FFFFFFF) return QLIN_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(h) || !aligned16(x_scale) || !aligned16(w_scale))
         return QLIN_ERR_ALIGN;

@@ -62,15 +62,26 @@ struct Piece {
     v4i b[Cfg<S>::BW];
 };
 
+// Piece p of the lane's rows; ok == false (the lane's word lies past k in a
+// half-full last W4A4 piece) reads piece 0 instead and keeps zeros.
 template <int S, int MW>
-__device__ __forceinline__ void load_piece(Piece<S, MW>& f, const v4i* const (&xp)[MW], const v4i* wp, int p) {
+__device__ __forceinline__ void load_piece(Piece<S, MW>& f, const v4i* const (&xp)[MW], const v4i* wp, int p,
+                                           bool ok) {
     using C = Cfg<S>;
+    const int pa = ok ? p : 0;
+    const v4i zero = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < C::BW; ++j) f.b[j] = __builtin_nontemporal_load(wp + p * (C::B4 ? 4 : C::STEPS * 4) + j);
+    for (int j = 0; j < C::BW; ++j) {
+        const v4i v = __builtin_nontemporal_load(wp + pa * (C::B4 ? 4 : C::STEPS * 4) + j);
+        f.b[j] = ok ? v : zero;
+    }
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-        for (int j = 0; j < C::AW; ++j) f.a[mt][j] = xp[mt][p * (C::A4 ? 4 : C::STEPS * 4) + j];
+        for (int j = 0; j < C::AW; ++j) {
+            const v4i v = xp[mt][pa * (C::A4 ? 4 : C::STEPS * 4) + j];
+            f.a[mt][j] = ok ? v : zero;
+        }
 }
 
 template <int S, int MW>
@@ -106,7 +117,9 @@ __global__ __launch_bounds__(64 * WK) void skinny_int_kernel(const uint8_t* __re
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, q = lane >> 4;
-    const int pieces = static_cast<int>(k / C::PK);
+    // W4A4 takes k % 128 == 64: a last piece of 64 codes, whose lane
+    // quarters 2 and 3 (bytes 32 .. 63 of the piece) hold no codes
+    const int pieces = static_cast<int>((k + C::PK - 1) / C::PK);
     const int p0 = wave * pieces / WK, p1 = (wave + 1) * pieces / WK;
     const int64_t col0 = static_cast<int64_t>(blockIdx.x) * 16;
     const int64_t row0 = static_cast<int64_t>(blockIdx.y) * (16 * MW);
@@ -132,10 +145,14 @@ __global__ __launch_bounds__(64 * WK) void skinny_int_kernel(const uint8_t* __re
 
     // two pieces per trip, both loaded before either is multiplied (a lone
     // last piece reloads itself: branch-free, every wait count static)
+    const int64_t kbytes_row = C::A4 ? k / 2 : k;   // W4A4: bytes of a row
     for (int p = p0; p < p1; p += 2) {
         Piece<S, MW> f0, f1;
-        load_piece<S, MW>(f0, xp, wp, p);
-        load_piece<S, MW>(f1, xp, wp, p + 1 < p1 ? p + 1 : p);
+        const int p1st = p + 1 < p1 ? p + 1 : p;
+        const bool ok0 = !C::A4 || static_cast<int64_t>(p) * 64 + 16 * q < kbytes_row;
+        const bool ok1 = !C::A4 || static_cast<int64_t>(p1st) * 64 + 16 * q < kbytes_row;
+        load_piece<S, MW>(f0, xp, wp, p, ok0);
+        load_piece<S, MW>(f1, xp, wp, p1st, ok1);
         mma_piece<S, MW>(f0, acc);
         if (p + 1 < p1) mma_piece<S, MW>(f1, acc);
     }

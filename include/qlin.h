@@ -268,7 +268,9 @@ qlin_status qlin_quantize_weights_composite(const void* w, qlin_dtype w_dtype, i
  *            (packed int4 for w4a4, int8 for w8a8), contiguous rows of k.
  *   y_dtype  F16, BF16, F32, or I32 (raw accumulators; the scales may then be NULL).
  *   y        out [m][n] contiguous.
- * Preconditions: m >= 0, n >= 1; k a multiple of 64 (w8a8) or of 128 (w4a4),
+ * Preconditions: m >= 0, n >= 1; k a multiple of 64 (for w4a4 the last
+ * 64-byte stage of 128 codes is then half full and its upper half reads as
+ * zeros),
  * at least one such step; k < 131072 (2^17), which keeps every int32
  * accumulator exact for any codes, -8 and -128 included.
  * These calls never split k (no scratch); a grid of few output tiles with a
@@ -359,8 +361,9 @@ qlin_status qlin_gemm_static_ws(qlin_scheme scheme, const void* xq, const float*
  *   h[m][c]  = round_{h_dtype}(gelu(g[m][c]) * u[m][c]), c = 0 .. f-1, h
  *            contiguous [m][f]; gelu is the erf form, evaluated in fp32 to
  *            within about one fp32 rounding; h_dtype F16, BF16 or F32.
- * Preconditions: m >= 0; n2 a multiple of 64; k a multiple of 128, below
- * 131072.  Errors: NULL pointers (QLIN_ERR_NULL), other dtypes
+ * Preconditions: m >= 0; n2 a multiple of 64; k a multiple of 64 (128 for
+ * E2M3 codes in qlin_gemm_geglu), below 131072.  Errors: NULL pointers
+ * (QLIN_ERR_NULL), other dtypes
  * (QLIN_ERR_DTYPE), shapes (QLIN_ERR_SHAPE), pointers not 16-byte aligned
  * (QLIN_ERR_ALIGN), h overlapping an input (QLIN_ERR_ALIAS); m == 0 returns
  * QLIN_OK without touching the device.  The first call on a device also

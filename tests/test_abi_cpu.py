@@ -127,9 +127,10 @@ def test_gemm_rejects(lib, fn, kw, status):
 
 
 @pytest.mark.parametrize("fn,k,status", [("qlin_gemm_w8a8", 192, q.QLIN_OK), ("qlin_gemm_w4a8", 192, q.QLIN_ERR_SHAPE),
-                                         ("qlin_gemm_w4a4", 192, q.QLIN_ERR_SHAPE)])
+                                         ("qlin_gemm_w4a4", 192, q.QLIN_OK), ("qlin_gemm_w4a4", 160, q.QLIN_ERR_SHAPE),
+                                         ("qlin_gemm_w8a8", 160, q.QLIN_ERR_SHAPE), ("qlin_gemm_w4a8", 256, q.QLIN_OK)])
 def test_gemm_k_step_per_scheme(lib, fn, k, status):
-    # int4 weights take k in multiples of 128; int8 x int8 in multiples of 64 (m = 0: no device call)
+    # W8A8 and W4A4 take k in multiples of 64, W4A8 in multiples of 128 (m = 0: no device call)
     assert getattr(lib, fn)(None, None, P2, P4, 0, 64, k, 0x70000000, 1, None) == status
 
 
@@ -149,7 +150,9 @@ def test_gemm_workspace_bytes(lib):
         assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 816, 2048, 16384) == 2 * 816 * 2048 * 4
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 52224, 2048, 16384) == 0    # large grid: no split
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 50, 1024, 4096) == 0        # small-M kernel: no split
-    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 192) == -1       # int4 k step is 128
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 160) == -1       # k step is 64
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 192) >= 0
+    assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A8, 816, 2048, 192) == -1       # W4A8 k step is 128
     assert lib.qlin_gemm_workspace_bytes(4, 816, 2048, 16384) == -1               # no such scheme
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 16384) == 0  # E2M3 never splits
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 192) == -1
@@ -202,8 +205,8 @@ def test_gemm_static_ws_rejects(lib):
     (dict(xq=None), q.QLIN_ERR_NULL), (dict(wq=None), q.QLIN_ERR_NULL), (dict(h=None), q.QLIN_ERR_NULL),
     (dict(sx=None), q.QLIN_ERR_NULL), (dict(sw=None), q.QLIN_ERR_NULL),
     (dict(hdt=3), q.QLIN_ERR_DTYPE), (dict(hdt=9), q.QLIN_ERR_DTYPE),
-    (dict(n2=96), q.QLIN_ERR_SHAPE), (dict(n2=32), q.QLIN_ERR_SHAPE), (dict(k=192), q.QLIN_ERR_SHAPE),
-    (dict(k=64), q.QLIN_ERR_SHAPE), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=131072 + 128), q.QLIN_ERR_SHAPE), (dict(k=131072), q.QLIN_ERR_SHAPE),
+    (dict(n2=96), q.QLIN_ERR_SHAPE), (dict(n2=32), q.QLIN_ERR_SHAPE), (dict(k=160), q.QLIN_ERR_SHAPE),
+    (dict(k=32), q.QLIN_ERR_SHAPE), (dict(m=-1), q.QLIN_ERR_SHAPE), (dict(k=131072 + 128), q.QLIN_ERR_SHAPE), (dict(k=131072), q.QLIN_ERR_SHAPE),
     (dict(xq=BAD), q.QLIN_ERR_ALIGN), (dict(h=BAD), q.QLIN_ERR_ALIGN),
     (dict(h=P + 64), q.QLIN_ERR_ALIAS),
 ])

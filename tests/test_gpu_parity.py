@@ -432,7 +432,7 @@ GEMM_SHAPES = [
     (50, 1024, 4096),
     (64, 256, 16384),
     (1, 96, 128),        # one token, fewer k pieces than waves
-    (33, 64, 192),       # k % 128 == 64: w8a8 only (w4a4 needs k % 128 == 0)
+    (33, 64, 192),       # k % 128 == 64: a half-full last int4 piece (w4a8 needs k % 128 == 0)
     (40, 100, 4096),
     (17, 99, 2048),      # odd n: ragged last column strip
     (5, 1000, 1024),
@@ -445,6 +445,8 @@ GEMM_SHAPES = [
     (65, 256, 16384),    # split-K
     (1000, 1800, 4096),  # int8 x int8: two K splits, one block per CU (240 CUs); ragged M and N
     (250, 4000, 256),    # int8 x int8: 64 x 64 tiles, one per CU (252); ragged M and N
+    (300, 520, 320),     # k % 128 == 64 on the large-tile GEMM: a half-full last int4 stage
+    (70, 99, 4160),      # ... with split-K: 33 stages in two splits, the half stage in the last
 ]
 
 
@@ -471,8 +473,8 @@ def test_gemm_raw_accumulators_bit_exact(scheme, m, n, k, ws):
     """Plain entry points (never split k) and qlin_gemm_ws with its workspace
     (split-K on the shapes marked so): raw int32 accumulators, bit-exact."""
     say(f"gemm i32 {scheme} {m}x{n}x{k} ws={ws}")
-    if scheme != "w8a8" and k % 128:
-        pytest.skip("int4 weights take k in multiples of 128")
+    if scheme == "w4a8" and k % 128:
+        pytest.skip("W4A8 takes k in multiples of 128")
     work = workspace_for(scheme, m, n, k) if ws else None
     if ws and work is None:
         pytest.skip("no split-K at this shape: the workspace call is the plain call")
@@ -505,6 +507,7 @@ BIG_GRID_SHAPES = [
     ("w4a8", 4352, 4096, 512),    # 4 k-stages, padded to 6 (3-stage ring)
     ("w8a8", 256, 4096, 2048),    # the 7B decoder's 256 tokens: 64 x 64 tiles, one per CU
     ("w8a8", 256, 11008, 512),    # 172 tiles of 128 x 128 (the deep ring), not 64 x 64
+    ("w4a4", 2100, 4096, 320),    # 128 x 256 tiles, a half-full last int4 stage
 ]
 
 
@@ -520,7 +523,8 @@ def test_gemm_big_grid_sampled_rows(scheme, m, n, k):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
 
-@pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256), (4100, 2048, 512), (2050, 8192, 256)])
+@pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256), (4100, 2048, 512), (2050, 8192, 256),
+                                   (1100, 2048, 192)])
 def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
     say(f"gemm geglu big grid {m}x{f}x{k}")
     n2 = 2 * f
@@ -542,7 +546,8 @@ def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
                                           ("w4a8", 300, 520, 1024), ("w4a8", 64, 256, 16384),
                                           ("w4a8", 17, 99, 2048), ("w4a4", 50, 1024, 1024),
                                           ("w8a8", 80, 100, 4096), ("w4a8", 9, 1000, 1024),
-                                          ("w8a8", 250, 4000, 256)])
+                                          ("w8a8", 250, 4000, 256), ("w4a4", 300, 520, 320),
+                                          ("w4a4", 33, 64, 192)])
 def test_gemm_dequant_epilogue(scheme, m, n, k, out):
     say(f"gemm {out} {scheme} {m}x{n}x{k}")
     a, b, abits, wbits, fn = scheme_codes(scheme, "e", m, n, k)
