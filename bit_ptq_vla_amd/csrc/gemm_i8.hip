@@ -1288,6 +1288,216 @@ __global__ __launch_bounds__(256, MINB) void gemm_f6_kernel(GemmParams p) {
     }
 }
 
+// ---- E2M3 with two blocks per CU --------------------------------------------
+//
+// The fused GeGLU GEMM on grids that fill the chip: 128 x 256 tiles, four
+// waves of 64 x 128, so that one block's epilogue (the GeLU work) runs under
+// the co-resident block's main loop, as for the int4 tiles (52224 x 32768 x
+// 2048: 3.10 ms against 3.64 ms with 256 x 256 tiles, one block per CU).  Two
+// blocks fit a CU with a two-stage ring (2 x 36 KB + the 8 KB GeLU table) and
+// fragments held per k-step rather than per stage: a k-step's operand of a
+// row is 24 bytes, a 16-byte and an 8-byte LDS read (k-step 0: chunk 3h and
+// the low half of chunk 3h+1; k-step 1: the high half of chunk 3h+1 and chunk
+// 3h+2).  Per stage: the k-step-0 MFMAs with the k-step-1 reads under them;
+// the synchronisation (next stage landed, every wave past this stage's
+// reads); the k-step-1 MFMAs with the DMA of stage it + 2 into this stage's
+// buffer and the next stage's k-step-0 reads under them.
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+template <int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_f6w_kernel(GemmParams p) {
+    constexpr int BM = 128, BN = 256, TM = 2, TN = 4, NS = 2, SB = 96;
+    constexpr int STAGE = (BM + BN) * SB;
+    constexpr int LOADS = STAGE / 4096;
+    constexpr int LA = BM * SB / 4096;
+    static_assert(LA * 4096 == BM * SB && LOADS * 4096 == STAGE, "whole 1 KB loads per wave");
+    constexpr int KM = TM * TN;                 // MFMAs per k-step
+    constexpr int KR = 2 * (TM + TN);           // LDS reads per k-step
+    constexpr bool GEGLU = OUT >= OUT_GEGLU;
+    constexpr int RING0 = GEGLU ? GTAB_BYTES : 0;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING0 + NS * STAGE];
+    int8_t* const ring = lds + RING0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int nblocks = gridDim.x;
+    int bid = blockIdx.x;
+    if ((nblocks & 7) == 0) bid = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+    int tile_m, tile_n;
+    if (p.group_m > 0) {
+        const int per_group = p.group_m * p.tiles_n;
+        const int g = bid / per_group;
+        const int first = g * p.group_m;
+        const int rows = (p.tiles_m - first) < p.group_m ? (p.tiles_m - first) : p.group_m;
+        const int r = bid - g * per_group;
+        tile_n = r / rows;
+        tile_m = first + (r - tile_n * rows);
+    } else {
+        tile_n = bid / p.tiles_m;
+        tile_m = bid - tile_n * p.tiles_m;
+    }
+    const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
+    const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
+    const int nst = p.stages;
+    const int nstp = (nst + 1) & ~1;
+    constexpr int OOB = 0x7FFFFFF0;
+    const int kb = static_cast<int>(p.kbytes);
+
+    const v4i rsrc_a = make_rsrc(p.a + m0 * p.kbytes, (p.m - m0) * p.kbytes);
+    const v4i rsrc_b = make_rsrc(p.b + n0 * p.kbytes, (p.n - n0) * p.kbytes);
+
+    int dvoff[LOADS];
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+        const int slot = (4 * q + wave) * 64 + lane;
+        const int s2 = q < LA ? slot : slot - BM * 6;
+        const int r = s2 / 6, pos = s2 - r * 6;
+        dvoff[q] = r * kb + (pos ^ ((r >> 3) & 1)) * 16;
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+    auto dma_one = [&](int st, uint32_t buf_addr, int q) __attribute__((always_inline)) {
+        const int off = st < nst ? dvoff[q] + st * SB : OOB;
+        dma16(q < LA ? rsrc_a : rsrc_b, off, buf_addr + wave_u * 1024 + q * 4096);
+    };
+
+    v16f_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int l32 = lane & 31;
+    const int hsel = lane >> 5;
+    const int sw = (l32 >> 3) & 1;
+    const int a_row = (wm * (BM / 2) + l32) * SB;
+    const int b_row = BM * SB + (wn * (BN / 2) + l32) * SB;
+    const int c0 = ((3 * hsel + 0) ^ sw) * 16, c1 = ((3 * hsel + 1) ^ sw) * 16, c2 = ((3 * hsel + 2) ^ sw) * 16;
+
+    struct KF {
+        v8i_t a[TM];
+        v8i_t b[TN];
+    };
+    KF f[2];
+    // read r (0 .. KR-1) of k-step KS of a fragment set from the stage buffer st
+    auto read_one = [&](const int8_t* st, KF& fr, auto kc, auto rc) __attribute__((always_inline)) {
+        constexpr int KS = decltype(kc)::value;
+        constexpr int r = decltype(rc)::value;
+        constexpr int which = r / 2, t = r % 2;
+        const int8_t* row = (which < TM) ? st + a_row + which * 32 * SB : st + b_row + (which - TM) * 32 * SB;
+        v8i_t& v = (which < TM) ? fr.a[which < TM ? which : 0] : fr.b[which < TM ? 0 : which - TM];
+        if constexpr (KS == 0) {
+            if constexpr (t == 0) {
+                const v4i d = *reinterpret_cast<const v4i*>(row + c0);
+                v[0] = d.x; v[1] = d.y; v[2] = d.z; v[3] = d.w;
+            } else {
+                const v2i_t e = *reinterpret_cast<const v2i_t*>(row + c1);
+                v[4] = e.x; v[5] = e.y;
+            }
+        } else {
+            if constexpr (t == 0) {
+                const v2i_t e = *reinterpret_cast<const v2i_t*>(row + c1 + 8);
+                v[0] = e.x; v[1] = e.y;
+            } else {
+                const v4i d = *reinterpret_cast<const v4i*>(row + c2);
+                v[2] = d.x; v[3] = d.y; v[4] = d.z; v[5] = d.w;
+            }
+        }
+    };
+    auto mfma_one = [&](const KF& fr, auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int i = q / TN, j = q % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.a[i], fr.b[j], acc[i][j], 2, 2, 0, 127, 0,
+                                                                      127);
+    };
+
+    if constexpr (GEGLU) {
+        static_assert(GTAB_BYTES == 2 * 4 * 1024, "two 16-byte loads per lane");
+        const v4i rsrc_t = make_rsrc(reinterpret_cast<const int8_t*>(g_gelu_neg_tab), GTAB_BYTES);
+        const uint32_t t_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + wave_u * 1024;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(rsrc_t, (i * 4 + wave) * 1024 + lane * 16, t_dst + i * 4096);
+    }
+#pragma unroll
+    for (int pst = 0; pst < NS; ++pst)
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) dma_one(pst, ring_addr + pst * STAGE, q);
+    wait_vmcnt<LOADS>();   // stage 0 (and the GeLU table, issued first) landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    static_for<0, KR>([&](auto rc) __attribute__((always_inline)) {
+        read_one(ring, f[0], std::integral_constant<int, 0>{}, rc);
+    });
+
+    auto stage = [&](auto par, int it) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;   // buffer of this stage
+        const int8_t* buf = ring + P * STAGE;
+        const int8_t* nbuf = ring + (P ^ 1) * STAGE;
+        const uint32_t buf_addr = ring_addr + P * STAGE;
+        // k-step 0: its MFMAs, the k-step-1 reads of this stage under them
+        static_for<0, KM>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mfma_one(f[0], qc);
+            static_for<0, KR>([&](auto rc) __attribute__((always_inline)) {
+                constexpr int r = decltype(rc)::value;
+                if constexpr (r * KM / KR == q) read_one(buf, f[1], std::integral_constant<int, 1>{}, rc);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // next stage landed (the only DMA in flight), every wave past this stage's reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // k-step 1: its MFMAs, the DMA of stage it + 2 and the next stage's k-step-0 reads under them
+        static_for<0, KM>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mfma_one(f[1], qc);
+            static_for<0, LOADS + KR>([&](auto oc) __attribute__((always_inline)) {
+                constexpr int o = decltype(oc)::value;
+                if constexpr (o * KM / (LOADS + KR) == q) {
+                    if constexpr (o < LOADS) dma_one(it + NS, buf_addr, o);
+                    else read_one(nbuf, f[0], std::integral_constant<int, 0>{}, std::integral_constant<int, o - LOADS>{});
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    for (int it = 0; it < nstp; it += 2) {
+        stage(std::integral_constant<int, 0>{}, it);
+        stage(std::integral_constant<int, 1>{}, it + 1);
+    }
+
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (m0 + wm * (BM / 2) >= p.m) return;
+    constexpr int REGION = NS * STAGE / 4 / 16 * 16;
+    if constexpr (GEGLU) {
+        store_tile_geglu<BM, BN, 0, OUT - OUT_GEGLU, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                                             reinterpret_cast<const float*>(lds),
+                                                             ring + wave * REGION);
+    } else {
+        store_tile_lds<BM, BN, 0, OUT, REGION>(acc, p, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                                               ring + wave * REGION, p.y);
+    }
+}
+
+template <int OUT>
+hipError_t launch_f6w(const GemmParams& p, hipStream_t st) {
+    dim3 grid(static_cast<unsigned>(p.tiles_m * p.tiles_n));
+    hipLaunchKernelGGL((gemm_f6w_kernel<OUT>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int ODT>
+hipError_t launch_f6w_geglu(const GemmParams& p, hipStream_t st) {
+    return launch_f6w<OUT_GEGLU + ODT>(p, st);
+}
+
 // Sum of split-K partials in split order (integer: bit-exact), then the
 // epilogue; four consecutive outputs per lane (n % 4 == 0), else one.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const int32_t* ws, int splits, int64_t m,
@@ -1559,6 +1769,15 @@ hipError_t launch_gemm_f6(const GemmPlan& plan, const void* xq, const float* x_s
     p.tiles_n = static_cast<int>((n + plan.bn - 1) / plan.bn);
     p.group_m = plan.group_m;
     p.y_dtype = y_dtype;
+    if (plan.bm == 128 && plan.bn == 256) {   // the two-blocks-per-CU GeGLU kernel
+        if (!geglu) return hipErrorInvalidValue;
+        switch (p.y_dtype) {
+            case BF16: return launch_f6w_geglu<BF16>(p, st);
+            case F16: return launch_f6w_geglu<F16>(p, st);
+            case F32: return launch_f6w_geglu<F32>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     if (plan.bm == 256) return launch_f6_out<256, 256, 1>(p, geglu, st);
     if (plan.bm == 128 && plan.bn == 128) return launch_f6_out<128, 128, 2>(p, geglu, st);
     return hipErrorInvalidValue;

@@ -107,7 +107,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
     return g;
 }
 
-GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k) {
+GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k, bool geglu) {
     (void)k;
     GemmPlan g;
     const int64_t cus = device_cus();
@@ -115,6 +115,12 @@ GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k) {
     g.deep = false;
     g.ws_bytes = 0;
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (tiles256 >= cus && geglu) {   // the fused GeGLU: 128 x 256 tiles, two blocks per CU
+        g.bm = 128;
+        g.bn = 256;
+        g.group_m = 8;
+        return g;
+    }
     if (tiles256 >= cus) {   // at least one 256 x 256 tile per CU
         g.bm = g.bn = 256;
         g.group_m = 4;

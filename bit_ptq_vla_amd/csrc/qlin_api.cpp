@@ -145,8 +145,8 @@ qlin_status gemm_common(const void* xq, const float* x_scale, const void* wq, co
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
     if (f6)
-        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n, k), xq, x_scale, wq, w_scale, m, n, k, y,
-                                            y_dtype, false, s));
+        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n, k, false), xq, x_scale, wq, w_scale, m, n, k,
+                                            y, y_dtype, false, s));
     if (m <= qlin::kSkinnyIntMaxM)
         return map_err(qlin::launch_skinny_int(xq, x_scale, wq, w_scale, m, n, k, int4, a8, y, y_dtype, s));
     if (use_static) {
@@ -481,8 +481,8 @@ qlin_status qlin_gemm_geglu(qlin_scheme scheme, const void* xq, const float* x_s
     if (st != QLIN_OK) return st;
     hipStream_t s = as_stream(stream);
     if (f6)
-        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n2, k), xq, x_scale, wq, w_scale, m, n2, k, h,
-                                            h_dtype, true, s));
+        return map_err(qlin::launch_gemm_f6(qlin::plan_gemm_f6(m, n2, k, true), xq, x_scale, wq, w_scale, m, n2, k,
+                                            h, h_dtype, true, s));
     return map_err(qlin::launch_gemm_geglu(xq, x_scale, wq, w_scale, m, n2, k, true, h, h_dtype, s));
 }
 

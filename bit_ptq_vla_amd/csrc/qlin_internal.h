@@ -88,7 +88,7 @@ hipError_t launch_gemm_geglu(const void* xq, const float* x_scale, const void* w
 // W4A4 with the codes stored as FP6 E2M3 fields (3 bytes per 4 codes) on the
 // scaled FP6 MFMA; k a multiple of 128; no split-K.  geglu: the gate|up
 // layout and epilogue of launch_gemm_geglu.
-GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k);
+GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k, bool geglu);
 hipError_t launch_gemm_f6(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
                           const float* w_scale, int64_t m, int64_t n, int64_t k, void* y, int y_dtype, bool geglu,
                           hipStream_t st);

@@ -158,12 +158,14 @@ def test_gemm_e2m3_static_scratch_entry_point():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("m,f,k", [(50, 64, 256), (130, 2048, 512), (1, 32, 128), (300, 4096, 1024),
-                                   (4100, 2048, 512), (2050, 8192, 256)])
+                                   (4100, 2048, 512), (2050, 8192, 256), (4100, 2080, 384)])
 def test_gemm_geglu_e2m3_equals_int4_path(m, f, k, out):
+    # the last three grids fill the chip: 128 x 256 tiles, two blocks per CU
+    # (4100 x 4160: ragged last tile row and column; 3 k-stages padded to 4)
     say(f"e2m3 gemm geglu {out} {m}x{f}x{k}")
-    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[out]
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out]
     n2 = 2 * f
     a, b, a6, b6, a4, b4 = operands("g", m, n2, k)
     sx = synth.random_scales(SEED, f"sxg/{m}", m).to(DEV)
