@@ -301,6 +301,27 @@ def layer_breakdown(model, m, reps=3):
     return out
 
 
+def sweep_e2m3_leg(model, m, steps=5, warmup=2):
+    """The same sweep (same weights, folds, scales and int4-grid codes) with
+    the W4A4 projections' codes in FP6 E2M3 storage: q|k|v and the fused
+    gate|up GEMMs on the FP6 matrix cores (bit-identical results), o and down
+    unchanged.  Step time over `steps` steps; the gate|up GEMM's mean launch
+    time from event pairs, against both the FP6 and the int8 peak."""
+    model.use_e2m3 = True
+    try:
+        ms_step, gu_ms, per_step, wall, clk = time_sweep(model, m, steps, warmup)
+    finally:
+        model.use_e2m3 = False
+    tops = model.ops(m) / (ms_step * 1e-3) / 1e12
+    gu_tops = 2 * m * 2 * model.FFN * model.HID / (gu_ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms_step, 4), "TOPS": round(tops, 1),
+            "frac_int8_peak_step": round(tops / INT8_PEAK_TOPS, 4), "steps": steps,
+            "gate_up_e2m3_geglu": {"us_per_launch": round(gu_ms * 1e3, 2), "TOPS": round(gu_tops, 1),
+                                   "frac_fp6_peak": round(gu_tops / FP6_PEAK_TOPS, 4),
+                                   "frac_int8_peak": round(gu_tops / INT8_PEAK_TOPS, 4)},
+            "sclk": clk}
+
+
 def sweep_side(model, ms=(6528, 816), reps=3):
     """The sweep at smaller batches (same weights, first m tokens): median of
     5 trials of `reps` steps each."""
@@ -734,7 +755,7 @@ def main():
     torch.cuda.set_device(dev)
     m = args.m
     log(f"bench: preparing the {args.layers}-layer sweep at M = {m} (weights quantized offline)")
-    model = SweepModel(dev, m, args.layers)
+    model = SweepModel(dev, m, args.layers, e2m3=not args.no_legs)
     log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
     ms_step, gu_ms, per_step, wall, clk = time_sweep(model, m, args.steps, args.warmup)
     tops = model.ops(m) / (ms_step * 1e-3) / 1e12
@@ -771,6 +792,8 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_legs:
+        log("bench: the sweep with the W4A4 codes in E2M3 storage (FP6 matrix cores)")
+        out["sweep_e2m3"] = sweep_e2m3_leg(model, m)
         log("bench: per-launch breakdown of a sweep layer")
         out["layer_breakdown_m%d" % m] = layer_breakdown(model, m)
         log("bench: sweep at M = 6528 and 816")

@@ -105,7 +105,10 @@ class SweepModel:
 
     HID, FFN = 2048, 16384
 
-    def __init__(self, dev, m_max: int, layers: int = 18):
+    def __init__(self, dev, m_max: int, layers: int = 18, e2m3: bool = False):
+        """e2m3: also keep the W4A4 weights (q|k|v, gate|up) in FP6 E2M3
+        storage -- the same int4-grid codes and scales -- so that
+        run_layer can take the FP6 matrix-core GEMMs (use_e2m3)."""
         import torch
 
         import bit_ptq_vla_amd as q
@@ -126,7 +129,10 @@ class SweepModel:
 
         self.x_attn, self.x_o, self.x_mlp = act("attn_in"), act("attn_out"), act("mlp_in")
         bf = torch.bfloat16
+        self.e2m3 = e2m3
+        self.use_e2m3 = False
         self.xq4 = torch.empty((m_max, hid // 2), dtype=torch.uint8, device=dev)
+        self.xq6 = torch.empty((m_max, hid * 3 // 4), dtype=torch.uint8, device=dev) if e2m3 else None
         self.xs4 = torch.empty(m_max, dtype=torch.float32, device=dev)
         self.xq8 = torch.empty((m_max, hid), dtype=torch.int8, device=dev)
         self.xs8 = torch.empty(m_max, dtype=torch.float32, device=dev)
@@ -159,6 +165,8 @@ class SweepModel:
         w_qkv = torch.cat([self.weight(li, nm, hid, hid) for nm in ("q", "k", "v")])
         s, L["inv_qkv"] = q.qlin_calibrate_fold(self.x_attn, w_qkv)
         L["wq_qkv"], L["ws_qkv"] = q.qlin_quantize_weights(w_qkv, fold_s=s, had_block=128, bits=4)
+        if self.e2m3:
+            L["wq6_qkv"], _ = q.qlin_quantize_weights(w_qkv, fold_s=s, had_block=128, bits=q.QLIN_BITS_E2M3)
         del w_qkv
         w_o = self.weight(li, "o", hid, hid)
         s, L["inv_o"] = q.qlin_calibrate_fold(self.x_o, w_o)
@@ -168,6 +176,8 @@ class SweepModel:
         w_gu = q.interleave_gate_up(w_gu[:ffn], w_gu[ffn:])
         s, L["inv_gu"] = q.qlin_calibrate_fold(self.x_mlp, w_gu)
         L["wq_gu"], L["ws_gu"] = q.qlin_quantize_weights(w_gu, fold_s=s, had_block=128, bits=4)
+        if self.e2m3:
+            L["wq6_gu"], _ = q.qlin_quantize_weights(w_gu, fold_s=s, had_block=128, bits=q.QLIN_BITS_E2M3)
         del w_gu
         # the down fold is calibrated on this layer's own h
         q.qlin_rotate_quant_act(self.x_mlp, fold_inv_s=L["inv_gu"], had_block=128, bits=4, out=(self.xq4, self.xs4))
@@ -202,20 +212,31 @@ class SweepModel:
                 evs[i].record()
 
         xq4, xs4, xq8, xs8 = self.xq4[:m], self.xs4[:m], self.xq8[:m], self.xs8[:m]
+        # the W4A4 codes packed int4, or in E2M3 storage on the FP6 matrix cores
+        e6 = self.use_e2m3
+        xq_w4, bits_w4 = (self.xq6[:m], q.QLIN_BITS_E2M3) if e6 else (xq4, 4)
         mark(0)
-        q.qlin_rotate_quant_act(self.x_attn[:m], fold_inv_s=L["inv_qkv"], had_block=128, bits=4, out=(xq4, xs4))
+        q.qlin_rotate_quant_act(self.x_attn[:m], fold_inv_s=L["inv_qkv"], had_block=128, bits=bits_w4,
+                                out=(xq_w4, xs4))
         mark(1)
-        q.qlin_gemm_w4a4(xq4, xs4, L["wq_qkv"], L["ws_qkv"], hid, out=self.y_qkv[:m])
+        if e6:
+            q.qlin_gemm_e2m3(xq_w4, xs4, L["wq6_qkv"], L["ws_qkv"], hid, out=self.y_qkv[:m])
+        else:
+            q.qlin_gemm_w4a4(xq4, xs4, L["wq_qkv"], L["ws_qkv"], hid, out=self.y_qkv[:m])
         mark(2)
         q.qlin_rotate_quant_act(self.x_o[:m], fold_inv_s=L["inv_o"], had_block=128, bits=8, out=(xq8, xs8))
         mark(3)
         q.qlin_gemm_w8a8(xq8, xs8, L["wq_o"], L["ws_o"], hid, out=self.y_o[:m], workspace=ws_o)
         mark(4)
-        q.qlin_rotate_quant_act(self.x_mlp[:m], fold_inv_s=L["inv_gu"], had_block=128, bits=4, out=(xq4, xs4))
+        q.qlin_rotate_quant_act(self.x_mlp[:m], fold_inv_s=L["inv_gu"], had_block=128, bits=bits_w4,
+                                out=(xq_w4, xs4))
         mark(5)
         if ev is not None:
             ev[0].record()
-        q.qlin_gemm_w4a4_geglu(xq4, xs4, L["wq_gu"], L["ws_gu"], hid, out=self.h[:m])
+        if e6:
+            q.qlin_gemm_geglu(q.QLIN_W4A4_E2M3, xq_w4, xs4, L["wq6_gu"], L["ws_gu"], hid, out=self.h[:m])
+        else:
+            q.qlin_gemm_w4a4_geglu(xq4, xs4, L["wq_gu"], L["ws_gu"], hid, out=self.h[:m])
         if ev is not None:
             ev[1].record()
         mark(6)

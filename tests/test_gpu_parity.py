@@ -1041,6 +1041,29 @@ def test_decoder7b_w8a8_m256():
 
 
 @pytest.mark.slow
+def test_sweep_layer_e2m3_storage_equals_int4():
+    """The benchmark's sweep layer with the W4A4 codes in E2M3 storage (q|k|v
+    and the fused gate|up GEMM on the FP6 matrix cores, the two-blocks-per-CU
+    GeGLU kernel at this size) gives the int4 layer's outputs bit for bit:
+    q|k|v, h and the down projection."""
+    from bit_ptq_vla_amd.workload import SweepModel
+
+    m = 6528
+    say(f"sweep layer E2M3 storage M={m}")
+    model = SweepModel(DEV, m, layers=1, e2m3=True)
+    L = model.layer[0]
+    outs = []
+    for e6 in (False, True):
+        model.use_e2m3 = e6
+        model.run_layer(L, m)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (model.y_qkv, model.h, model.y_dn)])
+    for name, a, b in zip(("q|k|v", "h", "down"), outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} differs between storages"
+    del model
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("m", [6528, 52224])
 def test_backbone_sweep_layer_large_m(m):
     """One layer of the 18-layer backbone sweep at M = 6528 and 52224: q (W4A4
