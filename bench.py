@@ -23,7 +23,9 @@ in TOPS.  roofline: the gate|up GEMM (the dominant kernel, 57% of the step's
 ops) timed by event pairs around each of its launches inside the timed
 region.
 
-Side legs (one JSON object each): the sweep at M = 6528 and 816, the
+Side legs (one JSON object each): the same sweep with the W4A4 codes in FP6
+E2M3 storage (the FP6 matrix-core GEMMs, bit-identical results), the sweep at
+M = 6528 and 816, the
 backbone MLP block at M = 816 (split-K down GEMM with its workspace), the W4A8
 GEMM, the 7B-decoder projections at M = 256 W8A8 (HBM-bound), the action
 expert over 10 denoising steps (W4A4, per-step static tables, W4A16; warm and

@@ -157,6 +157,12 @@ def test_gemm_workspace_bytes(lib):
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 16384) == 0  # E2M3 never splits
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4_E2M3, 816, 2048, 192) == -1
     assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 0, 2048, 16384) == 0
+    if not torch.cuda.is_available():   # plans for 256 CUs
+        # the 7B decoder's 4096-row weights at 256 tokens: 64 x 64 tiles, no split ...
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 256, 4096, 4096) == 0
+        # ... but with k past 128 stages the workspace call keeps split-K (four splits)
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 256, 4096, 11008) == 4 * 256 * 4096 * 4
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 16448) >= 0   # W4A4 at k % 128 == 64
 
 
 def gemm_ws(lib, scheme=q.QLIN_W8A8, xq=P, sx=P3, wq=P2, sw=P4, m=DOWN["m"], n=DOWN["n"], k=DOWN["k"],
