@@ -1689,6 +1689,27 @@ hipError_t static_scratch(int32_t** ptr) {
 hipError_t launch_gemm(const GemmPlan& plan, const void* xq, const float* x_scale, const void* wq,
                        const float* w_scale, int64_t m, int64_t n, int64_t k, bool int4, bool a8, void* y,
                        int y_dtype, int32_t* ws, hipStream_t st) {
+    if (plan.bm == 256 && plan.m_tail > 0 && plan.m_tail < m) {
+        // the full rounds of 256 x 256 tiles, then the last rows as 128 x 128
+        // tiles (two blocks per CU): the same per-element arithmetic
+        GemmPlan head = plan;
+        head.m_tail = 0;
+        const int64_t mh = m - plan.m_tail;
+        hipError_t e = launch_gemm(head, xq, x_scale, wq, w_scale, mh, n, k, int4, a8, y, y_dtype, ws, st);
+        if (e != hipSuccess) return e;
+        GemmPlan tail;
+        tail.bm = tail.bn = 128;
+        tail.splits = 1;
+        tail.deep = false;
+        tail.group_m = 0;
+        tail.ws_bytes = 0;
+        tail.m_tail = 0;
+        const int64_t a_row = (int4 && !a8) ? k / 2 : k;
+        const int64_t y_elem = (y_dtype == BF16 || y_dtype == F16) ? 2 : 4;
+        return launch_gemm(tail, static_cast<const int8_t*>(xq) + mh * a_row, x_scale ? x_scale + mh : nullptr, wq,
+                           w_scale, plan.m_tail, n, k, int4, a8, static_cast<char*>(y) + mh * n * y_elem, y_dtype,
+                           ws, st);
+    }
     GemmParams p;
     p.a = static_cast<const int8_t*>(xq);
     p.b = static_cast<const int8_t*>(wq);

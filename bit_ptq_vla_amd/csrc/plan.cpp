@@ -37,6 +37,7 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
     // (int8 keeps 128 columns: its 128 x 256 tile would spill at two blocks per
     // CU; so does W4A8, whose 128 x 256 stage would not leave room for 3 stages.)
     GemmPlan g;
+    g.m_tail = 0;
     const int64_t cus = device_cus();
     const int64_t kbytes = int4 ? k / 2 : k;
     const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
@@ -54,6 +55,18 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
         g.deep = false;
         g.group_m = 4;
         g.ws_bytes = 0;
+        // When the last round of 256 x 256 tiles would fill at most half of
+        // the CUs, its rows run instead as 128 x 128 tiles, two blocks per
+        // CU, in a second launch: the whole chip then shares them, rather
+        // than most CUs idling through a last round.  At 52224 x 2048 that is
+        // 6.375 rounds: 6 rounds of 256 x 256 tiles and 3072 rows (384 small
+        // tiles on 512 block slots).
+        const int64_t tn = (n + 255) / 256, tm = (m + 255) / 256;
+        if (cus % tn == 0) {
+            const int64_t per_round = cus / tn;               // tile rows of one full round
+            const int64_t full = tm / per_round * per_round;  // tile rows in full rounds
+            if (full > 0 && tm > full && (tm - full) * 2 <= per_round) g.m_tail = m - full * 256;
+        }
         return g;
     }
     // int8 x int8 grids that fill at most half the CUs with 128 x 128 tiles
@@ -114,6 +127,7 @@ GemmPlan plan_gemm_f6(int64_t m, int64_t n, int64_t k, bool geglu) {
     g.splits = 1;
     g.deep = false;
     g.ws_bytes = 0;
+    g.m_tail = 0;
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
     if (tiles256 >= cus && geglu) {   // the fused GeGLU: 128 x 256 tiles, two blocks per CU
         g.bm = 128;

@@ -68,6 +68,7 @@ struct GemmPlan {
     bool deep;      // grid fits one block per CU: one block per CU with a deeper DMA ring
     int group_m;    // tile order: 0 = rows fastest, else groups of group_m tile rows
     int64_t ws_bytes;
+    int64_t m_tail; // 256 x 256 plans: the last m_tail rows run as 128 x 128 tiles in a second launch
 };
 // a8 (with int4): int8 activations against int4 weights (W4A8).  Split-K
 // only when allow_split (the caller supplies the partials' workspace).

@@ -523,6 +523,43 @@ def test_gemm_big_grid_sampled_rows(scheme, m, n, k):
     assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
 
 
+# 256 x 256 grids whose last round would fill at most half of the 256 CUs:
+# the full rounds run as 256 x 256 tiles and the last rows as 128 x 128
+# tiles (two blocks per CU) in a second launch.
+TAIL_SHAPES = [
+    ("w8a8", 9316, 2048, 512),    # 37 tile rows of 8: 32 in full rounds, a ragged tail of 1124 rows
+    ("w4a8", 9316, 2048, 512),
+    ("w8a8", 8300, 4096, 256),    # 33 tile rows of 16: a tail of 108 rows
+]
+
+
+@pytest.mark.parametrize("out", ["i32", "bf16"])
+@pytest.mark.parametrize("scheme,m,n,k", TAIL_SHAPES)
+def test_gemm_256_grid_with_small_tile_tail(scheme, m, n, k, out):
+    """Rows on both sides of the split, the first and last rows and random
+    ones: raw accumulators bit-exact, dequantized outputs within tolerance,
+    against the oracle."""
+    say(f"gemm 256 + tail {scheme} {m}x{n}x{k} {out}")
+    a, b, abits, wbits, fn = scheme_codes(scheme, "tail", m, n, k)
+    tm, per_round = (m + 255) // 256, 256 // ((n + 255) // 256)
+    split = tm // per_round * per_round * 256
+    rows = np.array(sorted(set(_sample_rows(m, 24).tolist()) | set(range(split - 3, split + 3))))
+    ac, bc = codes_np(a, abits), codes_np(b, wbits)
+    if out == "i32":
+        acc = fn(a.to(DEV), None, b.to(DEV), None, k, y_dtype=torch.int32)
+        torch.cuda.synchronize()
+        got = acc.cpu().numpy().astype(np.int64)[rows]
+        ref = oracle.int_gemm(ac[rows], bc)
+        assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
+    else:
+        sx = synth.random_scales(SEED, f"sxt/{m}", m)
+        sw = synth.random_scales(SEED, f"swt/{n}", n)
+        y = fn(a.to(DEV), sx.to(DEV), b.to(DEV), sw.to(DEV), k, y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        _, _, y_ref = oracle.gemm(ac[rows], sx.numpy()[rows], bc, sw.numpy(), "bf16")
+        assert_ok(oracle.compare_outputs(f64(y)[rows], y_ref), "output")
+
+
 @pytest.mark.parametrize("m,f,k", [(1100, 1984, 256), (2100, 2048, 256), (4100, 2048, 512), (2050, 8192, 256),
                                    (1100, 2048, 192)])
 def test_gemm_geglu_big_grid_sampled_rows(m, f, k):
