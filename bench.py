@@ -262,6 +262,29 @@ def time_sweep(model, m, steps, warmup):
     return ms_step, statistics.mean(gu), per_step, wall, clk.summary()
 
 
+def copy_model(read_bytes, write_bytes, reps=5):
+    """The achievable time of a kernel that streams read_bytes in and
+    write_bytes out once, from two measurements on fresh device buffers of
+    the read size: a read-only stream (qlin_stream_read) gives the read
+    time, a device-to-device copy (read and write of the same bytes) the
+    added cost of writing.  Model: t = t_read(R) + (t_copy(R) - t_read(R)) * W / R."""
+    import torch
+
+    import bit_ptq_vla_amd as q
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(read_bytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    t_read = _median_us(lambda: q.qlin_stream_read(src, sink=sink), reps)
+    t_copy = _median_us(lambda: dst.copy_(src), reps)
+    del src, dst
+    torch.cuda.empty_cache()
+    model = t_read + (t_copy - t_read) * write_bytes / read_bytes
+    return {"read_GB/s": round(read_bytes / t_read / 1e3, 1), "copy_GB/s": round(2 * read_bytes / t_copy / 1e3, 1),
+            "model_us": round(model, 2)}
+
+
 def layer_breakdown(model, m, reps=3):
     """Mean duration of each of a layer's 8 launches at m tokens (events
     between consecutive launches, all layers, `reps` passes), with the
@@ -299,6 +322,10 @@ def layer_breakdown(model, m, reps=3):
             nbytes = m * k * 2 + m * k * bits // 8 + 4 * m
             r["GB/s"] = round(nbytes / (us * 1e-6) / 1e9, 1)
             r["frac_hbm"] = round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            # the achievable streaming time of the same read and write bytes on this GPU
+            cm = copy_model(m * k * 2, m * k * bits // 8 + 4 * m)
+            r["copy_model"] = cm
+            r["frac_of_copy_model"] = round(cm["model_us"] / us, 4)
         out[name] = r
     return out
 
