@@ -42,14 +42,17 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
     const int64_t kbytes = int4 ? k / 2 : k;
     const int64_t stages = (kbytes + STAGE_BYTES - 1) / STAGE_BYTES;
     g.group_m = 0;
-    // int8 activations with enough 256 x 256 tiles for every CU: one block per
-    // CU, each wave a 128 x 128 accumulator tile (half the LDS bytes per MFMA of
-    // a 64 x 128 wave tile), tiles in 4-row groups.  (W4A4 stays on the two-
+    // int8 activations with 256 x 256 tiles for at least 3/4 of the CUs: one
+    // block per CU, each wave a 128 x 128 accumulator tile (half the LDS bytes
+    // per MFMA of a 64 x 128 wave tile), tiles in 4-row groups.  Below one
+    // tile per CU this still beats the 128 x 128 two-block plan, whose tiles
+    // do about 0.6x the work per CU-second: at 6528 x 2048 (208 tiles on 256
+    // CUs) o takes 37 us against 50-52 us, down 223 us against 330-335 us.  (W4A4 stays on the two-
     // blocks-per-CU tiles below: its int4 unpack and epilogue VALU work is
     // covered there by the co-resident block's MFMAs; measured 45.6% against
     // 40.7% of the int8 peak for the 52224 x 32768 x 2048 gate|up GEMM.)
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-    if (tiles256 >= cus && (!int4 || a8)) {
+    if (tiles256 * 4 >= cus * 3 && (!int4 || a8)) {
         g.bm = g.bn = 256;
         g.splits = 1;
         g.deep = false;

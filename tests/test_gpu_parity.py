@@ -502,6 +502,8 @@ BIG_GRID_SHAPES = [
     ("w4a4", 4100, 4000, 512),    # 33 x 16 tiles of 128 x 256
     ("w4a8", 4100, 4096, 256),
     ("w8a8", 6528, 2560, 1024),   # 26 x 10 tiles, the last tile row half empty
+    ("w8a8", 6528, 2048, 1024),   # 208 tiles of 256 x 256 on 256 CUs (at least 3/4 of them: still this plan)
+    ("w4a8", 6100, 2000, 512),    # 24 x 8 = 192 tiles, exactly 3/4 of the CUs; ragged M and N
     ("w8a8", 4100, 4096, 192),    # 3 k-stages: one zero-filled stage pads the 4-stage ring
     ("w4a4", 4352, 4096, 384),    # 34 x 16 tiles of 128 x 256, 3 k-stages
     ("w4a8", 4352, 4096, 512),    # 4 k-stages, padded to 6 (3-stage ring)
