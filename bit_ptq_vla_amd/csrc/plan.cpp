@@ -95,14 +95,26 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, bool int4, bool a8, bool all
     }
     g.bm = 128;
     g.bn = (n >= 4096 && int4 && !a8) ? 256 : 128;
-    const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
     const int64_t slots = 2 * cus;   // two resident blocks per CU
-    int splits = 1;
     // split K only when the tile grid fills under half of the block slots,
     // keeping at least 16 stages (1 KiB of k per row) in every split
-    if (allow_split && tiles * 2 <= slots) {
-        while (tiles * splits * 2 <= slots && stages / (splits * 2) >= 16) splits *= 2;
+    auto split_for = [&](int64_t t) {
+        int s = 1;
+        if (allow_split && t * 2 <= slots) {
+            while (t * s * 2 <= slots && stages / (s * 2) >= 16) s *= 2;
+        }
+        return s;
+    };
+    // The wide tiles only when they, with their splits, fill every CU: at
+    // 816 x 6144 x 2048 (no split) their 168 tiles leave 88 CUs idle, and
+    // 336 tiles of 128 x 128 (two blocks per CU) take 23.1-23.6 us against
+    // 25.8-26.0 us.
+    if (g.bn == 256) {
+        const int64_t t = ((m + 127) / 128) * ((n + 255) / 256);
+        if (t * split_for(t) < cus) g.bn = 128;
     }
+    const int64_t tiles = ((m + g.bm - 1) / g.bm) * ((n + g.bn - 1) / g.bn);
+    int splits = split_for(tiles);
     // int8 x int8 with few tiles: the largest split that still gives every
     // block a CU of its own (the deep ring below), when it fills at least 3/4
     // of the CUs.  At 816 x 2048 x 16384 that is two splits on 224 CUs: the

@@ -608,7 +608,7 @@ def test_gemm_dequant_epilogue(scheme, m, n, k, out):
 GEGLU_SHAPES = [
     # m, f (h columns; n2 = 2 f interleaved weight rows), k
     (50, 64, 256),       # 128-wide tiles
-    (130, 2048, 512),    # 256-wide tiles, ragged m
+    (130, 2048, 512),    # 128-wide tiles (256-wide ones would not fill the CUs), ragged m
     (1, 32, 128),        # one token, one gate/up pair, ragged n tile
     (300, 4096, 1024),
 ]
