@@ -443,7 +443,8 @@ GEMM_SHAPES = [
     (80, 100, 4096),     # split-K, n % 8 == 4: four outputs per reduce lane
     (70, 99, 2048),      # split-K, odd n: one output per reduce lane
     (65, 256, 16384),    # split-K
-    (1000, 1800, 4096),  # int8 x int8: two K splits, one block per CU (240 CUs); ragged M and N
+    (1000, 1800, 4160),  # int8 x int8: two K splits, one block per CU (240 CUs); ragged M and N (k past
+                         # 64 stages: the 64 x 64 two-round plan does not apply)
     (250, 4000, 256),    # int8 x int8: 64 x 64 tiles, one per CU (252); ragged M and N
     (300, 520, 320),     # k % 128 == 64 on the large-tile GEMM: a half-full last int4 stage
     (70, 99, 4160),      # ... with split-K: 33 stages in two splits, the half stage in the last
@@ -508,6 +509,8 @@ BIG_GRID_SHAPES = [
     ("w4a4", 4352, 4096, 384),    # 34 x 16 tiles of 128 x 256, 3 k-stages
     ("w4a8", 4352, 4096, 512),    # 4 k-stages, padded to 6 (3-stage ring)
     ("w8a8", 256, 4096, 2048),    # the 7B decoder's 256 tokens: 64 x 64 tiles, one per CU
+    ("w8a8", 816, 2048, 2048),    # short k: 416 tiles of 64 x 64, two rounds
+    ("w8a8", 600, 2000, 1024),    # short k: 10 x 32 tiles of 64 x 64, ragged M and N
     ("w8a8", 256, 11008, 512),    # 172 tiles of 128 x 128 (the deep ring), not 64 x 64
     ("w4a4", 2100, 4096, 320),    # 128 x 256 tiles, a half-full last int4 stage
 ]
