@@ -163,6 +163,14 @@ def test_gemm_workspace_bytes(lib):
         # ... but with k past 128 stages the workspace call keeps split-K (four splits)
         assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 256, 4096, 11008) == 4 * 256 * 4096 * 4
         assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 816, 2048, 16448) >= 0   # W4A4 at k % 128 == 64
+        # short k (at most 64 stages): up to two rounds of 64 x 64 tiles take the
+        # place of split-K (o at 816 tokens: 416 tiles)
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 816, 2048, 2048) == 0
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 1000, 1800, 4096) == 0
+        # one stage more: two K splits, one block per CU
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W8A8, 1000, 1800, 4160) == 2 * 1000 * 1800 * 4
+        # W4A4 keeps 128 x 256 tiles when they fill the CUs with their splits
+        assert lib.qlin_gemm_workspace_bytes(q.QLIN_W4A4, 1024, 4096, 8192) == 4 * 1024 * 4096 * 4
 
 
 def gemm_ws(lib, scheme=q.QLIN_W8A8, xq=P, sx=P3, wq=P2, sw=P4, m=DOWN["m"], n=DOWN["n"], k=DOWN["k"],
